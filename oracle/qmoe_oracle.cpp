@@ -1,0 +1,324 @@
+/*
+ * qmoe_oracle.cpp -- TEST INFRASTRUCTURE ONLY (see qmoe_oracle.h).
+ *
+ * Plain fp64 evaluation of the weight-only-quantized MoE forward. Every value
+ * is widened exactly to double, every product and sum is formed in double in
+ * plain ascending loops, and only the final output is rounded (once) to the
+ * activation dtype. Speed is not a goal: weights are dequantised element by
+ * element from their packed bytes at the point of use.
+ *
+ * Readings of points the pages leave open (each is also a test in tests/):
+ *  - the second forward input holds logits; the softmax is taken here
+ *    (ClikaRT "QMoEWoQ" page: the caller computes router logits);
+ *  - softmax over all E experts, then the k largest are kept; their weights are
+ *    their probabilities, divided by their sum when renormalising;
+ *  - selection compares the logit values themselves (IEEE: -0 == +0), larger
+ *    first, equal values in ascending expert index; slots keep that order;
+ *  - a 4-bit byte holds element 2j in its low nibble and 2j+1 in its high nibble;
+ *  - dequant(q) = (q - 2^(bits-1)) * scale, q the unsigned field;
+ *  - block_size 0: one scale per output row; otherwise scale index floor(k/bs),
+ *    with a shorter last block when bs does not divide K;
+ *  - interleaved fusion: row 2i is gate, 2i+1 is up; concatenated: rows [0,I)
+ *    gate, [I,2I) up; separate stacks: fc1 gate, fc3 up; biases follow rows;
+ *  - SwiGLU: g' = min(g, L), u' = clamp(u, -L, L), h = g' * sigmoid(alpha g') * (u' + beta);
+ *  - biases are added before the activation (fc1/fc3) and before the routing
+ *    weight (fc2); shared_output is added after the weighted sum.
+ */
+#include "qmoe_oracle.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- exact widening of stored elements --------------------------------- */
+
+static double widen(const void* base, int32_t dtype, int64_t i) {
+  if (dtype == ORACLE_F32) {
+    float f;
+    std::memcpy(&f, static_cast<const char*>(base) + 4 * i, 4);
+    return static_cast<double>(f);
+  }
+  uint16_t h;
+  std::memcpy(&h, static_cast<const char*>(base) + 2 * i, 2);
+  uint32_t bits = static_cast<uint32_t>(h) << 16;  // a bfloat16 is the top half of a float
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return static_cast<double>(f);
+}
+
+/* ---- rounding of the result to bfloat16 (8 significant bits) ----------- */
+
+static uint16_t round_to_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  double r;
+  if (v == 0.0) {
+    r = v;
+  } else {
+    int e;
+    std::frexp(v, &e);              // |v| = m * 2^e, m in [0.5, 1)
+    int q = e - 8;                  // quantum of an 8-significant-bit number
+    if (q < -133) q = -133;         // subnormal bfloat16 quantum
+    r = std::ldexp(std::nearbyint(std::ldexp(v, -q)), q);  // nearest, ties to even
+    if (std::fabs(r) > 3.3895313892515355e38) r = std::copysign(INFINITY, v);
+  }
+  float f = static_cast<float>(r);  // exact: r has at most 8 significant bits
+  uint32_t bits;
+  std::memcpy(&bits, &f, 4);
+  return static_cast<uint16_t>(bits >> 16);
+}
+
+void oracle_round_bf16(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = round_to_bf16(v[i]);
+}
+
+static void store_out(const oracle_params* p, void* dst, int64_t i, double v) {
+  if (p->act_dtype == ORACLE_F32) {
+    float f = static_cast<float>(v);  // IEEE round-to-nearest-even
+    std::memcpy(static_cast<char*>(dst) + 4 * i, &f, 4);
+  } else {
+    uint16_t h = round_to_bf16(v);
+    std::memcpy(static_cast<char*>(dst) + 2 * i, &h, 2);
+  }
+}
+
+/* ---- routing: softmax over all experts, keep the top k ------------------ */
+
+static void route_token(const oracle_params* p, const void* logits, int64_t t, int32_t* ids,
+                        double* w) {
+  const int64_t E = p->E;
+  std::vector<double> l(E);
+  for (int64_t e = 0; e < E; ++e) l[e] = widen(logits, p->act_dtype, t * E + e);
+
+  // Selection: larger logit first; a stable sort keeps equal logits in index order.
+  std::vector<int32_t> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return l[a] > l[b]; });
+
+  // Softmax over all E (shifted by the maximum for range only; the value is unchanged).
+  double m = l[order[0]];
+  double denom = 0.0;
+  for (int64_t e = 0; e < E; ++e) denom += std::exp(l[e] - m);
+
+  double sum = 0.0;
+  for (int64_t j = 0; j < p->k; ++j) {
+    ids[j] = order[j];
+    w[j] = std::exp(l[order[j]] - m) / denom;
+    sum += w[j];
+  }
+  if (p->normalize)
+    for (int64_t j = 0; j < p->k; ++j) w[j] /= sum;
+}
+
+void oracle_route(const oracle_params* p, const void* logits, int32_t* ids, double* w) {
+  for (int64_t t = 0; t < p->T; ++t) route_token(p, logits, t, ids + t * p->k, w + t * p->k);
+}
+
+/* ---- grouping by expert -------------------------------------------------- */
+
+int64_t oracle_permute(const oracle_params* p, int32_t M, const int32_t* ids, int32_t* counts,
+                       int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                       int32_t* tiles, int32_t* num_tiles) {
+  const int64_t A = p->T * p->k, E = p->E;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < A; ++a) counts[ids[a]] += 1;
+
+  padded_offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int32_t tiles_e = (counts[e] + M - 1) / M;
+    padded_offsets[e + 1] = padded_offsets[e] + tiles_e * M;
+  }
+  for (int64_t r = 0; r < padded_offsets[E]; ++r) sorted_assign[r] = -1;
+
+  // Stable: scan assignments in ascending order once per expert.
+  for (int64_t e = 0; e < E; ++e) {
+    int32_t pos = padded_offsets[e];
+    for (int64_t a = 0; a < A; ++a) {
+      if (ids[a] == e) {
+        sorted_assign[pos] = static_cast<int32_t>(a);
+        assign_pos[a] = pos;
+        ++pos;
+      }
+    }
+  }
+
+  int32_t nt = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    for (int32_t r = 0; r * M < counts[e]; ++r) {
+      tiles[2 * nt] = static_cast<int32_t>(e);
+      tiles[2 * nt + 1] = std::min(M, counts[e] - r * M);
+      ++nt;
+    }
+  }
+  *num_tiles = nt;
+  return padded_offsets[E];
+}
+
+/* ---- dequantisation of one weight ---------------------------------------- */
+
+static int32_t qfield(const oracle_params* p, const uint8_t* w, int64_t N, int64_t K, int64_t e,
+                      int64_t n, int64_t kk) {
+  const int64_t row_bytes = K * p->bits / 8;
+  const uint8_t* row = w + (e * N + n) * row_bytes;
+  if (p->bits == 8) return row[kk];
+  uint8_t byte = row[kk / 2];
+  return (kk % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+double oracle_weight(const oracle_params* p, const oracle_stack* st, int64_t N, int64_t K,
+                     int64_t e, int64_t n, int64_t kk) {
+  const int32_t zero = 1 << (p->bits - 1);
+  double s;
+  if (p->block_size == 0) {
+    s = widen(st->s, p->scale_dtype, e * N + n);
+  } else {
+    const int64_t nb = (K + p->block_size - 1) / p->block_size;
+    s = widen(st->s, p->scale_dtype, (e * N + n) * nb + kk / p->block_size);
+  }
+  return static_cast<double>(qfield(p, st->w, N, K, e, n, kk) - zero) * s;
+}
+
+/* One output of a dequantised linear layer: sum_k in[k] * W[n][k] + b[n]. */
+static double linear_out(const oracle_params* p, const oracle_stack* st, int64_t N, int64_t K,
+                         int64_t e, int64_t n, const double* in) {
+  double acc = 0.0;
+  for (int64_t kk = 0; kk < K; ++kk) acc += in[kk] * oracle_weight(p, st, N, K, e, n, kk);
+  if (st->b) acc += widen(st->b, p->act_dtype, e * N + n);
+  return acc;
+}
+
+/* ---- activation ---------------------------------------------------------- */
+
+static double sigmoid(double v) { return 1.0 / (1.0 + std::exp(-v)); }
+
+static double swiglu(const oracle_params* p, double g, double u) {
+  const double L = p->limit;
+  g = std::min(g, L);
+  u = std::max(-L, std::min(u, L));
+  return g * sigmoid(p->alpha * g) * (u + p->beta);
+}
+
+static double plain_act(const oracle_params* p, double z) {
+  switch (p->activation) {
+    case ORACLE_ACT_RELU: return z > 0.0 ? z : 0.0;
+    case ORACLE_ACT_SILU: return z * sigmoid(z);
+    default: return z;  // identity
+  }
+}
+
+/* fc1 (and fc3) followed by the activation for one token row through expert e. */
+static void expert_fc1(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc3,
+                       int64_t e, const double* x, double* h) {
+  const int64_t H = p->H, I = p->I;
+  if (p->activation != ORACLE_ACT_SWIGLU) {
+    for (int64_t i = 0; i < I; ++i) h[i] = plain_act(p, linear_out(p, fc1, I, H, e, i, x));
+    return;
+  }
+  for (int64_t i = 0; i < I; ++i) {
+    double g, u;
+    if (p->fusion == 1) {         // interleaved: gate row 2i, up row 2i+1
+      g = linear_out(p, fc1, 2 * I, H, e, 2 * i, x);
+      u = linear_out(p, fc1, 2 * I, H, e, 2 * i + 1, x);
+    } else if (p->fusion == 2) {  // concatenated: gate rows [0,I), up rows [I,2I)
+      g = linear_out(p, fc1, 2 * I, H, e, i, x);
+      u = linear_out(p, fc1, 2 * I, H, e, I + i, x);
+    } else {                      // separate stacks: fc1 gate, fc3 up
+      g = linear_out(p, fc1, I, H, e, i, x);
+      u = linear_out(p, fc3, I, H, e, i, x);
+    }
+    h[i] = swiglu(p, g, u);
+  }
+}
+
+static void expert_fc2(const oracle_params* p, const oracle_stack* fc2, int64_t e, const double* h,
+                       double* y) {
+  for (int64_t m = 0; m < p->H; ++m) y[m] = linear_out(p, fc2, p->H, p->I, e, m, h);
+}
+
+static void widen_row(const void* base, int32_t dtype, int64_t row, int64_t len, double* out) {
+  for (int64_t i = 0; i < len; ++i) out[i] = widen(base, dtype, row * len + i);
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+void oracle_fc1_rows(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc3,
+                     const void* x, int64_t n_rows, const int32_t* row_token,
+                     const int32_t* row_expert, double* h, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::vector<double> xr(p->H);
+    widen_row(x, p->act_dtype, row_token[r], p->H, xr.data());
+    expert_fc1(p, fc1, fc3, row_expert[r], xr.data(), h + r * p->I);
+  }
+}
+
+void oracle_fc2_rows(const oracle_params* p, const oracle_stack* fc2, const void* h_in,
+                     int64_t n_rows, const int32_t* row_index, const int32_t* row_expert,
+                     double* y, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::vector<double> hr(p->I);
+    widen_row(h_in, p->act_dtype, row_index[r], p->I, hr.data());
+    expert_fc2(p, fc2, row_expert[r], hr.data(), y + r * p->H);
+  }
+}
+
+/* ---- combine -------------------------------------------------------------- */
+
+void oracle_combine(const oracle_params* p, const float* y, const int32_t* assign_pos,
+                    const float* w, const void* shared, double* out64, void* out_rounded) {
+  const int64_t H = p->H, k = p->k;
+  for (int64_t t = 0; t < p->T; ++t) {
+    for (int64_t m = 0; m < H; ++m) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j)
+        acc += static_cast<double>(w[t * k + j]) *
+               static_cast<double>(y[static_cast<int64_t>(assign_pos[t * k + j]) * H + m]);
+      if (shared) acc += widen(shared, p->act_dtype, t * H + m);
+      out64[t * H + m] = acc;
+      if (out_rounded) store_out(p, out_rounded, t * H + m, acc);
+    }
+  }
+}
+
+/* ---- whole forward, token by token ---------------------------------------- */
+
+void oracle_forward(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc2,
+                    const oracle_stack* fc3, const void* x, const void* logits, const void* shared,
+                    int64_t n_sel, const int64_t* sel, double* out64, void* out_rounded,
+                    int nthreads) {
+  const int64_t H = p->H, I = p->I, k = p->k;
+  const int64_t n = sel ? n_sel : p->T;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = sel ? sel[r] : r;
+    std::vector<int32_t> ids(k);
+    std::vector<double> w(k), xr(H), h(I), y(H), acc(H, 0.0);
+    route_token(p, logits, t, ids.data(), w.data());
+    widen_row(x, p->act_dtype, t, H, xr.data());
+    for (int64_t j = 0; j < k; ++j) {
+      expert_fc1(p, fc1, fc3, ids[j], xr.data(), h.data());
+      expert_fc2(p, fc2, ids[j], h.data(), y.data());
+      for (int64_t m = 0; m < H; ++m) acc[m] += w[j] * y[m];
+    }
+    for (int64_t m = 0; m < H; ++m) {
+      double v = acc[m] + (shared ? widen(shared, p->act_dtype, t * H + m) : 0.0);
+      out64[r * H + m] = v;
+      if (out_rounded) store_out(p, out_rounded, r * H + m, v);
+    }
+  }
+}

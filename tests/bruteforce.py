@@ -1,0 +1,109 @@
+"""An independent dense reference for tiny inputs, used to pin the oracle.
+
+It is built differently from the oracle on purpose:
+* every expert's weights are dequantised at once with numpy bit operations;
+* the expert set of a token is found by enumerating all C(E, k) subsets and
+  keeping the one with the largest logit sum (ties: the lexicographically
+  smallest index set), which equals "top-k, ties to the lower index";
+* every expert's FFN is evaluated for every token and mixed through a dense
+  [T, E] gate matrix; no grouping or permutation is involved;
+* the sigmoid comes from scipy.
+
+Sources for what is computed: CLIKA "MoE" page (router picks top-k experts,
+gated FFN, outputs combined under the router weights); CLIKA "QLinearWoQ" page
+(y = x @ dequant(W).T + bias); graiphic "QMoE" page (tensor shapes,
+swiglu_fusion, block_size, expert_weight_bits, activation parameters).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+from scipy.special import expit
+
+from synth.gen import as_f32
+
+
+def dequant_dense(w: np.ndarray, s: np.ndarray, cfg, N: int, K: int) -> np.ndarray:
+    E = w.shape[0]
+    if cfg.bits == 4:
+        lo = (w & 0x0F).astype(np.int64)
+        hi = (w >> 4).astype(np.int64)
+        q = np.stack([lo, hi], axis=-1).reshape(E, N, K)
+    else:
+        q = w.astype(np.int64)
+    sf = as_f32(s, cfg.scale_dtype).astype(np.float64)
+    if cfg.block_size == 0:
+        scale = np.broadcast_to(sf[:, :, None], (E, N, K))
+    else:
+        scale = np.repeat(sf, cfg.block_size, axis=2)[:, :, :K]
+    return (q - (1 << (cfg.bits - 1))).astype(np.float64) * scale
+
+
+def select(cfg, logits_row: np.ndarray):
+    best, best_sum = None, None
+    for subset in itertools.combinations(range(cfg.E), cfg.k):
+        s = float(sum(logits_row[list(subset)]))
+        if best_sum is None or s > best_sum:
+            best, best_sum = subset, s
+    return list(best)
+
+
+def gates(cfg, logits: np.ndarray) -> np.ndarray:
+    """Dense [T, E] routing weights (zero for unselected experts)."""
+    T = logits.shape[0]
+    G = np.zeros((T, cfg.E))
+    for t in range(T):
+        row = logits[t]
+        chosen = select(cfg, row)
+        p = np.exp(row - row.max())
+        p = p / p.sum()
+        wsel = p[chosen]
+        if cfg.normalize:
+            wsel = wsel / wsel.sum()
+        G[t, chosen] = wsel
+    return G
+
+
+def _act_pair(cfg, g, u):
+    L = cfg.limit
+    g = np.minimum(g, L)
+    u = np.clip(u, -L, L)
+    return g * expit(cfg.alpha * g) * (u + cfg.beta)
+
+
+def forward(cfg, inp) -> np.ndarray:
+    x = as_f32(inp.x, cfg.act_dtype).astype(np.float64)
+    lg = as_f32(inp.logits, cfg.act_dtype).astype(np.float64)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    W1 = dequant_dense(inp.w1, inp.s1, cfg, cfg.n1, H)
+    W2 = dequant_dense(inp.w2, inp.s2, cfg, H, I)
+
+    def bias(b):
+        return 0.0 if b is None else as_f32(b, cfg.act_dtype).astype(np.float64)
+
+    z1 = np.einsum("th,enh->etn", x, W1) + (0.0 if inp.b1 is None else bias(inp.b1)[:, None, :])
+    if cfg.activation == "swiglu":
+        if cfg.fusion == 1:
+            g, u = z1[:, :, 0::2], z1[:, :, 1::2]
+        elif cfg.fusion == 2:
+            g, u = z1[:, :, :I], z1[:, :, I:]
+        else:
+            W3 = dequant_dense(inp.w3, inp.s3, cfg, I, H)
+            z3 = np.einsum("th,enh->etn", x, W3) + (0.0 if inp.b3 is None else bias(inp.b3)[:, None, :])
+            g, u = z1, z3
+        h = _act_pair(cfg, g, u)
+    elif cfg.activation == "identity":
+        h = z1
+    elif cfg.activation == "relu":
+        h = np.maximum(z1, 0.0)
+    elif cfg.activation == "silu":
+        h = z1 * expit(z1)
+    else:
+        raise ValueError(cfg.activation)
+    y = np.einsum("eti,ehi->eth", h, W2) + (0.0 if inp.b2 is None else bias(inp.b2)[:, None, :])
+    G = gates(cfg, lg)
+    out = np.einsum("te,eth->th", G, y)
+    if inp.shared is not None:
+        out = out + as_f32(inp.shared, cfg.act_dtype).astype(np.float64)
+    return out

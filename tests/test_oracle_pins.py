@@ -1,0 +1,417 @@
+"""Pins for the CPU oracle: it is checked here against things other than itself.
+
+* an independent dense brute-force reference (tests/bruteforce.py) on tiny inputs,
+* closed forms (zero-point weights, integer-exact products, uniform and one-hot logits),
+* library routines (scipy softmax, torch bfloat16 rounding, torch silu, numpy stable sort),
+* layout equivalences that a wrong nibble order, gate/up swap or scale index would break,
+* the hand-worked examples in tests/golden/.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+import oracle
+from synth import configs, gen
+from synth.gen import as_f32, store
+from tests import bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+# --------------------------------------------------------------------------- brute force
+
+BRUTE_CASES = {
+    "f32-concat-b4-bs16": configs.tiny(),
+    "bf16-interleaved-b8-bs32-bias-clamp": configs.tiny(
+        act_dtype="bf16", scale_dtype="bf16", fusion=1, bits=8, block_size=32, fc1_bias=True,
+        fc2_bias=True, alpha=1.702, beta=1.0, limit=7.0, scale_lo=0.02, scale_hi=0.06),
+    "bf16-separate-fc3-perrow-bias": configs.tiny(
+        act_dtype="bf16", scale_dtype="bf16", fusion=0, block_size=0, fc1_bias=True,
+        fc2_bias=True, E=5, k=3),
+    "f32-ragged-bs32-K80": configs.tiny(H=80, I=48, block_size=32, limit=2.0,
+                                        scale_lo=0.05, scale_hi=0.1),
+    "f32-identity": configs.tiny(activation="identity", fusion=0, fc2_bias=True),
+    "f32-relu": configs.tiny(activation="relu", fusion=0, fc1_bias=True),
+    "bf16-silu-b8": configs.tiny(activation="silu", fusion=0, bits=8, act_dtype="bf16"),
+    "f32-no-renorm-E6k3": configs.tiny(normalize=False, E=6, k=3, logit_sigma=2.0),
+    "bf16-fscale-b8-bs64": configs.tiny(act_dtype="bf16", scale_dtype="f32", bits=8,
+                                        block_size=64, H=128, I=64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BRUTE_CASES))
+def test_oracle_matches_bruteforce(name):
+    cfg = BRUTE_CASES[name]
+    inp = gen.make_inputs(cfg, 7, shared=(name.startswith("bf16-separate")))
+    ref = bruteforce.forward(cfg, inp)
+    out64, _ = oracle.forward(cfg, inp)
+    assert np.max(np.abs(out64 - ref)) <= 1e-11 * max(rms(ref), 1e-30)
+
+
+def test_bruteforce_clamp_case_actually_clamps():
+    # The clamp case must exercise the limit, or it pins nothing about it.
+    cfg = BRUTE_CASES["bf16-interleaved-b8-bs32-bias-clamp"]
+    inp = gen.make_inputs(cfg, 7)
+    x = as_f32(inp.x, "bf16").astype(np.float64)
+    W1 = bruteforce.dequant_dense(inp.w1, inp.s1, cfg, cfg.n1, cfg.H)
+    z = np.einsum("th,enh->etn", x, W1)
+    assert (z > 7).mean() > 0.05 and (z < -7).mean() > 0.05
+
+
+# --------------------------------------------------------------------------- routing
+
+def test_route_matches_subset_bruteforce_with_many_ties():
+    cfg = configs.tiny(E=7, k=3, act_dtype="bf16")
+    rng = np.random.default_rng(5)
+    # values from a small set so exact ties are frequent, including -0 and +0
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    lg = store(vals[rng.integers(0, len(vals), size=(300, cfg.E))], "bf16")
+    ids, w = oracle.route(cfg, lg)
+    lf = as_f32(lg, "bf16").astype(np.float64)
+    ties = 0
+    for t in range(lf.shape[0]):
+        assert sorted(ids[t].tolist()) == bruteforce.select(cfg, lf[t])
+        # slot order: descending logit, ascending index among equals
+        assert all((lf[t, ids[t, j]] > lf[t, ids[t, j + 1]]) or
+                   (lf[t, ids[t, j]] == lf[t, ids[t, j + 1]] and ids[t, j] < ids[t, j + 1])
+                   for j in range(cfg.k - 1))
+        kth = lf[t, ids[t, -1]]
+        ties += int(np.sum(lf[t] == kth) > np.sum(lf[t, ids[t]] == kth))
+    assert ties > 30  # the boundary tie rule was exercised
+
+
+def test_route_uniform_logits_pick_lowest_indices():
+    for normalize, expect in ((True, 1 / 3), (False, 1 / 8)):
+        cfg = configs.tiny(E=8, k=3, normalize=normalize)
+        lg = np.full((4, 8), 0.25, np.float32)
+        ids, w = oracle.route(cfg, lg)
+        assert (ids == np.array([0, 1, 2])).all()
+        assert np.allclose(w, expect, rtol=0, atol=1e-15)
+
+
+def test_route_negative_zero_equals_positive_zero():
+    cfg = configs.tiny(E=4, k=2, act_dtype="bf16")
+    lg = store(np.array([[-0.0, 0.0, -0.0, -1.0]], np.float32), "bf16")
+    assert lg[0, 0] == 0x8000  # the stored pattern really is -0
+    ids, _ = oracle.route(cfg, lg)
+    assert ids.tolist() == [[0, 1]]
+
+
+def test_route_one_hot():
+    cfg = configs.tiny(E=6, k=1)
+    lg = np.zeros((6, 6), np.float32)
+    lg[np.arange(6), np.arange(6)[::-1]] = 30.0
+    ids, w = oracle.route(cfg, lg)
+    assert ids[:, 0].tolist() == [5, 4, 3, 2, 1, 0]
+    assert np.all(w == 1.0)  # renormalised single weight is exactly one
+
+
+def test_route_weights_are_scipy_softmax():
+    cfg = configs.tiny(E=9, k=9, normalize=False, act_dtype="bf16")
+    lg = store(np.random.default_rng(1).normal(0, 3, size=(50, 9)), "bf16")
+    ids, w = oracle.route(cfg, lg)
+    p = softmax(as_f32(lg, "bf16").astype(np.float64), axis=1)
+    assert np.allclose(np.take_along_axis(p, ids, 1), w, rtol=1e-13, atol=0)
+
+
+def test_route_renormalised_weights_sum_to_one():
+    cfg = configs.tiny(E=32, k=4, act_dtype="bf16")
+    lg = store(np.random.default_rng(2).normal(0, 2, size=(200, 32)), "bf16")
+    _, w = oracle.route(cfg, lg)
+    assert np.max(np.abs(w.sum(1) - 1.0)) < 1e-15
+    assert np.all(np.diff(w, axis=1) <= 0)  # larger logit, larger weight
+
+
+# --------------------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("M", [1, 4, 16, 128])
+def test_permute_is_stable_sort_padded(M):
+    cfg = configs.tiny(E=10, k=3)
+    ids = gen.gen_topk_ids(cfg, 57, skew=4.0)
+    perm = oracle.permute(cfg, ids, M)
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")  # library stable sort
+    counts = np.bincount(flat, minlength=cfg.E)
+    assert (perm["counts"] == counts).all() and counts.sum() == flat.size
+    offs = perm["padded_offsets"]
+    assert offs[0] == 0 and np.all(offs % M == 0)
+    assert np.all(np.diff(offs) == -(-counts // M) * M)
+    sa = perm["sorted_assign"]
+    real = sa[sa >= 0]
+    assert (real == order).all()
+    for e in range(cfg.E):
+        seg = sa[offs[e]:offs[e + 1]]
+        assert (seg[:counts[e]] >= 0).all() and (seg[counts[e]:] == -1).all()
+        assert np.all(np.diff(seg[:counts[e]]) > 0)
+    pos = perm["assign_pos"]
+    assert (sa[pos] == np.arange(flat.size)).all()  # unpermute(permute) = identity
+    tiles = perm["tiles"]
+    assert tiles[:, 1].sum() == flat.size
+    for t, (e, valid) in enumerate(tiles):
+        row0 = t * M
+        assert offs[e] <= row0 < offs[e + 1]
+        assert valid == min(M, counts[e] - (row0 - offs[e]))
+    assert perm["num_tiles"] <= oracle.max_tiles(cfg, 57, M)
+    assert perm["rows"] <= oracle.max_rows(cfg, 57, M)
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def _zero_point_weights(inp, cfg):
+    fill = 0x88 if cfg.bits == 4 else 0x80
+    for name in ("w1", "w2", "w3"):
+        a = getattr(inp, name)
+        if a is not None:
+            a[...] = fill
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_point_weights_give_bias_combination(bits):
+    cfg = configs.tiny(bits=bits, fc1_bias=True, fc2_bias=True, E=6, k=3, act_dtype="bf16",
+                       scale_dtype="bf16")
+    inp = gen.make_inputs(cfg, 9, shared=True)
+    _zero_point_weights(inp, cfg)
+    out64, _ = oracle.forward(cfg, inp)
+    lg = as_f32(inp.logits, "bf16").astype(np.float64)
+    p = softmax(lg, axis=1)
+    order = np.argsort(-lg, axis=1, kind="stable")[:, :cfg.k]
+    w = np.take_along_axis(p, order, 1)
+    w = w / w.sum(1, keepdims=True)
+    b2 = as_f32(inp.b2, "bf16").astype(np.float64)
+    expect = np.einsum("tj,tjh->th", w, b2[order]) + as_f32(inp.shared, "bf16")
+    assert np.max(np.abs(out64 - expect)) < 1e-14
+
+
+@pytest.mark.parametrize("bits,fusion", [(4, 0), (8, 0)])
+def test_identity_unit_scales_is_integer_matmul(bits, fusion):
+    # k=1 with renormalisation gives weight exactly 1; unit scales and small integer
+    # inputs make every product and sum an exact integer.
+    cfg = configs.tiny(bits=bits, fusion=fusion, activation="identity", k=1, E=3, H=64, I=32,
+                       block_size=16)
+    inp = gen.make_inputs(cfg, 6)
+    inp.x[...] = np.random.default_rng(3).integers(-3, 4, size=inp.x.shape).astype(np.float32)
+    inp.s1[...] = 1.0
+    inp.s2[...] = 1.0
+    out64, outr = oracle.forward(cfg, inp)
+    ids, w = oracle.route(cfg, inp.logits)
+    assert np.all(w == 1.0)
+    q1 = bruteforce.dequant_dense(inp.w1, inp.s1, cfg, cfg.I, cfg.H).astype(np.int64)
+    q2 = bruteforce.dequant_dense(inp.w2, inp.s2, cfg, cfg.H, cfg.I).astype(np.int64)
+    xi = inp.x.astype(np.int64)
+    expect = np.stack([(xi[t] @ q1[ids[t, 0]].T) @ q2[ids[t, 0]].T for t in range(6)])
+    assert np.array_equal(out64, expect.astype(np.float64))
+    assert np.array_equal(outr, expect.astype(np.float32))
+
+
+def test_linearity_identity_no_bias():
+    cfg = configs.tiny(activation="identity", fusion=0)
+    inp = gen.make_inputs(cfg, 5)
+    a, _ = oracle.forward(cfg, inp)
+    inp.x *= np.float32(4.0)  # exact scaling by a power of two
+    b, _ = oracle.forward(cfg, inp)
+    assert np.allclose(b, 4.0 * a, rtol=1e-13, atol=1e-300)
+
+
+def test_single_expert_is_dequant_ffn():
+    # E = 1, k = 1: the block is one weight-only-quantized FFN (QLinearWoQ composition).
+    cfg = configs.tiny(E=1, k=1, fusion=1, fc1_bias=True, fc2_bias=True)
+    inp = gen.make_inputs(cfg, 4)
+    out64, _ = oracle.forward(cfg, inp)
+    W1 = torch.from_numpy(bruteforce.dequant_dense(inp.w1, inp.s1, cfg, cfg.n1, cfg.H)[0])
+    W2 = torch.from_numpy(bruteforce.dequant_dense(inp.w2, inp.s2, cfg, cfg.H, cfg.I)[0])
+    x = torch.from_numpy(inp.x.astype(np.float64))
+    z = torch.nn.functional.linear(x, W1, torch.from_numpy(inp.b1[0].astype(np.float64)))
+    h = torch.nn.functional.silu(z[:, 0::2]) * z[:, 1::2]
+    y = torch.nn.functional.linear(h, W2, torch.from_numpy(inp.b2[0].astype(np.float64)))
+    assert np.allclose(out64, y.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_swiglu_clamp_reading():
+    # Only the gate is clamped from above; the up value is clamped on both sides.
+    cfg = configs.tiny(fusion=2, bits=8, block_size=0, H=16, I=16, E=1, k=1, alpha=1.702,
+                       beta=1.0, limit=7.0)
+    inp = gen.make_inputs(cfg, 1)
+    inp.x[...] = 0
+    inp.x[0, 0] = 1.0
+    inp.w1[...] = 0x80
+    g = np.array([10, -10, 3, -3, 0.5, 20, -20, 7] * 2, np.float64)
+    u = np.array([10, -10, -10, 10, 2, 0, 1, -7.5] * 2, np.float64)
+    inp.s1[...] = 0.5
+    inp.w1[0, :16, 0] = (128 + 2 * g).astype(np.uint8)
+    inp.w1[0, 16:, 0] = (128 + 2 * u).astype(np.uint8)
+    h = oracle.fc1_rows(cfg, inp, [0], [0])[0]
+    gp = np.minimum(g, 7.0)
+    up = np.clip(u, -7.0, 7.0)
+    sig = 1.0 / (1.0 + np.exp(-1.702 * gp))
+    assert np.allclose(h, gp * sig * (up + 1.0), rtol=1e-15, atol=0)
+    # standard SwiGLU (alpha 1, beta 0, no limit) is silu(g) * u
+    cfg2 = cfg.with_(alpha=1.0, beta=0.0, limit=math.inf)
+    h2 = oracle.fc1_rows(cfg2, inp, [0], [0])[0]
+    ref = (torch.nn.functional.silu(torch.tensor(g)) * torch.tensor(u)).numpy()
+    assert np.allclose(h2, ref, rtol=1e-15, atol=1e-300)
+
+
+# --------------------------------------------------------------------------- layout equivalences
+
+def _fwd(cfg, inp):
+    return oracle.forward(cfg, inp)[0]
+
+
+def test_interleaved_equals_concatenated():
+    cfg = configs.tiny(fusion=1, fc1_bias=True, act_dtype="bf16", scale_dtype="bf16")
+    inp = gen.make_inputs(cfg, 6)
+    a = _fwd(cfg, inp)
+    I = cfg.I
+    perm = np.concatenate([np.arange(0, 2 * I, 2), np.arange(1, 2 * I, 2)])
+    inp.w1, inp.s1, inp.b1 = inp.w1[:, perm].copy(), inp.s1[:, perm].copy(), inp.b1[:, perm].copy()
+    b = _fwd(cfg.with_(fusion=2), inp)
+    assert np.array_equal(a, b)
+
+
+def test_fused_equals_separate_stacks():
+    cfg = configs.tiny(fusion=2, fc1_bias=True, block_size=0)
+    inp = gen.make_inputs(cfg, 6)
+    a = _fwd(cfg, inp)
+    I = cfg.I
+    inp.w3, inp.s3, inp.b3 = inp.w1[:, I:].copy(), inp.s1[:, I:].copy(), inp.b1[:, I:].copy()
+    inp.w1, inp.s1, inp.b1 = inp.w1[:, :I].copy(), inp.s1[:, :I].copy(), inp.b1[:, :I].copy()
+    b = _fwd(cfg.with_(fusion=0), inp)
+    assert np.array_equal(a, b)
+
+
+def test_4bit_equals_8bit_shifted_by_120():
+    cfg4 = configs.tiny(bits=4, block_size=16)
+    inp = gen.make_inputs(cfg4, 6)
+    a = _fwd(cfg4, inp)
+
+    def widen(w):
+        lo, hi = (w & 0xF), (w >> 4)
+        return (np.stack([lo, hi], -1).reshape(w.shape[0], w.shape[1], -1) + 120).astype(np.uint8)
+
+    inp.w1, inp.w2 = widen(inp.w1), widen(inp.w2)
+    b = _fwd(cfg4.with_(bits=8), inp)
+    assert np.array_equal(a, b)
+
+
+def test_per_row_equals_constant_blocks():
+    cfg = configs.tiny(block_size=0, act_dtype="bf16", scale_dtype="bf16")
+    inp = gen.make_inputs(cfg, 6)
+    a = _fwd(cfg, inp)
+    cb = cfg.with_(block_size=16)
+    inp.s1 = np.repeat(inp.s1[:, :, None], cb.nblocks(cfg.H), 2).copy()
+    inp.s2 = np.repeat(inp.s2[:, :, None], cb.nblocks(cfg.I), 2).copy()
+    b = _fwd(cb, inp)
+    assert np.array_equal(a, b)
+
+
+def test_ragged_128_equals_64_with_pairs():
+    # K = 192 with block 128: the last block holds 64 elements.
+    cfg = configs.tiny(H=192, I=320, block_size=128, bits=8)
+    inp = gen.make_inputs(cfg, 5)
+    assert inp.s1.shape[2] == 2 and inp.s2.shape[2] == 3
+    a = _fwd(cfg, inp)
+    c64 = cfg.with_(block_size=64)
+    inp.s1 = np.repeat(inp.s1, 2, axis=2)[:, :, :3].copy()
+    inp.s2 = np.repeat(inp.s2, 2, axis=2)[:, :, :5].copy()
+    b = _fwd(c64, inp)
+    assert np.array_equal(a, b)
+
+
+def test_token_permutation_equivariance():
+    cfg = configs.tiny(act_dtype="bf16", E=6, k=2)
+    inp = gen.make_inputs(cfg, 9)
+    a = _fwd(cfg, inp)
+    perm = np.random.default_rng(0).permutation(9)
+    inp.x, inp.logits = inp.x[perm].copy(), inp.logits[perm].copy()
+    b = _fwd(cfg, inp)
+    assert np.array_equal(a[perm], b)
+
+
+def test_token_subset_equals_full():
+    cfg = configs.tiny(E=5, k=2)
+    inp = gen.make_inputs(cfg, 11)
+    full = _fwd(cfg, inp)
+    sel = np.array([10, 3, 3, 0])
+    part, _ = oracle.forward(cfg, inp, sel=sel)
+    assert np.array_equal(part, full[sel])
+
+
+# --------------------------------------------------------------------------- stage functions
+
+def test_stage_functions_compose_to_forward():
+    cfg = configs.tiny(E=5, k=2, fc1_bias=True, fc2_bias=True)
+    inp = gen.make_inputs(cfg, 8)
+    ids, w = oracle.route(cfg, inp.logits)
+    perm = oracle.permute(cfg, ids, 4)
+    rows = np.where(perm["sorted_assign"] >= 0)[0]
+    a = perm["sorted_assign"][rows]
+    expert = np.repeat(np.arange(cfg.E), np.diff(perm["padded_offsets"]))[rows]
+    h = oracle.fc1_rows(cfg, inp, a // cfg.k, expert)
+    y = oracle.fc2_rows(cfg, inp, h.astype(np.float32), np.arange(len(rows)), expert)
+    Y = np.zeros((perm["rows"], cfg.H), np.float32)
+    Y[rows] = y
+    out64, _ = oracle.combine(cfg, Y, perm["assign_pos"], w.astype(np.float32))
+    ref = _fwd(cfg, inp)
+    # only the f32 storage of h, y and w separates the two
+    assert np.max(np.abs(out64 - ref)) < 1e-5 * rms(ref)
+
+
+# --------------------------------------------------------------------------- rounding
+
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([
+        rng.normal(0, 1, 20000), rng.normal(0, 1e30, 200), rng.normal(0, 1e-38, 200),
+        np.array([0.0, -0.0, 1.0, -2.5, 3.3895313892515355e38, 1e-45, -1e-40]),
+    ]).astype(np.float32)
+    # include exact ties: float32 values with the low 16 bits equal to 0x8000
+    ties = (rng.integers(0x3F000000, 0x40000000, 500, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    v = np.concatenate([v, ties.view(np.float32)])
+    ours = oracle.round_bf16(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_round_bf16_is_single_rounding_from_double():
+    # 1 + 2^-8 is exactly half way between bf16 neighbours 1 and 1 + 2^-7: ties to even.
+    # Slightly above the half-way point must round up even though the float32
+    # nearest to it is the half-way point itself.
+    v = np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8], np.float64)
+    out = oracle.round_bf16(v)
+    assert out.tolist() == [0x3F80, 0x3F81, 0x3F82]
+
+
+# --------------------------------------------------------------------------- golden, by hand
+
+def test_golden_hand_examples():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    assert len(cases) >= 2
+    for case in cases:
+        c = case["config"]
+        cfg = configs.tiny(**c)
+        T = case["T"]
+        inp = gen.make_inputs(cfg, T)
+        inp.x[...] = np.asarray(case["x"], np.float32)
+        inp.logits[...] = np.asarray(case["logits"], np.float32)
+        inp.w1[...] = case["w1_fill"]
+        for e, n, byte, val in case["w1_set"]:
+            inp.w1[e, n, byte] = val
+        inp.s1[...] = np.asarray(case["s1"], np.float32).reshape(inp.s1.shape)
+        inp.w2[...] = case["w2_fill"]
+        for e, n, byte, val in case["w2_set"]:
+            inp.w2[e, n, byte] = val
+        inp.s2[...] = case["s2_fill"]
+        out64, _ = oracle.forward(cfg, inp)
+        assert np.allclose(out64, np.asarray(case["expect"]), rtol=1e-15, atol=1e-15), case["name"]
