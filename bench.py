@@ -1,0 +1,225 @@
+"""Throughput of the weight-only-quantized MoE forward on one MI355X.
+
+A step is one whole forward (route, permute, fc1+SwiGLU, fc2, combine) over one batch of
+synthetic tokens, launched through the library's C ABI entry points. Inputs are resident
+in HBM before the timed region. Several device copies of the expert stacks are rotated
+from step to step so that the 256 MB Infinity Cache cannot serve a step's weights from
+the previous step.
+
+Default workload: the decode-shaped int4 layer (T=64, H=I=2880, E=32, k=4, 4-bit,
+block 32, bf16 scales, interleaved SwiGLU with alpha 1.702, beta 1, limit 7, bf16 biases).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "tokens/s per QMoE layer + weight-stream HBM GB/s (decode T<=64; prefill T=4096)"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--bits", type=int, default=4)
+    ap.add_argument("--block", type=int, default=32)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32)
+    return ap.parse_args()
+
+
+def workload(args):
+    from synth import configs
+    cfg = configs.ALL[args.workload]
+    if args.workload == "c5":
+        cfg = configs.c5_point(args.bits, args.block)
+    T = args.T if args.T is not None else (64 if args.workload == "c2" else max(cfg.T_points))
+    return cfg, T
+
+
+def stack_bytes(cfg, N, K, bias):
+    w = N * K * cfg.bits // 8
+    sb = 2 if cfg.scale_dtype == "bf16" else 4
+    ab = 2 if cfg.act_dtype == "bf16" else 4
+    s = N * (cfg.nblocks(K) if cfg.block_size else 1) * sb
+    return w + s + (N * ab if bias else 0)
+
+
+def algorithmic(cfg, T, counts):
+    """Minimum bytes each launch must move, and the forward's flops (real rows only)."""
+    ab = 2 if cfg.act_dtype == "bf16" else 4
+    A = T * cfg.k
+    touched = int(np.count_nonzero(counts))
+    fc1_e = stack_bytes(cfg, cfg.n1, cfg.H, cfg.fc1_bias)
+    if cfg.has_fc3:
+        fc1_e += stack_bytes(cfg, cfg.I, cfg.H, cfg.fc1_bias)
+    fc2_e = stack_bytes(cfg, cfg.H, cfg.I, cfg.fc2_bias)
+    fc1 = touched * fc1_e + T * cfg.H * ab + A * cfg.I * ab
+    fc2 = touched * fc2_e + A * cfg.I * ab + A * cfg.H * 4
+    weights = touched * (fc1_e + fc2_e)
+    flops = 2 * A * (cfg.n1 * cfg.H + (cfg.I * cfg.H if cfg.has_fc3 else 0) + cfg.I * cfg.H)
+    return dict(touched=touched, fc1_bytes=fc1, fc2_bytes=fc2, weight_bytes=weights, flops=flops,
+                fc1_flops=2 * A * (cfg.n1 + (cfg.I if cfg.has_fc3 else 0)) * cfg.H)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the forward runs on a single MI355X; "
+              "multi-GPU sharding is described in DESIGN.md and not launched here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_quantized_softmax_amd as qm
+    from synth import gen
+    from tests.gpu_helpers import DeviceInputs, params_for
+
+    cfg, T = workload(args)
+    torch.cuda.set_device(0)
+    print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
+    inp = gen.make_inputs(cfg, T)
+    d = DeviceInputs(inp)
+    p = params_for(cfg, T)
+    qm.qmoe_validate(p)
+
+    per_copy = sum(t.numel() * t.element_size() for st in (d.fc1, d.fc2, d.fc3) if st
+                   for t in st if t is not None)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(per_copy, 1)) + 1)
+    copies = min(copies, 64)
+    stacks = [(d.fc1, d.fc2, d.fc3)]
+    for _ in range(copies - 1):
+        stacks.append(tuple(None if st is None else tuple(None if t is None else t.clone() for t in st)
+                            for st in (d.fc1, d.fc2, d.fc3)))
+
+    # stage buffers (the same kernels qmoe_forward launches, called one by one)
+    A = T * cfg.k
+    rows, tiles = qm.qmoe_max_rows(p), qm.qmoe_max_tiles(p)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    adt = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+    ids = torch.empty((T, cfg.k), **i32)
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(cfg.E, **i32)
+    offs = torch.empty(cfg.E + 1, **i32)
+    sa = torch.empty(rows, **i32)
+    pos = torch.empty(A, **i32)
+    tl = torch.empty((tiles, 2), **i32)
+    nt = torch.empty(1, **i32)
+    scratch = torch.empty(max(qm.qmoe_permute_scratch_size(p), 256), dtype=torch.uint8, device="cuda")
+    h = torch.empty((rows, cfg.I), dtype=adt, device="cuda")
+    y = torch.empty((rows, cfg.H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, cfg.H), dtype=adt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+
+    def step(i, timed):
+        fc1, fc2, fc3 = stacks[i % copies]
+        qm.qmoe_route(p, d.logits, ids, w, stream)
+        qm.qmoe_permute(p, ids, counts, offs, sa, pos, tl, nt, scratch, stream)
+        if timed:
+            ev[i][0].record(stream)
+        qm.qmoe_grouped_gemm_fc1_swiglu(p, d.x, sa, tl, nt, fc1, fc3, h, stream)
+        if timed:
+            ev[i][1].record(stream)
+            ev[i][2].record(stream)
+        qm.qmoe_grouped_gemm_fc2(p, h, tl, nt, fc2, y, stream)
+        if timed:
+            ev[i][3].record(stream)
+        qm.qmoe_combine(p, y, pos, w, None, out, stream)
+
+    print(f"[bench] {copies} weight copies of {per_copy / 1e6:.1f} MB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fc1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    fc2_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    # whole-forward entry point, same inputs, for reference
+    ws = qm.alloc_workspace(p)
+    for i in range(args.warmup):
+        fc1, fc2, fc3 = stacks[i % copies]
+        qm.qmoe_forward(p, d.x, d.logits, fc1, fc2, fc3, None, out, ws, stream)
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for i in range(args.steps):
+        fc1, fc2, fc3 = stacks[i % copies]
+        qm.qmoe_forward(p, d.x, d.logits, fc1, fc2, fc3, None, out, ws, stream)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - f0) * 1e3 / args.steps
+
+    alg = algorithmic(cfg, T, counts.cpu().numpy())
+    fc1_gbps = alg["fc1_bytes"] / (fc1_ms * 1e-3) / 1e9
+    stream_gbps = alg["weight_bytes"] / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
+    decode = T <= 64
+    if decode or alg["flops"] / alg["weight_bytes"] < 300:
+        roof = dict(bound="hbm", achieved=round(fc1_gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(fc1_gbps / HBM_PEAK_GBPS, 4), traffic=None)
+    else:
+        tf = alg["fc1_flops"] / (fc1_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(T, args.cpu_tokens)
+        threads = min(16, os.cpu_count() or 1)
+        sel = np.arange(n)
+        print(f"[bench] cpu oracle on {n} tokens, {threads} threads", file=sys.stderr, flush=True)
+        c0 = time.perf_counter()
+        oracle.forward(cfg, inp, sel=sel, nthreads=threads)
+        csec = time.perf_counter() - c0
+        cpu = dict(value=round(n / csec, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"first {n} of the {T} tokens of the same workload, fp64, {csec:.1f} s")
+
+    value = T / (ms_per_step * 1e-3)
+    line = dict(
+        metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms_per_step, 5), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16" if cfg.act_dtype == "bf16" else "f32",
+        data="synthetic",
+        config=dict(workload=f"{cfg.name} T={T}", T=T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k,
+                    bits=cfg.bits, block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
+                    weight_copies=copies, touched_experts=alg["touched"]),
+        roofline=roof,
+        cpu_baseline=cpu,
+        weight_stream_GBps=round(stream_gbps, 1),
+        kernel_ms=dict(fc1=round(fc1_ms, 5), fc2=round(fc2_ms, 5)),
+        forward_entry_ms=round(fwd_ms, 5),
+        algorithmic=dict(fc1_bytes=alg["fc1_bytes"], fc2_bytes=alg["fc2_bytes"],
+                         weight_bytes=alg["weight_bytes"], flops=alg["flops"]),
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * qmoe.h -- C ABI of the weight-only-quantized mixture-of-experts forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the QMoE / QMoEWoQ block forward:
+ *   out[t] = sum_{j<k} w[t,j] * FFN_{e[t,j]}(x[t])  (+ shared_output[t])
+ * where the router picks the k experts with the largest router logits and
+ * weighs them by their softmax probability (optionally renormalised), and
+ *   FFN_e(x) = dequant(W2_e) . act(dequant(W1_e) . x + b1_e) + b2_e,
+ *   dequant(q) = (q - 2^(bits-1)) * scale   per output row or per K-block.
+ * Sources: ClikaRT "QMoEWoQ" page (class description: expert weights stay
+ * quantized and are decoded block by block inside the GEMM dot; forward:
+ * x [T,H] and router_logits [T,E] give [T,H] in x's dtype, optional
+ * shared_output folded into the combine); CLIKA "MoE" page (top-k routing,
+ * gated FFN, combine under the router weights; routing kwargs); CLIKA
+ * "QLinearWoQ" page (y = x @ dequant(W).T + bias); graiphic "QMoE" page (input
+ * tensors and their shapes; attributes activation_alpha/beta, activation_type,
+ * block_size, expert_weight_bits, k, normalize_routing_weights, swiglu_fusion,
+ * swiglu_limit).
+ *
+ * Conventions shared by every entry point:
+ *  - Every array argument is a DEVICE pointer owned by the caller, row-major and
+ *    densely packed. The library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued
+ *    asynchronously on it; no call synchronises with the host.
+ *  - Parameters are validated on the host before anything is enqueued; on a
+ *    validation failure nothing is launched and the call returns a non-zero
+ *    qmoe_status, with a message available from qmoe_last_error().
+ *  - A launch failure reported by the HIP runtime returns QMOE_ERR_DEVICE. A
+ *    fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - num_tokens == 0 is valid: the call returns QMOE_OK and enqueues nothing.
+ *  - Calls on different streams with distinct output buffers may run concurrently.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_ERR_INVALID = 1,      /* a parameter outside its documented range */
+  QMOE_ERR_SHAPE = 2,        /* sizes inconsistent with each other or with the layout */
+  QMOE_ERR_DTYPE = 3,        /* an element type combination that is not accepted */
+  QMOE_ERR_UNSUPPORTED = 4,  /* valid on the pages but not implemented here */
+  QMOE_ERR_UNBOUND = 5,      /* a required pointer is NULL (an unbound weight slot) */
+  QMOE_ERR_DEVICE = 6        /* the HIP runtime reported an error */
+} qmoe_status;
+
+typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1 } qmoe_dtype;
+
+/* activation_type of the graiphic "QMoE" page. gelu is not provided. */
+typedef enum {
+  QMOE_ACT_SWIGLU = 0,
+  QMOE_ACT_IDENTITY = 1,
+  QMOE_ACT_RELU = 2,
+  QMOE_ACT_SILU = 3
+} qmoe_act;
+
+typedef struct {
+  /* T, H, I, E, k: tokens, hidden_size, inter_size, num_experts, top-k
+     (ClikaRT QMoEWoQ::make counts; graiphic QMoE attribute k). 1 <= k <= E <= 1024. */
+  int64_t num_tokens, hidden_size, inter_size, num_experts, k;
+  /* expert_weight_bits: 4 (two fields per byte, element 2j in the low nibble) or 8. */
+  int32_t expert_weight_bits;
+  /* block_size: 0 = one scale per output row; else a power of two >= 16, one scale
+     per block_size elements along K. A K that block_size does not divide is
+     accepted with a shorter last block unless strict_blocks is set. */
+  int32_t block_size;
+  /* swiglu_fusion: 0 separate gate (fc1) and up (fc3) stacks; 1 fused, row 2i gate and
+     row 2i+1 up; 2 fused, rows [0,I) gate and [I,2I) up. Must be 0 unless swiglu. */
+  int32_t swiglu_fusion;
+  int32_t activation;                /* qmoe_act */
+  int32_t normalize_routing_weights; /* non-zero: divide the k weights by their sum */
+  /* SwiGLU: h = g' * sigmoid(alpha * g') * (u' + beta), g' = min(g, L),
+     u' = clamp(u, -L, L). swiglu_limit <= 0 or +inf means no clamp. */
+  float swiglu_alpha, swiglu_beta, swiglu_limit;
+  int32_t act_dtype;    /* qmoe_dtype of x, router logits, biases, shared_output, output */
+  int32_t scale_dtype;  /* qmoe_dtype of the scales */
+  /* Rows per expert tile of the grouping. 0 = the library's choice for these shapes
+     (qmoe_tile_m). Every call of one forward must use the same value. */
+  int32_t tile_m;
+  int32_t strict_blocks; /* non-zero: reject a K that block_size does not divide */
+} qmoe_params;
+
+/* One quantized expert stack (graiphic QMoE fcN_experts_weights / fcN_scales / fcN_experts_bias).
+   weights: uint8 [E, N, K*bits/8]; scales: scale_dtype [E, N] (block_size 0) or
+   [E, N, ceil(K/block_size)]; bias: act_dtype [E, N] or NULL. */
+typedef struct {
+  const void* weights;
+  const void* scales;
+  const void* bias;
+} qmoe_stack;
+
+/* Checks the parameters; QMOE_OK when every entry point accepts them. */
+qmoe_status qmoe_validate(const qmoe_params* p);
+
+/* The tile height used when p->tile_m == 0, from shapes only (never from routed data). */
+int32_t qmoe_tile_m(const qmoe_params* p);
+
+/* Worst-case padded rows and tiles of the grouping for these parameters. */
+int64_t qmoe_max_rows(const qmoe_params* p);
+int64_t qmoe_max_tiles(const qmoe_params* p);
+
+/* Bytes of device scratch qmoe_permute needs (may be 0). */
+size_t qmoe_permute_scratch_size(const qmoe_params* p);
+
+/* Bytes of device workspace qmoe_forward needs (256-byte aligned start required). */
+size_t qmoe_workspace_size(const qmoe_params* p);
+
+/*
+ * Routing (CLIKA "MoE" page: router picks top-k experts per token; routing_mode
+ * "softmax_topk", renormalize; graiphic "QMoE" page: k, normalize_routing_weights;
+ * ClikaRT "QMoEWoQ" page: the caller hands router logits to forward).
+ *   router_logits [T, E] act_dtype  ->  topk_ids [T, k] int32, topk_w [T, k] float32.
+ * Experts are selected by descending logit, equal logits in ascending expert index
+ * (-0 equals +0); slot j holds the j-th selected expert. topk_w = softmax over all
+ * E logits at the selected experts, divided by their sum if normalising.
+ * Logits must be finite; the result for NaN or Inf logits is unspecified.
+ */
+qmoe_status qmoe_route(const qmoe_params* p, const void* router_logits, int32_t* topk_ids,
+                       float* topk_w, void* stream);
+
+/*
+ * Grouping of the T*k assignments a = t*k + j by expert (the per-expert work lists
+ * behind the per-expert kernels of the ClikaRT "QMoEWoQ" page).
+ *   topk_ids [T*k] int32 in [0, E)  ->
+ *   counts [E]              assignments per expert;
+ *   padded_offsets [E+1]    first row of each expert; each group padded to a multiple of M;
+ *   sorted_assign [max_rows] a at each row, ascending a within an expert, -1 on padding
+ *                           (rows beyond padded_offsets[E] are left untouched);
+ *   assign_pos [T*k]        row of each assignment (sorted_assign[assign_pos[a]] == a);
+ *   tile_list [max_tiles, 2] (expert, valid rows) of tile i, which covers rows [i*M, i*M+M);
+ *   num_tiles [1]           number of tiles written.
+ * M = qmoe_tile_m(p) or p->tile_m. scratch: qmoe_permute_scratch_size(p) bytes (may be NULL
+ * when that size is 0). The result is deterministic and independent of scheduling.
+ * Ids outside [0, E) give an unspecified grouping.
+ */
+qmoe_status qmoe_permute(const qmoe_params* p, const int32_t* topk_ids, int32_t* counts,
+                         int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                         int32_t* tile_list, int32_t* num_tiles, void* scratch,
+                         size_t scratch_bytes, void* stream);
+
+/*
+ * fc1 (and fc3) grouped GEMM over the quantized expert stacks with the activation
+ * fused into its epilogue (graiphic "QMoE" page: fc1/fc3 inputs, activation
+ * attributes, swiglu_fusion; ClikaRT "QMoEWoQ" page: each weight block is decoded
+ * inside the GEMM dot, never as a dense copy).
+ *   x [T, H] act_dtype; sorted_assign, tile_list, num_tiles from qmoe_permute;
+ *   fc1: weights [E, f*I, H*bits/8] (f = 2 for fused SwiGLU, else 1);
+ *   fc3: separate up stack [E, I, H*bits/8] (only with swiglu and swiglu_fusion 0);
+ *   h [max_rows, I] act_dtype (written for every real row of every tile; padding rows
+ *   of a tile are written as zeros).
+ * Row r of tile i (expert e, r < valid) computes, for a = sorted_assign[i*M + r] and
+ * t = a / k: z = x[t] . dequant(W1_e)^T + b1_e, then h = act(z) (SwiGLU on the
+ * gate/up pair selected by swiglu_fusion).
+ */
+qmoe_status qmoe_grouped_gemm_fc1_swiglu(const qmoe_params* p, const void* x,
+                                         const int32_t* sorted_assign, const int32_t* tile_list,
+                                         const int32_t* num_tiles, qmoe_stack fc1, qmoe_stack fc3,
+                                         void* h, void* stream);
+
+/*
+ * fc2 grouped GEMM (graiphic "QMoE" page: fc2_experts_weights [E, H, I*bits/8],
+ * fc2_scales, fc2_experts_bias).
+ *   h [max_rows, I] act_dtype (rows of tile i from qmoe_grouped_gemm_fc1_swiglu);
+ *   y [max_rows, H] float32: y = h . dequant(W2_e)^T + b2_e for the real rows of each tile.
+ */
+qmoe_status qmoe_grouped_gemm_fc2(const qmoe_params* p, const void* h, const int32_t* tile_list,
+                                  const int32_t* num_tiles, qmoe_stack fc2, float* y,
+                                  void* stream);
+
+/*
+ * Weighted combine (CLIKA "MoE" page: outputs combine under the router weights;
+ * ClikaRT "QMoEWoQ" page forward: shared_output folds into the same epilogue and the
+ * result takes x's dtype).
+ *   out[t, :] = round( sum_{j<k} topk_w[t, j] * y[assign_pos[t*k + j], :] + shared[t, :] )
+ * summed in float32 in slot order j, rounded once (nearest-even) to act_dtype.
+ * shared_output [T, H] act_dtype may be NULL. No atomics: each output is written once.
+ */
+qmoe_status qmoe_combine(const qmoe_params* p, const float* y, const int32_t* assign_pos,
+                         const float* topk_w, const void* shared_output, void* output,
+                         void* stream);
+
+/*
+ * The whole forward: route, permute, fc1 + activation, fc2, combine (ClikaRT
+ * "QMoEWoQ" page, forward; graiphic "QMoE" page, the node's inputs and attributes).
+ *   input [T, H] act_dtype; router_logits [T, E] act_dtype; shared_output [T, H] or NULL;
+ *   output [T, H] act_dtype; fc3 ignored unless swiglu with swiglu_fusion 0.
+ *   workspace: at least qmoe_workspace_size(p) bytes, 256-byte aligned; its contents on
+ *   entry do not matter and are clobbered.
+ * Nothing is synchronised and no device-side count returns to the host, so the call
+ * can be captured in a HIP graph.
+ */
+qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* router_logits,
+                         qmoe_stack fc1, qmoe_stack fc2, qmoe_stack fc3,
+                         const void* shared_output, void* output, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Message of the last failing call on this thread (library-owned, valid until the next
+   call on this thread); "" after a successful call. */
+const char* qmoe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

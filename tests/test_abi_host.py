@@ -1,0 +1,181 @@
+"""The C ABI library without a GPU: it loads, exports every declared entry point, and
+rejects bad parameters and unbound pointers on the host before any device work."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_softmax_amd as qm
+from weight_only_quantized_softmax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libqmoe.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.EXPORTS) == set(names)
+
+
+def good(**kw):
+    base = dict(num_tokens=64, hidden_size=2880, inter_size=2880, num_experts=32, k=4,
+                expert_weight_bits=4, block_size=32, swiglu_fusion=1, swiglu_alpha=1.702,
+                swiglu_beta=1.0, swiglu_limit=7.0)
+    base.update(kw)
+    T = base.pop("num_tokens")
+    H, I, E, k = (base.pop(n) for n in ("hidden_size", "inter_size", "num_experts", "k"))
+    return qm.make_params(T, H, I, E, k, **base)
+
+
+def status(p):
+    return _lib.load().qmoe_validate(p)
+
+
+def test_good_params_validate(lib):
+    assert status(good()) == _lib.QMOE_OK
+    assert lib.qmoe_last_error() == b""
+    assert qm.qmoe_workspace_size(good()) > 0
+
+
+BAD = [
+    (dict(k=0), _lib.QMOE_ERR_INVALID),
+    (dict(k=33, num_experts=64), _lib.QMOE_ERR_UNSUPPORTED),
+    (dict(k=5, num_experts=4), _lib.QMOE_ERR_INVALID),
+    (dict(num_experts=0), _lib.QMOE_ERR_UNSUPPORTED),
+    (dict(num_experts=513), _lib.QMOE_ERR_UNSUPPORTED),
+    (dict(expert_weight_bits=0), _lib.QMOE_ERR_INVALID),
+    (dict(expert_weight_bits=2), _lib.QMOE_ERR_INVALID),
+    (dict(block_size=24), _lib.QMOE_ERR_INVALID),
+    (dict(block_size=8), _lib.QMOE_ERR_INVALID),
+    (dict(block_size=1024), _lib.QMOE_ERR_UNSUPPORTED),
+    (dict(swiglu_fusion=3), _lib.QMOE_ERR_INVALID),
+    (dict(activation="identity", swiglu_fusion=1), _lib.QMOE_ERR_INVALID),
+    (dict(num_tokens=-1), _lib.QMOE_ERR_INVALID),
+    (dict(hidden_size=2881), _lib.QMOE_ERR_SHAPE),
+    (dict(hidden_size=2880 + 16), _lib.QMOE_ERR_UNSUPPORTED),  # bf16 path needs K % 32
+    (dict(block_size=128, strict_blocks=True), _lib.QMOE_ERR_SHAPE),  # 2880 % 128 != 0
+    (dict(tile_m=8), _lib.QMOE_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD, ids=[str(k) for k, _ in BAD])
+def test_bad_params_rejected(lib, kw, want):
+    p = good(**kw)
+    assert status(p) == want
+    assert lib.qmoe_last_error() != b""
+    assert lib.qmoe_workspace_size(p) == 0
+
+
+def test_ragged_block_accepted_without_strict(lib):
+    assert status(good(block_size=128)) == _lib.QMOE_OK
+
+
+def test_bad_dtype_enum(lib):
+    p = good()
+    p.act_dtype = 7
+    assert status(p) == _lib.QMOE_ERR_DTYPE
+    p = good()
+    p.scale_dtype = -1
+    assert status(p) == _lib.QMOE_ERR_DTYPE
+
+
+def test_f32_tile_fits_lds(lib):
+    p = good(act_dtype="f32", hidden_size=128, inter_size=256, block_size=32)
+    assert status(p) == _lib.QMOE_OK
+    assert lib.qmoe_tile_m(p) == 16
+    p = good(act_dtype="f32", hidden_size=4096, inter_size=4096, block_size=32)
+    assert lib.qmoe_tile_m(p) == 2
+    assert status(good(act_dtype="f32", hidden_size=4096, inter_size=4096, tile_m=16)) == \
+        _lib.QMOE_ERR_UNSUPPORTED
+
+
+def test_max_rows_and_tiles(lib):
+    p = good(num_tokens=64)  # T*k = 256, M = 16, E = 32
+    assert lib.qmoe_tile_m(p) == 16
+    assert lib.qmoe_max_tiles(p) == 256 // 16 + 32
+    assert lib.qmoe_max_rows(p) == (256 // 16 + 32) * 16
+    p = good(num_tokens=1)
+    assert lib.qmoe_max_tiles(p) == 0 + 4
+
+
+# Null pointers are rejected before any launch (no GPU is touched on these paths).
+def test_unbound_pointers(lib):
+    p = good()
+    V = ctypes.c_void_p
+    assert lib.qmoe_route(p, None, V(16), V(16), None) == _lib.QMOE_ERR_UNBOUND
+    assert b"router_logits" in lib.qmoe_last_error()
+    assert lib.qmoe_combine(p, V(16), None, V(16), None, V(16), None) == _lib.QMOE_ERR_UNBOUND
+    st = _lib.QmoeStack(weights=16, scales=None, bias=None)
+    full = _lib.QmoeStack(weights=16, scales=16, bias=None)
+    assert lib.qmoe_grouped_gemm_fc2(p, V(16), V(16), V(16), st, V(16), None) == \
+        _lib.QMOE_ERR_UNBOUND
+    assert b"fc2.scales" in lib.qmoe_last_error()
+    # separate gate/up stacks need fc3
+    p0 = good(swiglu_fusion=0)
+    assert lib.qmoe_grouped_gemm_fc1_swiglu(p0, V(16), V(16), V(16), V(16), full,
+                                            _lib.QmoeStack(), V(16), None) == \
+        _lib.QMOE_ERR_UNBOUND
+    assert b"fc3" in lib.qmoe_last_error()
+    assert lib.qmoe_forward(p, V(16), V(16), full, full, _lib.QmoeStack(), None, V(16), None, 0,
+                            None) == _lib.QMOE_ERR_UNBOUND
+    assert b"workspace" in lib.qmoe_last_error()
+
+
+def test_workspace_checks(lib):
+    p = good()
+    V = ctypes.c_void_p
+    full = _lib.QmoeStack(weights=16, scales=16, bias=None)
+    need = lib.qmoe_workspace_size(p)
+    assert lib.qmoe_forward(p, V(16), V(16), full, full, _lib.QmoeStack(), None, V(16), V(256),
+                            need - 1, None) == _lib.QMOE_ERR_INVALID
+    assert lib.qmoe_forward(p, V(16), V(16), full, full, _lib.QmoeStack(), None, V(16), V(300),
+                            need, None) == _lib.QMOE_ERR_INVALID
+    assert b"aligned" in lib.qmoe_last_error()
+
+
+def test_permute_scratch(lib):
+    small = good(num_tokens=64)
+    assert lib.qmoe_permute_scratch_size(small) == 0
+    big = good(num_tokens=4096, num_experts=64, k=6)
+    need = lib.qmoe_permute_scratch_size(big)
+    assert need > 0
+    V = ctypes.c_void_p
+    args = [V(16)] * 7
+    assert lib.qmoe_permute(big, *args, None, 0, None) == _lib.QMOE_ERR_UNBOUND
+    assert lib.qmoe_permute(big, *args, V(16), need - 1, None) == _lib.QMOE_ERR_INVALID
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    p = good(num_tokens=0)
+    assert status(p) == _lib.QMOE_OK
+    V = ctypes.c_void_p
+    # nothing is dereferenced or launched for T = 0, even with NULL buffers
+    assert lib.qmoe_route(p, None, None, None, None) == _lib.QMOE_OK
+    assert lib.qmoe_forward(p, None, None, _lib.QmoeStack(), _lib.QmoeStack(), _lib.QmoeStack(),
+                            None, None, None, 0, None) == _lib.QMOE_OK
+
+
+def test_infinite_limit_and_defaults_marshal(lib):
+    p = good(swiglu_limit=math.inf)
+    assert math.isinf(p.swiglu_limit)
+    assert status(p) == _lib.QMOE_OK

@@ -1,0 +1,364 @@
+"""Parity of the HIP path with the CPU oracle, stage by stage and end to end.
+
+Every input is seeded and synthetic (synth/). Routing indices and the grouping are
+compared bit for bit; floating outputs within the stated tolerance: max |err| <=
+1e-4 * RMS for fp32 activations and 2e-2 * RMS for bf16 activations, measured against
+the oracle's fp64 value before rounding. At full workload sizes the routing and grouping
+of all tokens are compared, and outputs on a sample of tokens the oracle evaluates one by
+one.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_softmax_amd as qm
+from synth import configs, gen
+from synth.gen import as_f32, store
+from tests.gpu_helpers import (TOL, DeviceInputs, dev, host, host_f64, max_excess_err,
+                               max_rel_err, params_for, rms)
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qm._lib.load()  # the HIP library must be present on a GPU machine
+    torch.cuda.init()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------- route
+
+def run_route(cfg, logits_np, T):
+    p = params_for(cfg, T)
+    lg = dev(logits_np, cfg.act_dtype)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    qm.qmoe_route(p, lg, ids, w)
+    torch.cuda.synchronize()
+    return host(ids), host(w)
+
+
+ROUTE_CASES = {
+    "c1": (configs.C1, 16), "c2-T64": (configs.C2, 64), "c3-T4096": (configs.C3, 4096),
+    "c4-T512": (configs.C4, 512), "c5-T4096": (configs.C5, 4096),
+    "E512-k8": (configs.tiny(E=512, k=8, act_dtype="bf16", logit_sigma=0.5), 300),
+    "E130-k32": (configs.tiny(E=130, k=32, act_dtype="f32", normalize=False), 100),
+    "E1-k1": (configs.tiny(E=1, k=1, act_dtype="bf16"), 7),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROUTE_CASES))
+def test_route_matches_oracle(name):
+    cfg, T = ROUTE_CASES[name]
+    say("route", name, cfg.E, cfg.k, T)
+    _, logits, _ = gen.gen_activations(cfg, T)
+    ids, w = run_route(cfg, logits, T)
+    rids, rw = oracle.route(cfg, logits)
+    assert np.array_equal(ids, rids)
+    assert np.max(np.abs(w - rw)) < 2e-6
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 6), (130, 4)])
+def test_route_ties_and_signed_zero(E, k):
+    cfg = configs.tiny(E=E, k=k, act_dtype="bf16")
+    rng = np.random.default_rng(E)
+    vals = np.array([-0.0, 0.0, 0.0, -1.5, 1.0, 1.0, 2.0], np.float32)
+    logits = store(vals[rng.integers(0, len(vals), size=(257, E))], "bf16")
+    logits[0, :] = 0x8000  # all -0: experts 0..k-1
+    logits[1, :] = store(np.full(E, 0.25, np.float32), "bf16")
+    ids, w = run_route(cfg, logits, 257)
+    rids, rw = oracle.route(cfg, logits)
+    assert np.array_equal(ids, rids)
+    assert ids[0].tolist() == list(range(k)) and ids[1].tolist() == list(range(k))
+    assert np.max(np.abs(w - rw)) < 2e-6
+
+
+# --------------------------------------------------------------------------- permute
+
+def run_permute(cfg, ids_np, T):
+    p = params_for(cfg, T)
+    M = qm.qmoe_tile_m(p)
+    rows, tiles = qm.qmoe_max_rows(p), qm.qmoe_max_tiles(p)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids = dev(np.ascontiguousarray(ids_np, np.int32))
+    counts = torch.full((cfg.E,), -5, **i32)
+    offs = torch.full((cfg.E + 1,), -5, **i32)
+    sa = torch.full((rows,), -5, **i32)
+    pos = torch.full((T * cfg.k,), -5, **i32)
+    tl = torch.full((tiles, 2), -5, **i32)
+    nt = torch.full((1,), -5, **i32)
+    scratch = torch.empty(max(qm.qmoe_permute_scratch_size(p), 4), dtype=torch.uint8, device="cuda")
+    qm.qmoe_permute(p, ids, counts, offs, sa, pos, tl, nt, scratch)
+    torch.cuda.synchronize()
+    return M, dict(counts=host(counts), padded_offsets=host(offs), sorted_assign=host(sa),
+                   assign_pos=host(pos), tiles=host(tl), num_tiles=int(host(nt)[0]))
+
+
+PERMUTE_CASES = [
+    # (E, k, T, skew): fused one-block path and multi-block path (T*k > 4096)
+    (32, 4, 1, 0.0), (32, 4, 8, 0.0), (32, 4, 64, 0.0), (128, 4, 512, 0.0), (8, 2, 4096, 6.0),
+    (64, 6, 4096, 0.0), (64, 6, 256, 0.0), (1, 1, 5000, 0.0), (7, 3, 3000, 50.0), (512, 8, 700, 0.0),
+]
+
+
+@pytest.mark.parametrize("E,k,T,skew", PERMUTE_CASES)
+def test_permute_matches_oracle(E, k, T, skew):
+    cfg = configs.tiny(E=E, k=k, act_dtype="bf16", H=64, I=64)
+    say("permute", E, k, T, skew)
+    ids = gen.gen_topk_ids(cfg, T, skew=skew)
+    M, got = run_permute(cfg, ids, T)
+    ref = oracle.permute(cfg, ids, M)
+    P, nt = ref["rows"], ref["num_tiles"]
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["padded_offsets"], ref["padded_offsets"])
+    assert np.array_equal(got["sorted_assign"][:P], ref["sorted_assign"])
+    assert np.all(got["sorted_assign"][P:] == -5)  # rows past the layout are untouched
+    assert np.array_equal(got["assign_pos"], ref["assign_pos"])
+    assert got["num_tiles"] == nt
+    assert np.array_equal(got["tiles"][:nt], ref["tiles"])
+
+
+# --------------------------------------------------------------------------- fc1 / fc2 stages
+
+def oracle_layout(cfg, T, M, seed=0):
+    ids = gen.gen_topk_ids(cfg, T, seed=seed, skew=2.0)
+    perm = oracle.permute(cfg, ids, M)
+    sa = perm["sorted_assign"]
+    expert_of_row = np.repeat(np.arange(cfg.E), np.diff(perm["padded_offsets"]))
+    return ids, perm, sa, expert_of_row
+
+
+STAGE_CFGS = {
+    "c1": configs.C1,
+    "c2-interleaved-b4-bs32-bias-clamp": configs.C2.with_(H=512, I=256, E=8),
+    "c3-separate-perrow": configs.C3.with_(H=1024, I=768, E=4, logit_skew=0.0),
+    "c4-b8-bs128-ragged-f32scale": configs.C4.with_(H=704, I=352, E=8),
+    "c5-b4-bs16": configs.c5_point(4, 16).with_(H=512, I=256, E=8),
+    "c5-b8-bs32": configs.c5_point(8, 32).with_(H=512, I=256, E=8),
+    "c5-b4-bs64": configs.c5_point(4, 64).with_(H=512, I=256, E=8),
+    "c5-b8-bs128": configs.c5_point(8, 128).with_(H=512, I=256, E=8),
+    "identity-b4-bs32": configs.tiny(activation="identity", fusion=0, act_dtype="bf16",
+                                     scale_dtype="bf16", H=256, I=128, block_size=32,
+                                     fc1_bias=True, fc2_bias=True),
+    "relu-b8-perrow": configs.tiny(activation="relu", fusion=0, act_dtype="bf16", bits=8,
+                                   block_size=0, H=256, I=128),
+    "silu-f32": configs.tiny(activation="silu", fusion=0, H=128, I=64, fc1_bias=True),
+    "f32-interleaved-b8-bias": configs.tiny(fusion=1, bits=8, H=96, I=80, block_size=32,
+                                            fc1_bias=True, fc2_bias=True, limit=3.0),
+}
+
+
+def _stage_inputs(name, T):
+    cfg = STAGE_CFGS[name]
+    assert cfg.H % 32 == 0 or cfg.act_dtype == "f32"
+    inp = gen.make_inputs(cfg, T)
+    p = params_for(cfg, T)
+    M = qm.qmoe_tile_m(p)
+    return cfg, inp, p, M
+
+
+@pytest.mark.parametrize("name", sorted(STAGE_CFGS))
+def test_fc1_stage(name):
+    T = 40
+    cfg, inp, p, M = _stage_inputs(name, T)
+    say("fc1", name, cfg.H, cfg.I, cfg.E, "M", M)
+    ids, perm, sa, erow = oracle_layout(cfg, T, M)
+    d = DeviceInputs(inp)
+    rows = qm.qmoe_max_rows(p)
+    sa_pad = np.full(rows, -1, np.int32)
+    sa_pad[:len(sa)] = sa
+    tl = np.zeros((qm.qmoe_max_tiles(p), 2), np.int32)
+    tl[:perm["num_tiles"]] = perm["tiles"]
+    tdt = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+    h = torch.full((rows, cfg.I), 7.0, dtype=tdt, device="cuda")
+    qm.qmoe_grouped_gemm_fc1_swiglu(p, d.x, dev(sa_pad), dev(tl),
+                                    dev(np.array([perm["num_tiles"]], np.int32)), d.fc1, d.fc3, h)
+    torch.cuda.synchronize()
+    got = host_f64(h, cfg.act_dtype)
+    real = np.where(sa >= 0)[0]
+    ref = oracle.fc1_rows(cfg, inp, sa[real] // cfg.k, erow[real], nthreads=NTHREADS)
+    err = max_rel_err(got[real], ref)
+    if cfg.act_dtype == "bf16":
+        # h is stored in bfloat16: the bound applies to the error beyond that rounding
+        ex = max_excess_err(got[real], ref)
+        say(f"  fc1 max err / rms {err:.3e}, beyond bf16 storage {ex:.3e}")
+        assert ex <= TOL["bf16"]
+    else:
+        say(f"  fc1 max err / rms {err:.3e}")
+        assert err <= TOL["f32"]
+    pads = np.where(sa < 0)[0]
+    assert np.all(got[pads] == 0.0)
+
+
+@pytest.mark.parametrize("name", sorted(STAGE_CFGS))
+def test_fc2_stage(name):
+    T = 40
+    cfg, inp, p, M = _stage_inputs(name, T)
+    say("fc2", name)
+    ids, perm, sa, erow = oracle_layout(cfg, T, M, seed=1)
+    rows = qm.qmoe_max_rows(p)
+    hin = gen.gen_stage_h(cfg, rows, sigma=3.0)
+    hin[sa.size:] = 0
+    hin[:sa.size][sa < 0] = 0  # padding rows hold zeros, as fc1 writes them
+    d = DeviceInputs(inp)
+    tl = np.zeros((qm.qmoe_max_tiles(p), 2), np.int32)
+    tl[:perm["num_tiles"]] = perm["tiles"]
+    y = torch.full((rows, cfg.H), 7.0, dtype=torch.float32, device="cuda")
+    qm.qmoe_grouped_gemm_fc2(p, dev(hin, cfg.act_dtype), dev(tl),
+                             dev(np.array([perm["num_tiles"]], np.int32)), d.fc2, y)
+    torch.cuda.synchronize()
+    got = host(y).astype(np.float64)
+    real = np.where(sa >= 0)[0]
+    ref = oracle.fc2_rows(cfg, inp, hin, real, erow[real], nthreads=NTHREADS)
+    err = max_rel_err(got[real], ref)
+    say("  fc2 max err / rms", err)
+    # y stays fp32 on both paths; the products of bf16 inputs are exact, so it is far
+    # inside the bf16 bound
+    assert err <= (1e-4 if cfg.act_dtype == "f32" else 1e-3)
+
+
+# --------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dtype,H,shared", [("bf16", 2880, False), ("bf16", 2048, True),
+                                             ("f32", 1442, True), ("f32", 128, False)])
+def test_combine_stage(dtype, H, shared):
+    c = configs.tiny(E=16, k=4, H=H, I=64, act_dtype=dtype)
+    T = 33
+    p = params_for(c, T)
+    ids = gen.gen_topk_ids(c, T)
+    perm = oracle.permute(c, ids, qm.qmoe_tile_m(p))
+    y = gen.gen_stage_y(c, perm["rows"])
+    w = gen.gen_topk_w(c, T)
+    sh = gen.gen_activations(c, T, shared=True)[2] if shared else None
+    out = torch.empty((T, H), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device="cuda")
+    qm.qmoe_combine(p, dev(y), dev(perm["assign_pos"]), dev(w),
+                    dev(sh, dtype) if sh is not None else None, out)
+    torch.cuda.synchronize()
+    ref64, _ = oracle.combine(c, y, perm["assign_pos"], w, sh)
+    assert max_rel_err(host_f64(out, dtype), ref64) <= TOL[dtype]
+
+
+def test_combine_rounds_to_nearest_even():
+    # k = 1 with weight 1: the output is the bf16 rounding of y itself.
+    c = configs.tiny(E=2, k=1, H=4096, act_dtype="bf16")
+    T = 8
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0x3F000000, 0x40000000, size=(T, c.H), dtype=np.uint32)
+    bits[:, ::2] = (bits[:, ::2] & 0xFFFF0000) | 0x8000  # exact ties
+    y = bits.view(np.float32)
+    p = params_for(c, T)
+    out = torch.empty((T, c.H), dtype=torch.bfloat16, device="cuda")
+    qm.qmoe_combine(p, dev(y), dev(np.arange(T, dtype=np.int32)), dev(np.ones((T, 1), np.float32)),
+                    None, out)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(host(out), ref)
+
+
+# --------------------------------------------------------------------------- end to end
+
+def forward_gpu(cfg, inp, d=None, reshape3d=False):
+    T = inp.x.shape[0]
+    d = d or DeviceInputs(inp)
+    p = params_for(cfg, T)
+    x = d.x.view(1, T, cfg.H) if reshape3d else d.x
+    sh = d.shared.view(1, T, cfg.H) if (reshape3d and d.shared is not None) else d.shared
+    out = qm.forward(p, x, d.logits, d.fc1, d.fc2, d.fc3, sh)
+    torch.cuda.synchronize()
+    return out.reshape(T, cfg.H), d
+
+
+def check_forward(cfg, T, sample=None, shared=False, seed=0):
+    say("forward", cfg.name, "T", T, "bits", cfg.bits, "bs", cfg.block_size)
+    inp = gen.make_inputs(cfg, T, seed=seed, shared=shared)
+    out, d = forward_gpu(cfg, inp)
+    got = host_f64(out, cfg.act_dtype)
+    # routing and grouping of every token, bit for bit
+    ids_g, _ = run_route(cfg, inp.logits, T)
+    ids_o, w_o = oracle.route(cfg, inp.logits)
+    assert np.array_equal(ids_g, ids_o)
+    M, perm_g = run_permute(cfg, ids_o, T)
+    perm_o = oracle.permute(cfg, ids_o, M)
+    assert np.array_equal(perm_g["sorted_assign"][:perm_o["rows"]], perm_o["sorted_assign"])
+    assert np.array_equal(perm_g["assign_pos"], perm_o["assign_pos"])
+    # outputs
+    if sample is None or sample >= T:
+        sel = np.arange(T)
+    else:
+        rng = np.random.default_rng(seed + 17)
+        sel = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=sample - 2, replace=False)]))
+    ref64, _ = oracle.forward(cfg, inp, sel=sel, nthreads=NTHREADS)
+    err = max_rel_err(got[sel], ref64)
+    floor = 0.0
+    if cfg.act_dtype == "bf16":
+        floor = max_rel_err(as_f32(oracle.round_bf16(ref64), "bf16").astype(np.float64), ref64)
+    say(f"  max|err|/rms = {err:.3e} (tolerance {TOL[cfg.act_dtype]:.0e}; rounding floor {floor:.3e})")
+    assert err <= TOL[cfg.act_dtype]
+    return out, d, inp
+
+
+def test_forward_c1_tiny_fp32():
+    check_forward(configs.C1, 16)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_forward_c2_decode(T):
+    check_forward(configs.C2, T, shared=(T == 8))
+
+
+def test_forward_c3_prefill_sampled():
+    check_forward(configs.C3, 4096, sample=12)
+
+
+def test_forward_c4_many_experts_sampled():
+    check_forward(configs.C4, 512, sample=16)
+
+
+@pytest.mark.parametrize("bits", configs.C5_BITS)
+@pytest.mark.parametrize("bs", configs.C5_BLOCKS)
+@pytest.mark.parametrize("T", configs.C5.T_points)
+def test_forward_c5_sweep(T, bs, bits):
+    check_forward(configs.c5_point(bits, bs), T, sample=6)
+
+
+def test_forward_deterministic_and_3d_input():
+    cfg = configs.C2
+    inp = gen.make_inputs(cfg, 64, shared=True)
+    a, d = forward_gpu(cfg, inp)
+    b, _ = forward_gpu(cfg, inp, d)
+    c, _ = forward_gpu(cfg, inp, d, reshape3d=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_forward_edge_cases():
+    # one expert, k = E, every token on one expert, T = 1
+    for cfg, T in [(configs.tiny(E=1, k=1, act_dtype="bf16", H=128, I=64, fc2_bias=True), 37),
+                   (configs.tiny(E=4, k=4, act_dtype="bf16", H=128, I=64, normalize=False), 20),
+                   (configs.tiny(E=6, k=2, act_dtype="bf16", H=64, I=96, logit_skew=40.0), 50),
+                   (configs.tiny(E=3, k=2, act_dtype="f32", H=64, I=32), 1)]:
+        check_forward(cfg, T)
+
+
+def test_forward_zero_tokens():
+    cfg = configs.C2
+    p = params_for(cfg, 0)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, cfg.E), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(16, dtype=torch.uint8, device="cuda")
+    out = qm.forward(p, x, lg, (w, w, None), (w, w, None))
+    assert out.shape == (0, cfg.H)

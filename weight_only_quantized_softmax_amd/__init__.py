@@ -1,0 +1,176 @@
+"""Python binding of the MI355X weight-only-quantized MoE library (libqmoe.so).
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch is used
+for device memory and the current stream. The entry points carry the C ABI's names
+(include/qmoe.h); ``forward`` is a convenience wrapper in the shape of the QMoEWoQ
+forward (x, router_logits, shared_output) -> out (ClikaRT "QMoEWoQ" page, forward).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (ACT, QMOE_BF16, QMOE_ERR_DTYPE, QMOE_ERR_SHAPE, QMOE_ERR_UNBOUND, QMOE_F32,
+                   QmoeError, QmoeParams, QmoeStack, check, load)
+
+__all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
+           "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
+           "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
+           "qmoe_forward", "forward", "QmoeError", "QmoeParams"]
+
+_DT = {"f32": QMOE_F32, "bf16": QMOE_BF16}
+_TORCH_DT = {QMOE_F32: torch.float32, QMOE_BF16: torch.bfloat16}
+
+Stack = Optional[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]]
+
+
+def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts: int, k: int, *,
+                expert_weight_bits: int = 4, block_size: int = 0, swiglu_fusion: int = 0,
+                activation: str = "swiglu", normalize_routing_weights: bool = True,
+                swiglu_alpha: float = 1.0, swiglu_beta: float = 0.0,
+                swiglu_limit: float = math.inf, act_dtype: str = "bf16",
+                scale_dtype: str = "bf16", tile_m: int = 0,
+                strict_blocks: bool = False) -> QmoeParams:
+    return QmoeParams(num_tokens=num_tokens, hidden_size=hidden_size, inter_size=inter_size,
+                      num_experts=num_experts, k=k, expert_weight_bits=expert_weight_bits,
+                      block_size=block_size, swiglu_fusion=swiglu_fusion,
+                      activation=ACT[activation],
+                      normalize_routing_weights=int(bool(normalize_routing_weights)),
+                      swiglu_alpha=swiglu_alpha, swiglu_beta=swiglu_beta,
+                      swiglu_limit=swiglu_limit, act_dtype=_DT[act_dtype],
+                      scale_dtype=_DT[scale_dtype], tile_m=tile_m,
+                      strict_blocks=int(bool(strict_blocks)))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise QmoeError(QMOE_ERR_UNBOUND, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise QmoeError(QMOE_ERR_SHAPE, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _stack(st: Stack, name: str) -> QmoeStack:
+    if st is None:
+        return QmoeStack()
+    w, s, b = (tuple(st) + (None,))[:3]
+    return QmoeStack(weights=_ptr(w, name + ".weights"), scales=_ptr(s, name + ".scales"),
+                     bias=_ptr(b, name + ".bias"))
+
+
+def _expect(t: torch.Tensor, shape: Sequence[int], dtype: torch.dtype, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise QmoeError(QMOE_ERR_SHAPE, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise QmoeError(QMOE_ERR_DTYPE, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def qmoe_validate(p: QmoeParams) -> None:
+    check(load().qmoe_validate(p))
+
+
+def qmoe_tile_m(p: QmoeParams) -> int:
+    return int(load().qmoe_tile_m(p))
+
+
+def qmoe_max_rows(p: QmoeParams) -> int:
+    return int(load().qmoe_max_rows(p))
+
+
+def qmoe_max_tiles(p: QmoeParams) -> int:
+    return int(load().qmoe_max_tiles(p))
+
+
+def qmoe_permute_scratch_size(p: QmoeParams) -> int:
+    return int(load().qmoe_permute_scratch_size(p))
+
+
+def qmoe_workspace_size(p: QmoeParams) -> int:
+    n = int(load().qmoe_workspace_size(p))
+    if n == 0:
+        check(load().qmoe_validate(p))
+    return n
+
+
+def qmoe_route(p, router_logits, topk_ids, topk_w, stream=None) -> None:
+    check(load().qmoe_route(p, _ptr(router_logits, "router_logits"), _ptr(topk_ids, "topk_ids"),
+                            _ptr(topk_w, "topk_w"), _stream(stream)))
+
+
+def qmoe_permute(p, topk_ids, counts, padded_offsets, sorted_assign, assign_pos, tile_list,
+                 num_tiles, scratch=None, stream=None) -> None:
+    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    check(load().qmoe_permute(p, _ptr(topk_ids, "topk_ids"), _ptr(counts, "counts"),
+                              _ptr(padded_offsets, "padded_offsets"),
+                              _ptr(sorted_assign, "sorted_assign"), _ptr(assign_pos, "assign_pos"),
+                              _ptr(tile_list, "tile_list"), _ptr(num_tiles, "num_tiles"),
+                              _ptr(scratch, "scratch"), nbytes, _stream(stream)))
+
+
+def qmoe_grouped_gemm_fc1_swiglu(p, x, sorted_assign, tile_list, num_tiles, fc1: Stack,
+                                 fc3: Stack, h, stream=None) -> None:
+    check(load().qmoe_grouped_gemm_fc1_swiglu(
+        p, _ptr(x, "x"), _ptr(sorted_assign, "sorted_assign"), _ptr(tile_list, "tile_list"),
+        _ptr(num_tiles, "num_tiles"), _stack(fc1, "fc1"), _stack(fc3, "fc3"), _ptr(h, "h"),
+        _stream(stream)))
+
+
+def qmoe_grouped_gemm_fc2(p, h, tile_list, num_tiles, fc2: Stack, y, stream=None) -> None:
+    check(load().qmoe_grouped_gemm_fc2(p, _ptr(h, "h"), _ptr(tile_list, "tile_list"),
+                                       _ptr(num_tiles, "num_tiles"), _stack(fc2, "fc2"),
+                                       _ptr(y, "y"), _stream(stream)))
+
+
+def qmoe_combine(p, y, assign_pos, topk_w, shared_output, output, stream=None) -> None:
+    check(load().qmoe_combine(p, _ptr(y, "y"), _ptr(assign_pos, "assign_pos"),
+                              _ptr(topk_w, "topk_w"), _ptr(shared_output, "shared_output"),
+                              _ptr(output, "output"), _stream(stream)))
+
+
+def qmoe_forward(p, input, router_logits, fc1: Stack, fc2: Stack, fc3: Stack, shared_output,
+                 output, workspace, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().qmoe_forward(p, _ptr(input, "input"), _ptr(router_logits, "router_logits"),
+                              _stack(fc1, "fc1"), _stack(fc2, "fc2"), _stack(fc3, "fc3"),
+                              _ptr(shared_output, "shared_output"), _ptr(output, "output"),
+                              _ptr(workspace, "workspace"), nbytes, _stream(stream)))
+
+
+def alloc_workspace(p: QmoeParams, device="cuda") -> torch.Tensor:
+    return torch.empty(max(qmoe_workspace_size(p), 256), dtype=torch.uint8, device=device)
+
+
+def forward(p: QmoeParams, x: torch.Tensor, router_logits: torch.Tensor, fc1: Stack, fc2: Stack,
+            fc3: Stack = None, shared_output: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = QMoE(x, router_logits) (+ shared_output); x is [T, H] or [B, S, H]."""
+    H = p.hidden_size
+    dt = _TORCH_DT[p.act_dtype]
+    x2 = x.reshape(-1, H)
+    if x2.shape[0] != p.num_tokens:
+        raise QmoeError(QMOE_ERR_SHAPE, f"x holds {x2.shape[0]} tokens, params say {p.num_tokens}")
+    _expect(x2, (p.num_tokens, H), dt, "x")
+    _expect(router_logits.reshape(-1, p.num_experts), (p.num_tokens, p.num_experts), dt,
+            "router_logits")
+    if shared_output is not None:
+        _expect(shared_output, tuple(x.shape), dt, "shared_output")
+    out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(p, x.device)
+    qmoe_forward(p, x2, router_logits.reshape(-1, p.num_experts), fc1, fc2, fc3,
+                 None if shared_output is None else shared_output.reshape(-1, H),
+                 out.view(-1, H), workspace, stream)
+    return out

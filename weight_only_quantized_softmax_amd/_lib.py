@@ -1,0 +1,87 @@
+"""ctypes view of libqmoe.so (the C ABI declared in include/qmoe.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmoe.so")
+
+QMOE_OK, QMOE_ERR_INVALID, QMOE_ERR_SHAPE, QMOE_ERR_DTYPE = 0, 1, 2, 3
+QMOE_ERR_UNSUPPORTED, QMOE_ERR_UNBOUND, QMOE_ERR_DEVICE = 4, 5, 6
+STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "UNBOUND",
+                6: "DEVICE"}
+
+QMOE_F32, QMOE_BF16 = 0, 1
+ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
+
+
+class QmoeParams(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("hidden_size", ctypes.c_int64),
+                ("inter_size", ctypes.c_int64), ("num_experts", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("expert_weight_bits", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("swiglu_fusion", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("normalize_routing_weights", ctypes.c_int32),
+                ("swiglu_alpha", ctypes.c_float), ("swiglu_beta", ctypes.c_float),
+                ("swiglu_limit", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("scale_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("strict_blocks", ctypes.c_int32)]
+
+
+class QmoeStack(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p)]
+
+
+EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
+           "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
+           "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
+           "qmoe_forward", "qmoe_last_error")
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python weight_only_quantized_softmax_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(QmoeParams)
+    vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+    st = ctypes.c_int
+    L.qmoe_validate.argtypes, L.qmoe_validate.restype = [P], st
+    L.qmoe_tile_m.argtypes, L.qmoe_tile_m.restype = [P], ctypes.c_int32
+    L.qmoe_max_rows.argtypes, L.qmoe_max_rows.restype = [P], i64
+    L.qmoe_max_tiles.argtypes, L.qmoe_max_tiles.restype = [P], i64
+    L.qmoe_permute_scratch_size.argtypes, L.qmoe_permute_scratch_size.restype = [P], sz
+    L.qmoe_workspace_size.argtypes, L.qmoe_workspace_size.restype = [P], sz
+    L.qmoe_route.argtypes, L.qmoe_route.restype = [P, vp, vp, vp, vp], st
+    L.qmoe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qmoe_permute.restype = st
+    L.qmoe_grouped_gemm_fc1_swiglu.argtypes = [P, vp, vp, vp, vp, QmoeStack, QmoeStack, vp, vp]
+    L.qmoe_grouped_gemm_fc1_swiglu.restype = st
+    L.qmoe_grouped_gemm_fc2.argtypes = [P, vp, vp, vp, QmoeStack, vp, vp]
+    L.qmoe_grouped_gemm_fc2.restype = st
+    L.qmoe_combine.argtypes, L.qmoe_combine.restype = [P, vp, vp, vp, vp, vp, vp], st
+    L.qmoe_forward.argtypes = [P, vp, vp, QmoeStack, QmoeStack, QmoeStack, vp, vp, vp, sz, vp]
+    L.qmoe_forward.restype = st
+    L.qmoe_last_error.argtypes, L.qmoe_last_error.restype = [], ctypes.c_char_p
+    _lib = L
+    return L
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"qmoe {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def check(status: int) -> None:
+    if status != QMOE_OK:
+        msg = load().qmoe_last_error().decode(errors="replace")
+        raise QmoeError(status, msg)

@@ -1,0 +1,400 @@
+// C ABI of the QMoE library: host-side validation, workspace layout, variant choice
+// from shapes only, and launches on the caller's stream. See include/qmoe.h.
+#include "../../include/qmoe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+qmoe_status fail(qmoe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+qmoe_status ok() {
+  g_error.clear();
+  return QMOE_OK;
+}
+
+qmoe_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QMOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+constexpr int64_t kMaxExperts = 512;
+constexpr int64_t kMaxTopK = 32;
+constexpr int kMaxBlock = 512;
+constexpr int64_t kF32LdsBytes = 48 * 1024;
+
+bool swiglu(const qmoe_params* p) { return p->activation == QMOE_ACT_SWIGLU; }
+bool has_fc3(const qmoe_params* p) { return swiglu(p) && p->swiglu_fusion == 0; }
+int64_t n1_rows(const qmoe_params* p) {
+  return (swiglu(p) && p->swiglu_fusion != 0) ? 2 * p->inter_size : p->inter_size;
+}
+
+int32_t default_tile_m(const qmoe_params* p) {
+  if (p->act_dtype == QMOE_BF16) return 16;
+  const int64_t kmax = std::max(p->hidden_size, p->inter_size);
+  int32_t m = 16;
+  while (m > 1 && m * kmax * 4 > kF32LdsBytes) m >>= 1;
+  return m;
+}
+
+int32_t tile_m_of(const qmoe_params* p) { return p->tile_m > 0 ? p->tile_m : default_tile_m(p); }
+
+qmoe_status validate(const qmoe_params* p) {
+  if (!p) return fail(QMOE_ERR_UNBOUND, "params is NULL");
+  if (p->num_tokens < 0) return fail(QMOE_ERR_INVALID, "num_tokens %lld < 0", (long long)p->num_tokens);
+  if (p->hidden_size < 1 || p->inter_size < 1)
+    return fail(QMOE_ERR_INVALID, "hidden_size and inter_size must be positive");
+  if (p->num_experts < 1 || p->num_experts > kMaxExperts)
+    return fail(QMOE_ERR_UNSUPPORTED, "num_experts %lld outside [1, %lld]",
+                (long long)p->num_experts, (long long)kMaxExperts);
+  if (p->k < 1 || p->k > p->num_experts)
+    return fail(QMOE_ERR_INVALID, "k %lld outside [1, num_experts]", (long long)p->k);
+  if (p->k > kMaxTopK) return fail(QMOE_ERR_UNSUPPORTED, "k %lld > %lld", (long long)p->k, (long long)kMaxTopK);
+  if (p->expert_weight_bits != 4 && p->expert_weight_bits != 8)
+    return fail(QMOE_ERR_INVALID, "expert_weight_bits %d is not 4 or 8", p->expert_weight_bits);
+  if (p->block_size != 0 && (!is_pow2(p->block_size) || p->block_size < 16))
+    return fail(QMOE_ERR_INVALID, "block_size %d must be 0 or a power of two >= 16", p->block_size);
+  if (p->block_size > kMaxBlock)
+    return fail(QMOE_ERR_UNSUPPORTED, "block_size %d > %d", p->block_size, kMaxBlock);
+  if (p->activation < QMOE_ACT_SWIGLU || p->activation > QMOE_ACT_SILU)
+    return fail(QMOE_ERR_INVALID, "activation %d unknown", p->activation);
+  if (p->swiglu_fusion < 0 || p->swiglu_fusion > 2)
+    return fail(QMOE_ERR_INVALID, "swiglu_fusion %d outside {0, 1, 2}", p->swiglu_fusion);
+  if (!swiglu(p) && p->swiglu_fusion != 0)
+    return fail(QMOE_ERR_INVALID, "swiglu_fusion must be 0 unless the activation is swiglu");
+  if (p->act_dtype != QMOE_F32 && p->act_dtype != QMOE_BF16)
+    return fail(QMOE_ERR_DTYPE, "act_dtype %d unknown", p->act_dtype);
+  if (p->scale_dtype != QMOE_F32 && p->scale_dtype != QMOE_BF16)
+    return fail(QMOE_ERR_DTYPE, "scale_dtype %d unknown", p->scale_dtype);
+  const int pack = 8 / p->expert_weight_bits;
+  if (p->hidden_size % pack || p->inter_size % pack)
+    return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be multiples of %d", pack);
+  if (p->strict_blocks && p->block_size &&
+      (p->hidden_size % p->block_size || p->inter_size % p->block_size))
+    return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be divisible by block_size %d",
+                p->block_size);
+  if (p->num_tokens * p->k >= (int64_t(1) << 31))
+    return fail(QMOE_ERR_UNSUPPORTED, "num_tokens * k must stay below 2^31");
+  const int32_t m = tile_m_of(p);
+  if (p->act_dtype == QMOE_BF16) {
+    if (p->hidden_size % 32 || p->inter_size % 32)
+      return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs hidden_size and inter_size multiples of 32");
+    if (m != 16) return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16 (got %d)", m);
+  } else {
+    const int64_t kmax = std::max(p->hidden_size, p->inter_size);
+    if (m < 1 || m > 16 || m * kmax * 4 > kF32LdsBytes)
+      return fail(QMOE_ERR_UNSUPPORTED, "f32 path: tile_m %d with K %lld does not fit", m,
+                  (long long)kmax);
+  }
+  return ok();
+}
+
+int64_t max_tiles_of(const qmoe_params* p) {
+  const int64_t A = p->num_tokens * p->k;
+  const int32_t m = tile_m_of(p);
+  return A / m + std::min<int64_t>(p->num_experts, A);
+}
+
+int64_t max_rows_of(const qmoe_params* p) { return max_tiles_of(p) * tile_m_of(p); }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Workspace {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_assign;
+  int32_t* assign_pos;
+  int32_t* tiles;
+  int32_t* num_tiles;
+  void* perm_scratch;
+  void* h;
+  float* y;
+  size_t bytes;
+};
+
+Workspace carve(const qmoe_params* p, char* base) {
+  const int64_t A = p->num_tokens * p->k;
+  const int64_t rows = max_rows_of(p);
+  const size_t act = p->act_dtype == QMOE_BF16 ? 2 : 4;
+  Workspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  w.topk_ids = reinterpret_cast<int32_t*>(take(A * 4));
+  w.topk_w = reinterpret_cast<float*>(take(A * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(p->num_experts * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((p->num_experts + 1) * 4));
+  w.sorted_assign = reinterpret_cast<int32_t*>(take(rows * 4));
+  w.assign_pos = reinterpret_cast<int32_t*>(take(A * 4));
+  w.tiles = reinterpret_cast<int32_t*>(take(max_tiles_of(p) * 8));
+  w.num_tiles = reinterpret_cast<int32_t*>(take(4));
+  w.perm_scratch = take(qmoe::permute_scratch_bytes(A, static_cast<int>(p->num_experts)));
+  w.h = take(rows * p->inter_size * act);
+  w.y = reinterpret_cast<float*>(take(rows * p->hidden_size * 4));
+  w.bytes = off;
+  return w;
+}
+
+qmoe::GemmArgs gemm_args(const qmoe_params* p) {
+  qmoe::GemmArgs g{};
+  g.topk = static_cast<int>(p->k);
+  g.bs = p->block_size;
+  g.fusion = p->swiglu_fusion;
+  g.act = p->activation;
+  g.alpha = p->swiglu_alpha;
+  g.beta = p->swiglu_beta;
+  g.limit = (p->swiglu_limit > 0.f) ? p->swiglu_limit : INFINITY;
+  g.inter = static_cast<int>(p->inter_size);
+  g.M = tile_m_of(p);
+  return g;
+}
+
+qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
+                    const int32_t* tiles, const int32_t* num_tiles, qmoe_stack fc1,
+                    qmoe_stack fc3, void* h, hipStream_t s) {
+  qmoe::GemmArgs g = gemm_args(p);
+  g.a = x;
+  g.sorted_assign = sorted_assign;
+  g.tile_list = tiles;
+  g.num_tiles = num_tiles;
+  g.w = static_cast<const uint8_t*>(fc1.weights);
+  g.s = fc1.scales;
+  g.b = fc1.bias;
+  if (has_fc3(p)) {
+    g.w3 = static_cast<const uint8_t*>(fc3.weights);
+    g.s3 = fc3.scales;
+    g.b3 = fc3.bias;
+  }
+  g.out = h;
+  g.K = static_cast<int>(p->hidden_size);
+  g.N = static_cast<int>(n1_rows(p));
+  g.ncols = static_cast<int>(p->inter_size);
+  g.nb = p->block_size ? static_cast<int>((p->hidden_size + p->block_size - 1) / p->block_size) : 0;
+  const int mode = swiglu(p) ? qmoe::kModeSwiglu : qmoe::kModePlainAct;
+  const bool sbf = p->scale_dtype == QMOE_BF16;
+  hipError_t e = p->act_dtype == QMOE_BF16
+                     ? qmoe::launch_gemm_bf16(g, mode, p->expert_weight_bits, sbf, max_tiles_of(p), s)
+                     : qmoe::launch_gemm_f32(g, mode, p->expert_weight_bits, sbf, max_tiles_of(p), s);
+  return device_status(e, "fc1 launch");
+}
+
+qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
+                    const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s) {
+  qmoe::GemmArgs g = gemm_args(p);
+  g.a = h;
+  g.tile_list = tiles;
+  g.num_tiles = num_tiles;
+  g.w = static_cast<const uint8_t*>(fc2.weights);
+  g.s = fc2.scales;
+  g.b = fc2.bias;
+  g.out = y;
+  g.K = static_cast<int>(p->inter_size);
+  g.N = static_cast<int>(p->hidden_size);
+  g.ncols = static_cast<int>(p->hidden_size);
+  g.nb = p->block_size ? static_cast<int>((p->inter_size + p->block_size - 1) / p->block_size) : 0;
+  const bool sbf = p->scale_dtype == QMOE_BF16;
+  hipError_t e =
+      p->act_dtype == QMOE_BF16
+          ? qmoe::launch_gemm_bf16(g, qmoe::kModeFc2, p->expert_weight_bits, sbf, max_tiles_of(p), s)
+          : qmoe::launch_gemm_f32(g, qmoe::kModeFc2, p->expert_weight_bits, sbf, max_tiles_of(p), s);
+  return device_status(e, "fc2 launch");
+}
+
+qmoe_status need(const void* ptr, const char* name) {
+  if (!ptr) return fail(QMOE_ERR_UNBOUND, "%s is NULL", name);
+  return QMOE_OK;
+}
+
+#define QMOE_TRY(expr)                  \
+  do {                                  \
+    qmoe_status st__ = (expr);          \
+    if (st__ != QMOE_OK) return st__;   \
+  } while (0)
+
+qmoe_status check_stack(const qmoe_stack& st, const char* name) {
+  char buf[64];
+  snprintf(buf, sizeof(buf), "%s.weights", name);
+  QMOE_TRY(need(st.weights, buf));
+  snprintf(buf, sizeof(buf), "%s.scales", name);
+  QMOE_TRY(need(st.scales, buf));
+  return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmoe_status qmoe_validate(const qmoe_params* p) { return validate(p); }
+
+int32_t qmoe_tile_m(const qmoe_params* p) { return p ? tile_m_of(p) : 0; }
+
+int64_t qmoe_max_rows(const qmoe_params* p) { return p ? max_rows_of(p) : 0; }
+
+int64_t qmoe_max_tiles(const qmoe_params* p) { return p ? max_tiles_of(p) : 0; }
+
+size_t qmoe_permute_scratch_size(const qmoe_params* p) {
+  if (!p) return 0;
+  return qmoe::permute_scratch_bytes(p->num_tokens * p->k, static_cast<int>(p->num_experts));
+}
+
+size_t qmoe_workspace_size(const qmoe_params* p) {
+  if (validate(p) != QMOE_OK) return 0;
+  return carve(p, nullptr).bytes;
+}
+
+qmoe_status qmoe_route(const qmoe_params* p, const void* router_logits, int32_t* topk_ids,
+                       float* topk_w, void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(router_logits, "router_logits"));
+  QMOE_TRY(need(topk_ids, "topk_ids"));
+  QMOE_TRY(need(topk_w, "topk_w"));
+  return device_status(
+      qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                         static_cast<int>(p->num_experts), static_cast<int>(p->k),
+                         p->normalize_routing_weights, topk_ids, topk_w,
+                         static_cast<hipStream_t>(stream)),
+      "route launch");
+}
+
+qmoe_status qmoe_permute(const qmoe_params* p, const int32_t* topk_ids, int32_t* counts,
+                         int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                         int32_t* tile_list, int32_t* num_tiles, void* scratch,
+                         size_t scratch_bytes, void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(topk_ids, "topk_ids"));
+  QMOE_TRY(need(counts, "counts"));
+  QMOE_TRY(need(padded_offsets, "padded_offsets"));
+  QMOE_TRY(need(sorted_assign, "sorted_assign"));
+  QMOE_TRY(need(assign_pos, "assign_pos"));
+  QMOE_TRY(need(tile_list, "tile_list"));
+  QMOE_TRY(need(num_tiles, "num_tiles"));
+  const size_t want = qmoe_permute_scratch_size(p);
+  if (want > 0) {
+    QMOE_TRY(need(scratch, "scratch"));
+    if (scratch_bytes < want)
+      return fail(QMOE_ERR_INVALID, "permute scratch %zu bytes < %zu", scratch_bytes, want);
+  }
+  return device_status(
+      qmoe::launch_permute(topk_ids, p->num_tokens * p->k, static_cast<int>(p->num_experts),
+                           tile_m_of(p), counts, padded_offsets, sorted_assign, assign_pos,
+                           tile_list, num_tiles, scratch, static_cast<hipStream_t>(stream)),
+      "permute launch");
+}
+
+qmoe_status qmoe_grouped_gemm_fc1_swiglu(const qmoe_params* p, const void* x,
+                                         const int32_t* sorted_assign, const int32_t* tile_list,
+                                         const int32_t* num_tiles, qmoe_stack fc1, qmoe_stack fc3,
+                                         void* h, void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(x, "x"));
+  QMOE_TRY(need(sorted_assign, "sorted_assign"));
+  QMOE_TRY(need(tile_list, "tile_list"));
+  QMOE_TRY(need(num_tiles, "num_tiles"));
+  QMOE_TRY(check_stack(fc1, "fc1"));
+  if (has_fc3(p)) QMOE_TRY(check_stack(fc3, "fc3"));
+  QMOE_TRY(need(h, "h"));
+  return run_fc1(p, x, sorted_assign, tile_list, num_tiles, fc1, fc3, h,
+                 static_cast<hipStream_t>(stream));
+}
+
+qmoe_status qmoe_grouped_gemm_fc2(const qmoe_params* p, const void* h, const int32_t* tile_list,
+                                  const int32_t* num_tiles, qmoe_stack fc2, float* y,
+                                  void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(h, "h"));
+  QMOE_TRY(need(tile_list, "tile_list"));
+  QMOE_TRY(need(num_tiles, "num_tiles"));
+  QMOE_TRY(check_stack(fc2, "fc2"));
+  QMOE_TRY(need(y, "y"));
+  return run_fc2(p, h, tile_list, num_tiles, fc2, y, static_cast<hipStream_t>(stream));
+}
+
+qmoe_status qmoe_combine(const qmoe_params* p, const float* y, const int32_t* assign_pos,
+                         const float* topk_w, const void* shared_output, void* output,
+                         void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(y, "y"));
+  QMOE_TRY(need(assign_pos, "assign_pos"));
+  QMOE_TRY(need(topk_w, "topk_w"));
+  QMOE_TRY(need(output, "output"));
+  return device_status(
+      qmoe::launch_combine(y, assign_pos, topk_w, shared_output, output,
+                           p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                           static_cast<int>(p->hidden_size), static_cast<int>(p->k),
+                           static_cast<hipStream_t>(stream)),
+      "combine launch");
+}
+
+qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* router_logits,
+                         qmoe_stack fc1, qmoe_stack fc2, qmoe_stack fc3,
+                         const void* shared_output, void* output, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(input, "input"));
+  QMOE_TRY(need(router_logits, "router_probs"));
+  QMOE_TRY(check_stack(fc1, "fc1"));
+  QMOE_TRY(check_stack(fc2, "fc2"));
+  if (has_fc3(p)) QMOE_TRY(check_stack(fc3, "fc3"));
+  QMOE_TRY(need(output, "output"));
+  QMOE_TRY(need(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(QMOE_ERR_INVALID, "workspace must be 256-byte aligned");
+  Workspace w = carve(p, static_cast<char*>(workspace));
+  if (workspace_bytes < w.bytes)
+    return fail(QMOE_ERR_INVALID, "workspace %zu bytes < %zu", workspace_bytes, w.bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t A = p->num_tokens * p->k;
+  QMOE_TRY(device_status(
+      qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                         static_cast<int>(p->num_experts), static_cast<int>(p->k),
+                         p->normalize_routing_weights, w.topk_ids, w.topk_w, s),
+      "route launch"));
+  QMOE_TRY(device_status(
+      qmoe::launch_permute(w.topk_ids, A, static_cast<int>(p->num_experts), tile_m_of(p), w.counts,
+                           w.offsets, w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles,
+                           w.perm_scratch, s),
+      "permute launch"));
+  QMOE_TRY(run_fc1(p, input, w.sorted_assign, w.tiles, w.num_tiles, fc1, fc3, w.h, s));
+  QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s));
+  QMOE_TRY(device_status(
+      qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output,
+                           p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                           static_cast<int>(p->hidden_size), static_cast<int>(p->k), s),
+      "combine launch"));
+  return ok();
+}
+
+const char* qmoe_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

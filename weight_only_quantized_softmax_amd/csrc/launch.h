@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// Grouping: one fused block up to this many assignments, otherwise three kernels
+// over chunks of kPermChunk assignments.
+constexpr int64_t kPermFusedMax = 4096;
+constexpr int kPermChunk = 4096;
+
+// K held in LDS per pass by the bf16 grouped GEMM.
+constexpr int kGemmChunk = 1024;
+
+enum GemmMode { kModeSwiglu = 0, kModePlainAct = 1, kModeFc2 = 2 };
+
+struct GemmArgs {
+  const void* a;               // x [T, K] (fc1) or h [P, K] (fc2), activation dtype
+  const int32_t* sorted_assign;  // fc1: assignment of each padded row
+  const int32_t* tile_list;    // [tiles, 2] (expert, valid rows)
+  const int32_t* num_tiles;
+  const uint8_t* w;            // stack [E, N, K*bits/8] (fc1 gate or fused, or fc2)
+  const void* s;
+  const void* b;
+  const uint8_t* w3;           // separate up stack (swiglu_fusion 0)
+  const void* s3;
+  const void* b3;
+  void* out;                   // h [P, ncols] act dtype, or y [P, ncols] f32
+  int K;                       // contraction length
+  int N;                       // rows of the stack at w
+  int ncols;                   // output columns (I for fc1, H for fc2)
+  int inter;                   // I (row offset of the up half in concatenated fusion)
+  int topk;                    // k, to map an assignment to its token
+  int bs;                      // block size, 0 = per output row
+  int nb;                      // scales per row when bs > 0
+  int fusion;
+  int act;
+  float alpha, beta, limit;
+  int M;                       // tile rows
+};
+
+hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
+                        int32_t* ids, float* w, hipStream_t s);
+
+size_t permute_scratch_bytes(int64_t A, int E);
+hipError_t launch_permute(const int32_t* ids, int64_t A, int E, int M, int32_t* counts,
+                          int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                          int32_t* tile_list, int32_t* num_tiles, void* scratch, hipStream_t s);
+
+// bf16 activations, MFMA 16-row tiles. mode: GemmMode.
+hipError_t launch_gemm_bf16(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                            int64_t max_tiles, hipStream_t s);
+
+// f32 activations, VALU kernel.
+hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                           int64_t max_tiles, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
+                          const void* shared, void* out, bool bf16, int T, int H, int k,
+                          hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,227 @@
+// Grouping of token-expert assignments by expert into padded row tiles.
+//
+// The per-expert work lists behind the per-expert kernels of the ClikaRT "QMoEWoQ"
+// page: assignment a = t*k + j goes to expert topk_ids[a]; every expert's rows are
+// consecutive, in ascending a, and padded to a multiple of the tile height M.
+//
+// Determinism without order-dependent atomics: counting uses atomics (a count does
+// not depend on arrival order); ranks come from wave ballots -- the lanes holding
+// the same expert id are found by matching the id bit by bit over ceil(log2 E)
+// ballots, and a lane's rank is the number of matching lanes below it -- plus
+// per-wave counts in LDS summed in wave order, and per-block bases summed in block
+// order. The result is a pure function of topk_ids.
+#include "common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;
+
+// Exclusive scan of one int per thread over the block; also returns the total.
+__device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */, int* total) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < kPermWaves; ++i) {
+      int c = tmp[i];
+      tmp[i] = run;
+      run += c;
+    }
+    tmp[kPermWaves] = run;
+  }
+  __syncthreads();
+  const int excl = tmp[w] + inc - v;
+  *total = tmp[kPermWaves];
+  __syncthreads();
+  return excl;
+}
+
+// Counts of assignments [a0, a1) per expert into cnt (LDS, zeroed by the caller).
+__device__ void block_histogram(const int32_t* __restrict__ ids, int64_t a0, int64_t a1, int* cnt) {
+  for (int64_t a = a0 + threadIdx.x; a < a1; a += blockDim.x) atomicAdd(&cnt[ids[a]], 1);
+}
+
+// Writes the stable positions of assignments [a0, a1): run[e] (LDS) holds the next free
+// row of expert e and is advanced past the chunk's rows. wc is LDS [kPermWaves][E].
+__device__ void block_rank_scatter(const int32_t* __restrict__ ids, int64_t a0, int64_t a1, int E,
+                                   int ebits, int* run, int* wc, int32_t* __restrict__ sorted_assign,
+                                   int32_t* __restrict__ assign_pos) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  for (int64_t base = a0; base < a1; base += kPermThreads) {
+    const int64_t a = base + tid;
+    const bool valid = a < a1;
+    const int e = valid ? ids[a] : 0;
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wc[i] = 0;
+    __syncthreads();
+    uint64_t same = ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) wc[w * E + e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w2 = 0; w2 < w; ++w2) pre += wc[w2 * E + e];
+      const int pos = run[e] + pre + rank;
+      sorted_assign[pos] = static_cast<int32_t>(a);
+      assign_pos[a] = pos;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kPermThreads) {
+      int s = 0;
+      for (int w2 = 0; w2 < kPermWaves; ++w2) s += wc[w2 * E + ee];
+      run[ee] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// From per-expert counts: padded offsets, counts, tiles, padding markers and the tile count.
+// Expert e is handled by thread e (E <= kPermThreads). off_lds receives the offsets.
+__device__ void block_layout(const int* cnt, int E, int M, int* scan_tmp, int* off_lds,
+                             int32_t* __restrict__ counts, int32_t* __restrict__ padded_offsets,
+                             int32_t* __restrict__ sorted_assign, int32_t* __restrict__ tile_list,
+                             int32_t* __restrict__ num_tiles) {
+  const int e = threadIdx.x;
+  const int c = e < E ? cnt[e] : 0;
+  const int ntile = (c + M - 1) / M;
+  int total = 0;
+  const int excl = block_exclusive_scan(ntile * M, scan_tmp, &total);
+  if (e < E) {
+    off_lds[e] = excl;
+    counts[e] = c;
+    padded_offsets[e + 1] = excl + ntile * M;
+    if (e == 0) padded_offsets[0] = 0;
+    const int t0 = excl / M;
+    for (int i = 0; i < ntile; ++i) {
+      tile_list[2 * (t0 + i)] = e;
+      tile_list[2 * (t0 + i) + 1] = min(M, c - i * M);
+    }
+    for (int r = excl + c; r < excl + ntile * M; ++r) sorted_assign[r] = -1;
+  }
+  if (threadIdx.x == 0) *num_tiles = total / M;
+  __syncthreads();
+}
+
+// Whole grouping in one block (small assignment counts).
+__global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int E, int ebits, int M,
+    int32_t* __restrict__ counts, int32_t* __restrict__ padded_offsets,
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+    int32_t* __restrict__ tile_list, int32_t* __restrict__ num_tiles) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                 // [E]
+  int* run = cnt + E;             // [E]
+  int* scan_tmp = run + E;        // [kPermWaves + 1]
+  int* wc = scan_tmp + kPermWaves + 1;  // [kPermWaves][E]
+  for (int i = threadIdx.x; i < E; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  block_histogram(ids, 0, A, cnt);
+  __syncthreads();
+  block_layout(cnt, E, M, scan_tmp, run, counts, padded_offsets, sorted_assign, tile_list,
+               num_tiles);
+  block_rank_scatter(ids, 0, A, E, ebits, run, wc, sorted_assign, assign_pos);
+}
+
+// Multi-block grouping, step 1: per-block counts blk[b][e].
+__global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int32_t* __restrict__ ids,
+                                                                    int64_t A, int E, int chunk,
+                                                                    int32_t* __restrict__ blk) {
+  extern __shared__ int cnt[];
+  for (int i = threadIdx.x; i < E; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t a1 = min(A, a0 + chunk);
+  block_histogram(ids, a0, a1, cnt);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kPermThreads) blk[static_cast<int64_t>(blockIdx.x) * E + i] = cnt[i];
+}
+
+// Step 2 (one block): totals, layout, and blk[b][e] turned into each block's first row.
+__global__ __launch_bounds__(kPermThreads) void permute_layout_kernel(
+    int nblk, int E, int M, int32_t* __restrict__ blk, int32_t* __restrict__ counts,
+    int32_t* __restrict__ padded_offsets, int32_t* __restrict__ sorted_assign,
+    int32_t* __restrict__ tile_list, int32_t* __restrict__ num_tiles) {
+  extern __shared__ int lds[];
+  int* cnt = lds;            // [E]
+  int* off = cnt + E;        // [E]
+  int* scan_tmp = off + E;   // [kPermWaves + 1]
+  const int e = threadIdx.x;
+  if (e < E) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk[static_cast<int64_t>(b) * E + e];
+      blk[static_cast<int64_t>(b) * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  block_layout(cnt, E, M, scan_tmp, off, counts, padded_offsets, sorted_assign, tile_list,
+               num_tiles);
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) blk[static_cast<int64_t>(b) * E + e] += off[e];
+}
+
+// Step 3: stable scatter of each block's assignments from its first rows.
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int E, int ebits, int chunk,
+    const int32_t* __restrict__ blk, int32_t* __restrict__ sorted_assign,
+    int32_t* __restrict__ assign_pos) {
+  extern __shared__ int lds[];
+  int* run = lds;      // [E]
+  int* wc = run + E;   // [kPermWaves][E]
+  for (int i = threadIdx.x; i < E; i += kPermThreads)
+    run[i] = blk[static_cast<int64_t>(blockIdx.x) * E + i];
+  __syncthreads();
+  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t a1 = min(A, a0 + chunk);
+  block_rank_scatter(ids, a0, a1, E, ebits, run, wc, sorted_assign, assign_pos);
+}
+
+static int bits_for(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+size_t permute_scratch_bytes(int64_t A, int E) {
+  if (A <= kPermFusedMax) return 0;
+  const int64_t nblk = (A + kPermChunk - 1) / kPermChunk;
+  return static_cast<size_t>(nblk) * E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t A, int E, int M, int32_t* counts,
+                          int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                          int32_t* tile_list, int32_t* num_tiles, void* scratch, hipStream_t s) {
+  const int ebits = bits_for(E);
+  if (A <= kPermFusedMax) {
+    const size_t lds = (2 * E + kPermWaves + 1 + kPermWaves * E) * sizeof(int);
+    permute_fused_kernel<<<1, kPermThreads, lds, s>>>(ids, A, E, ebits, M, counts, padded_offsets,
+                                                      sorted_assign, assign_pos, tile_list,
+                                                      num_tiles);
+    return hipGetLastError();
+  }
+  const int nblk = static_cast<int>((A + kPermChunk - 1) / kPermChunk);
+  int32_t* blk = static_cast<int32_t*>(scratch);
+  permute_hist_kernel<<<nblk, kPermThreads, E * sizeof(int), s>>>(ids, A, E, kPermChunk, blk);
+  permute_layout_kernel<<<1, kPermThreads, (2 * E + kPermWaves + 1) * sizeof(int), s>>>(
+      nblk, E, M, blk, counts, padded_offsets, sorted_assign, tile_list, num_tiles);
+  permute_scatter_kernel<<<nblk, kPermThreads, (E + kPermWaves * E) * sizeof(int), s>>>(
+      ids, A, E, ebits, kPermChunk, blk, sorted_assign, assign_pos);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe
