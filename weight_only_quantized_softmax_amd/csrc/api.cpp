@@ -164,6 +164,8 @@ qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   qmoe::GemmArgs g{};
   g.topk = static_cast<int>(p->k);
   g.bs = p->block_size;
+  g.bs_shift = 0;
+  while (g.bs > 0 && (1 << g.bs_shift) < g.bs) ++g.bs_shift;
   g.fusion = p->swiglu_fusion;
   g.act = p->activation;
   g.alpha = p->swiglu_alpha;

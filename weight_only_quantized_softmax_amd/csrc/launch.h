@@ -34,6 +34,7 @@ struct GemmArgs {
   int inter;                   // I (row offset of the up half in concatenated fusion)
   int topk;                    // k, to map an assignment to its token
   int bs;                      // block size, 0 = per output row
+  int bs_shift;                // log2(bs) when bs > 0
   int nb;                      // scales per row when bs > 0
   int fusion;
   int act;
