@@ -235,7 +235,7 @@ def test_fc2_stage(name):
 @pytest.mark.parametrize("dtype,H,shared", [("bf16", 2880, False), ("bf16", 2048, True),
                                              ("f32", 1442, True), ("f32", 128, False)])
 def test_combine_stage(dtype, H, shared):
-    c = configs.tiny(E=16, k=4, H=H, I=64, act_dtype=dtype)
+    c = configs.tiny(E=16, k=4, H=H, I=64, act_dtype=dtype, block_size=32, scale_dtype="bf16")
     T = 33
     p = params_for(c, T)
     ids = gen.gen_topk_ids(c, T)
@@ -254,7 +254,7 @@ def test_combine_stage(dtype, H, shared):
 
 def test_combine_rounds_to_nearest_even():
     # k = 1 with weight 1: the output is the bf16 rounding of y itself.
-    c = configs.tiny(E=2, k=1, H=4096, act_dtype="bf16")
+    c = configs.tiny(E=2, k=1, H=4096, act_dtype="bf16", block_size=32, scale_dtype="bf16")
     T = 8
     rng = np.random.default_rng(3)
     bits = rng.integers(0x3F000000, 0x40000000, size=(T, c.H), dtype=np.uint32)

@@ -16,6 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          # no packed fp32 instructions in generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs: the epilogues read them every scale block
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -100,6 +100,20 @@ qmoe_status validate(const qmoe_params* p) {
     if (p->hidden_size % 32 || p->inter_size % 32)
       return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs hidden_size and inter_size multiples of 32");
     if (m != 16) return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16 (got %d)", m);
+    // 32-bit buffer offsets: activations, h and one expert's stack must stay below 2 GiB
+    const int64_t kmax = std::max(p->hidden_size, p->inter_size);
+    const int64_t rows_max = (p->num_tokens * p->k) / 16 + std::min<int64_t>(p->num_experts, p->num_tokens * p->k);
+    if (p->num_tokens * p->hidden_size * 2 >= (int64_t(1) << 31) ||
+        rows_max * 16 * p->inter_size * 2 >= (int64_t(1) << 31) ||
+        2 * p->inter_size * kmax * p->expert_weight_bits / 8 >= (int64_t(1) << 31))
+      return fail(QMOE_ERR_UNSUPPORTED, "bf16 path: a tensor or one expert's stack reaches 2 GiB");
+    if (p->block_size) {
+      const int64_t nb = (kmax + p->block_size - 1) / p->block_size;
+      const int64_t sbytes = p->scale_dtype == QMOE_BF16 ? 2 : 4;
+      if (2 * 64 * nb * sbytes > 64 * 1024)
+        return fail(QMOE_ERR_UNSUPPORTED, "bf16 path: %lld scales per row do not fit in LDS",
+                    (long long)nb);
+    }
   } else {
     const int64_t kmax = std::max(p->hidden_size, p->inter_size);
     if (m < 1 || m > 16 || m * kmax * 4 > kF32LdsBytes)
@@ -194,6 +208,7 @@ qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_a
   }
   g.out = h;
   g.K = static_cast<int>(p->hidden_size);
+  g.a_rows = p->num_tokens;
   g.N = static_cast<int>(n1_rows(p));
   g.ncols = static_cast<int>(p->inter_size);
   g.nb = p->block_size ? static_cast<int>((p->hidden_size + p->block_size - 1) / p->block_size) : 0;
@@ -216,6 +231,7 @@ qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
   g.b = fc2.bias;
   g.out = y;
   g.K = static_cast<int>(p->inter_size);
+  g.a_rows = max_rows_of(p);
   g.N = static_cast<int>(p->hidden_size);
   g.ncols = static_cast<int>(p->hidden_size);
   g.nb = p->block_size ? static_cast<int>((p->inter_size + p->block_size - 1) / p->block_size) : 0;

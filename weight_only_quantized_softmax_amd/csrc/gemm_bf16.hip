@@ -4,17 +4,20 @@
 // block is decoded inside the GEMM dot, never as a dense copy. graiphic "QMoE" page:
 // stack shapes [E, N, K/pack], scales per row or per K-block, activation attributes.
 //
-// One workgroup = one 16-row tile of one expert x 64 output columns (four waves of 16).
-// The tile's activation rows are staged in LDS, K at a time in chunks. Each lane of a
-// wave owns one output column n and one quarter kq of every 32-wide K step, and decodes
-// its 8 weights of the step in registers:
+// Work unit of one wave: one 16-row tile of one expert x 16 output columns (x two weight
+// streams, gate and up, for fc1 with SwiGLU) over a range of K. A workgroup holds four
+// such waves; with split-K they share columns and divide K, and add their partial sums
+// in LDS at the end. Waves never synchronise otherwise: each streams its own weights and
+// loads its own activation fragments, both through raw buffer loads.
+// Each lane owns one output column n and one quarter kq of every 32-wide K step, and
+// decodes its 8 weights of the step in registers:
 //   4-bit: each nibble q becomes the bfloat16 128+q by OR-ing it into the exponent
 //          pattern of 128 (exact), two nibbles per 32-bit register;
 //   8-bit: each byte becomes the exact bfloat16 q.
 // The MFMA therefore computes sum x*(c+q) with c = 128 (4-bit) or 0 (8-bit). The zero
-// point z and the offset c are removed by starting each scale block's accumulation at
-// -(c+z)*sum(x over the block), and the block's scale multiplies the block's
-// accumulator once. Per-row scales multiply the finished sum.
+// point z and the offset c are removed by a second MFMA of the same activations against
+// the constant -(c+z) (exact in bfloat16), and each scale block's accumulator is
+// multiplied by the block's scale once. Per-row scales multiply the finished sum.
 #include "common.h"
 #include "launch.h"
 
@@ -23,14 +26,44 @@ namespace qmoe {
 constexpr int kM = 16;
 constexpr int kRowPad = 8;  // bf16 elements of padding per LDS row (keeps 16 rows on distinct banks)
 
+// Raw buffer access: a descriptor (base, byte size) in scalar registers and a 32-bit byte
+// offset per lane; reads at or past the size return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kAuxStream = 2;     // cache policy bits of a streamed load
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every buffer: reads zeros
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Same, marked non-temporal: streamed weights should not displace reused lines.
+__device__ __forceinline__ u32x4 buf_load16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxStream));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// (v & mask) | magic in one gfx950 three-input bit operation.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  return __builtin_amdgcn_bitop3_b32(v, mask, magic, 0xEA);
+}
+
 __device__ __forceinline__ bf16x8 decode4(uint32_t w) {
   // element order of the result: [e0, e4, e1, e5, e2, e6, e3, e7] of the 8 nibbles
   const uint32_t magic = 0x43004300u, mask = 0x000F000Fu;
   u32x4 r;
-  r[0] = (w & mask) | magic;
-  r[1] = ((w >> 4) & mask) | magic;
-  r[2] = ((w >> 8) & mask) | magic;
-  r[3] = ((w >> 12) & mask) | magic;
+  r[0] = and_or(w, mask, magic);
+  r[1] = and_or(w >> 4, mask, magic);
+  r[2] = and_or(w >> 8, mask, magic);
+  r[3] = and_or(w >> 12, mask, magic);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -47,18 +80,17 @@ __device__ __forceinline__ bf16x8 decode8(u32x2 w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Reorders 8 bf16 activations [x0..x7] to [x0, x4, x1, x5, x2, x6, x3, x7] (the 4-bit order).
+// Reorders 8 bf16 activations [x0..x7] to [x0, x4, x1, x5, x2, x6, x3, x7] (the 4-bit
+// decode order) with four byte permutes.
 __device__ __forceinline__ u32x4 order_for_nibbles(u32x4 d) {
   u32x4 o;
-  o[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
-  o[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
-  o[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
-  o[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
+  o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
   return o;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
 // Raw scale storage: bf16 scales stay 16-bit until they are used.
 template <typename ST>
@@ -96,10 +128,21 @@ __device__ __forceinline__ void transpose_rows4(u32x4& d) {
 //          takes bytes [8j, 8j+8) of every lane (k slots spread over the 64).
 // G > 1 splits an MFMA whose k slots span G scale blocks into G MFMAs, each with the
 // weights of the other blocks' lanes zeroed.
-template <int BITS, typename ST, int MODE, int BS>
-__global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
+//
+// Workgroup: four waves on one 16-row tile, as CPB groups of 16 output columns times SK
+// K-splits (CPB * SK = 4). K advances in chunks of 256 bytes of every weight row (four
+// super-steps); the split-K waves of a column group take the chunk's super-steps in turn
+// and add their partial sums in LDS at the end. Per chunk:
+//   - the tile's activations for the next chunk are loaded into registers, then stored
+//     to LDS (in the nibble order of the decode) with their block sums between two
+//     barriers at the end of the chunk;
+//   - the weights of the chunk two ahead are requested as one burst per wave into a
+//     three-slot register ring, so a row is read 256 contiguous bytes at a time and two
+//     chunks of weights stay in flight.
+// All scales of the workgroup's rows are staged in LDS once, at the start.
+template <int BITS, typename ST, int MODE, int BS, int SK>
+__global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
   constexpr bool PERROW = BS == 0;
-  // 4-bit blocks of 16..64 take the transposed layout; spans of several blocks are split
   constexpr bool XPOSE = BITS == 4 && BS > 0 && BS < 128;
   constexpr int G = BITS == 4 ? (BS == 16 ? 2 : 1) : (BS == 16 ? 4 : (BS == 32 ? 2 : 1));
   constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
@@ -108,22 +151,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
   constexpr int KC = BITS == 4 ? 512 : 256;     // K per chunk (256 bytes of every row)
   constexpr int SSK = BITS == 4 ? 128 : 64;     // K per super-step
   constexpr int SPC = KC / SSK;                 // super-steps per chunk (4)
+  constexpr int SPW = SPC / SK;                 // super-steps per chunk of one wave
   constexpr int MPS = SSK / 32;                 // MFMAs per super-step
   constexpr int NX = KC / 128;                  // activation uint4 staged per thread
-  // correction / scale group: a scale block, or the part of one inside a K chunk (the
-  // block's scale then multiplies each part's accumulator)
+  constexpr int CPB = 4 / SK;                   // 16-column groups per workgroup
+  constexpr int SROWS = NS * CPB * 16;          // scale rows staged per workgroup
+  // correction group: a scale block, or the part of one inside a K chunk
   constexpr int GS = PERROW ? KC : (BS < KC ? BS : KC);
-  constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
   constexpr int GSHIFT = GS == 16 ? 4 : GS == 32 ? 5 : GS == 64 ? 6 : GS == 128 ? 7 : GS == 256 ? 8 : 9;
   static_assert((1 << GSHIFT) == GS, "block length must be a power of two in [16, 512]");
-  constexpr int GPC = KC / GS;                    // blocks per chunk
-  constexpr int TPR = 256 / (NS * 64);            // staging threads per scale row (2 or 4)
-  constexpr int NSE = PERROW ? 1 : (GPC + TPR - 1) / TPR;  // scales staged per thread
+  constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
   constexpr int kMaxGroups = KC / 16;
+  constexpr int GLANES = GS / 8;                // staging lanes per correction group
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[kM][KC + kRowPad];
-  __shared__ __attribute__((aligned(16))) float corr[kMaxGroups][kM];  // -(c+z)*sum(x) per block, row
-  __shared__ float sc[PERROW ? 1 : kMaxGroups][NS * 64];                // scales per block, column
+  __shared__ __attribute__((aligned(16))) float corr[kMaxGroups][kM];  // -(c+z)*sum(x) per group, row
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];   // scales, split-K partials
 
   const int tile = blockIdx.y;
   if (tile >= *g.num_tiles) return;
@@ -134,70 +177,69 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
-  const int col0 = blockIdx.x * 64;
-  const int col = col0 + wave * 16 + n;
+  const int ks = wave % SK, cgl = wave / SK;     // K split and column group of this wave
+  const int col0 = blockIdx.x * CPB * 16;
+  const int col = col0 + cgl * 16 + n;
   const bool col_ok = col < g.ncols;
   const int K = g.K;
-  const int64_t row_bytes = static_cast<int64_t>(K) * BITS / 8;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
+  const int nchunks = (K + KC - 1) / KC;
 
-  // stack row, weight row and scale row of column c in stream st
-  auto stack_row = [&](int st, int c) -> int64_t {
-    if (!kTwo) return static_cast<int64_t>(e) * g.N + c;
-    if (g.fusion == 1) return static_cast<int64_t>(e) * g.N + 2 * c + st;
-    if (g.fusion == 2) return static_cast<int64_t>(e) * g.N + st * g.inter + c;
-    return st == 0 ? static_cast<int64_t>(e) * g.N + c : static_cast<int64_t>(e) * g.inter + c;
+  auto local_row = [&](int st, int c) -> int {
+    if (!kTwo) return c;
+    if (g.fusion == 1) return 2 * c + st;
+    if (g.fusion == 2) return st * g.inter + c;
+    return c;
   };
-  auto wbase = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.w3 : g.w; };
-  auto sbase = [&](int st) {
-    return static_cast<const ST*>((st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s);
-  };
+  auto stream_rows = [&](int st) { return (kTwo && g.fusion == 0) ? g.inter : g.N; };
+  auto stream_w = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.w3 : g.w; };
+  auto stream_s = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s; };
+  auto stream_b = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b; };
 
   const int c = col_ok ? col : g.ncols - 1;
-  const uint8_t* wrow[NS];
-  int64_t grow[NS];
+  rsrc_t wres[NS];
+  uint32_t woff[NS];
+  int lrow[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    grow[st] = stack_row(st, c);
-    wrow[st] = wbase(st) + grow[st] * row_bytes;
+    const int nr = stream_rows(st);
+    wres[st] = make_rsrc(stream_w(st) + static_cast<int64_t>(e) * nr * row_bytes,
+                         static_cast<uint32_t>(nr) * row_bytes);
+    lrow[st] = local_row(st, c);
+    woff[st] = static_cast<uint32_t>(lrow[st]) * row_bytes + 16 * kq;
   }
+  // the weights of one wave for chunk ci: its SPW super-steps, in one burst
+  typedef u32x4 Slot[NS][SPW];
+  auto wload = [&](int ci, Slot& w) {
+#pragma unroll
+    for (int v = 0; v < SPW; ++v)
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        w[st][v] = buf_load16(wres[st], woff[st] + static_cast<uint32_t>(ci * KC + SSK * (v * SK + ks)) * BITS / 8);
+  };
 
-  constexpr int gs = GS;
-  constexpr int gshift = GSHIFT;
-  constexpr int glanes = GS / 8;  // loader lanes per block
-  const int nchunks = (K + KC - 1) / KC;
-  // scale staging: thread tid stages groups part, part + TPR, ... of scale row srow
-  const int srow = tid % (NS * 64), spart = tid / (NS * 64);
-  const ST* sptr = nullptr;
-  if (!PERROW) {
-    const int st = srow / 64;
-    const int cc = min(col0 + (srow % 64), g.ncols - 1);
-    sptr = sbase(st) + stack_row(st, cc) * g.nb;
+  // ---- activations: rows of this tile, staged K chunk by K chunk ----
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
+  uint32_t xoff[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int f = tid + 256 * i;
+    const int m = f / (KC / 8), kk = (f % (KC / 8)) * 8;
+    if (m < valid) {
+      const int64_t src = (MODE == kModeFc2) ? row0 + m : g.sorted_assign[row0 + m] / g.topk;
+      xoff[i] = static_cast<uint32_t>((src * K + kk) * 2);
+    } else {
+      xoff[i] = kOutOfRange;  // padding rows read zeros
+    }
   }
-
-  // ---- staging of one chunk: activations (+ block sums) and scales ----
   u32x4 sx[NX];
-  ST ss[NSE];
   auto stage_load = [&](int ci) {
     const int k0 = ci * KC;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      const int f = tid + 256 * i;
-      const int m = f / (KC / 8), kk = (f % (KC / 8)) * 8;
-      const bool ok = (k0 + kk < K) && (m < valid);
-      int64_t src;
-      if (MODE == kModeFc2) {
-        src = row0 + min(m, valid - 1);
-      } else {
-        src = g.sorted_assign[row0 + min(m, valid - 1)] / g.topk;
-      }
-      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.a) + src * K +
-                                                      min(k0 + kk, K - 8));
-      sx[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (!PERROW) {
-#pragma unroll
-      for (int i = 0; i < NSE; ++i)
-        ss[i] = sptr[min((k0 + (spart + TPR * i) * GS) >> BSHIFT, g.nb - 1)];
+      const int kk = ((tid + 256 * i) % (KC / 8)) * 8;
+      const u32x4 v = buf_load16(xres, xoff[i] + 2 * k0);
+      sx[i] = (k0 + kk < K) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto stage_store = [&]() {
@@ -206,33 +248,52 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
       const int f = tid + 256 * i;
       const int m = f / (KC / 8), kk = (f % (KC / 8)) * 8;
       u32x4 d = sx[i];
-      float ps = bf16_lo(d[0]) + bf16_hi(d[0]) + bf16_lo(d[1]) + bf16_hi(d[1]) + bf16_lo(d[2]) +
-                 bf16_hi(d[2]) + bf16_lo(d[3]) + bf16_hi(d[3]);
-      for (int o = 1; o < glanes; o <<= 1) ps += __shfl_xor(ps, o);
-      if ((kk & (gs - 1)) == 0) corr[kk >> gshift][m] = -kCorr * ps;
+      float ps = bf16_to_f32(d[0] & 0xFFFFu) + __uint_as_float(d[0] & 0xFFFF0000u) +
+                 bf16_to_f32(d[1] & 0xFFFFu) + __uint_as_float(d[1] & 0xFFFF0000u) +
+                 bf16_to_f32(d[2] & 0xFFFFu) + __uint_as_float(d[2] & 0xFFFF0000u) +
+                 bf16_to_f32(d[3] & 0xFFFFu) + __uint_as_float(d[3] & 0xFFFF0000u);
+#pragma unroll
+      for (int o = 1; o < GLANES; o <<= 1) ps += __shfl_xor(ps, o);
+      if ((kk & (GS - 1)) == 0) corr[kk >> GSHIFT][m] = -kCorr * ps;
       if (BITS == 4) d = order_for_nibbles(d);
       *reinterpret_cast<u32x4*>(&xs[m][kk]) = d;
     }
-    if (!PERROW) {
-#pragma unroll
-      for (int i = 0; i < NSE; ++i) {
-        const int gi = spart + TPR * i;
-        if (gi < GPC) sc[gi][srow] = scale_value<ST>(ss[i]);
-      }
-    }
   };
 
-  // ---- weights of one chunk: SPC 16-byte loads per stream ----
-  auto wload = [&](int ci, u32x4 (&w)[NS][SPC]) {
+  // ---- prologue: first chunks in flight, scales of the workgroup's rows into LDS ----
+  Slot w0, w1, w2;
+  stage_load(0);
+  wload(0, w0);
+  wload(min(1, nchunks - 1), w1);
+  const int nb = PERROW ? 1 : g.nb;
+  ST* scl = reinterpret_cast<ST*>(dyn);
+  if (!PERROW) {
+    constexpr int TPR = 256 / SROWS;  // threads per scale row
+    const int rowb = nb * static_cast<int>(sizeof(ST));
+    const int r = tid / TPR, part = tid % TPR;
+    const int st = __builtin_amdgcn_readfirstlane(r / (CPB * 16));  // uniform per wave
+    const int cc = min(col0 + r % (CPB * 16), g.ncols - 1);
+    const int nr = stream_rows(st);
+    const rsrc_t sres = make_rsrc(static_cast<const unsigned char*>(stream_s(st)) +
+                                      static_cast<int64_t>(e) * nr * rowb,
+                                  static_cast<uint32_t>(nr) * rowb);
+    const uint32_t sb = static_cast<uint32_t>(local_row(st, cc)) * rowb;
+    unsigned char* dst = dyn + r * rowb;
+    if ((rowb & 3) == 0) {
+#pragma unroll 8
+      for (int w = part; w < rowb / 4; w += TPR)
+        *reinterpret_cast<uint32_t*>(dst + 4 * w) = buf_load4(sres, sb + 4 * w);
+    } else {
+#pragma unroll 8
+      for (int h = part; h < rowb / 2; h += TPR)
+        *reinterpret_cast<uint16_t*>(dst + 2 * h) = buf_load2(sres, sb + 2 * h);
+    }
+  }
+  stage_store();
+  __syncthreads();
+  const ST* my_scl[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int u = 0; u < SPC; ++u) {
-        const int64_t off = min<int64_t>((static_cast<int64_t>(ci) * KC + SSK * u) * BITS / 8 + 16 * kq,
-                                         row_bytes - 16);
-        w[st][u] = *reinterpret_cast<const u32x4*>(wrow[st] + off);
-      }
-  };
+  for (int st = 0; st < NS; ++st) my_scl[st] = scl + (st * CPB * 16 + cgl * 16 + n) * nb;
 
   floatx4 acc[NS][G];
   float tot[NS][4];
@@ -243,39 +304,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[st][i] = 0.f;
   }
+  const bf16x8 zero = {};
+  const int lgrp2 = kq >> 1;
 
-  u32x4 wcur[NS][SPC];
-  stage_load(0);
-  wload(0, wcur);
-  stage_store();
-  __syncthreads();
-
-  const int lgrp2 = kq >> 1;  // lane's block among two
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int cn = min(ci + 1, nchunks - 1);
-    stage_load(cn);
-    u32x4 wnxt[NS][SPC];
-    wload(cn, wnxt);
+  // Computes this wave's super-steps of chunk ci from slot w and the LDS tile.
+  auto compute = [&](Slot& w, int ci) {
     const int k0 = ci * KC;
-
-    if (PERROW) {
+    if (PERROW && k0 < K && ks == 0) {
+      // the chunk's correction enters once per column group (split-K partials add up)
 #pragma unroll
       for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[st][0][i] += corr[0][4 * kq + i];
     }
-
 #pragma unroll
-    for (int u = 0; u < SPC; ++u) {
-      const int ks = k0 + SSK * u;  // first k of the super-step
-      if (ks >= K) break;
+    for (int v = 0; v < SPW; ++v) {
+      const int u = v * SK + ks;    // super-step inside the chunk
+      const int ksu = k0 + SSK * u; // its first k
+      if (ksu >= K) break;
+      u32x4 wv[NS];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) wv[st] = w[st][v];
       if (XPOSE) {
 #pragma unroll
-        for (int st = 0; st < NS; ++st) transpose_rows4(wcur[st][u]);
+        for (int st = 0; st < NS; ++st) transpose_rows4(wv[st]);
       }
 #pragma unroll
       for (int j = 0; j < MPS; ++j) {
-        const int kj = ks + 32 * j;
+        const int kj = ksu + 32 * j;
         if (XPOSE && kj >= K) break;
         int xo;  // this lane's 8 activations for MFMA j, offset inside the chunk
         if (BITS == 4)
@@ -287,9 +343,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           if (BITS == 4) {
-            bw[st] = decode4(wcur[st][u][j]);
+            bw[st] = decode4(wv[st][j]);
           } else {
-            u32x2 w2 = {wcur[st][u][2 * j], wcur[st][u][2 * j + 1]};
+            u32x2 w2 = {wv[st][2 * j], wv[st][2 * j + 1]};
             bw[st] = decode8(w2);
           }
         }
@@ -299,21 +355,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
             acc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw[st], acc[st][0], 0, 0, 0);
           continue;
         }
-        // span of this MFMA and where its scale blocks start and end
+        // where this MFMA's scale groups start and end
         int first, last, gl0;
-        if (BITS == 4 && XPOSE) {
-          gl0 = (kj - k0) >> gshift;
+        if (XPOSE) {
+          gl0 = (kj - k0) >> GSHIFT;
           if (G == 1) {
-            first = (kj & (gs - 1)) == 0;
-            last = ((kj + 32) & (gs - 1)) == 0 || kj + 32 >= K;
+            first = (kj & (GS - 1)) == 0;
+            last = ((kj + 32) & (GS - 1)) == 0 || kj + 32 >= K;
           } else {
             first = last = 1;  // two blocks of 16 inside the 32
           }
         } else {
-          // the MFMA's k slots spread over the whole super-step [ks, ks + SSK)
-          gl0 = (ks - k0) >> gshift;
-          first = (j == 0) && ((ks & (gs - 1)) == 0);
-          last = (j == MPS - 1) && (((ks + SSK) & (gs - 1)) == 0 || ks + SSK >= K);
+          // the MFMA's k slots spread over the whole super-step [ksu, ksu + SSK); with
+          // split-K each super-step is scaled on its own
+          gl0 = (ksu - k0) >> GSHIFT;
+          first = (j == 0) && (SK > 1 || (ksu & (GS - 1)) == 0);
+          last = (j == MPS - 1) && (SK > 1 || ((ksu + SSK) & (GS - 1)) == 0 || ksu + SSK >= K);
         }
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
@@ -325,15 +382,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
             for (int st = 0; st < NS; ++st) acc[st][gg] = c0;
           }
 #pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const bf16x8 zero = {};
-            const bf16x8 b = mine ? bw[st] : zero;
-            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, b, acc[st][gg], 0, 0, 0);
-          }
+          for (int st = 0; st < NS; ++st)
+            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? bw[st] : zero,
+                                                                  acc[st][gg], 0, 0, 0);
           if (last) {
+            const int blk = min((k0 + gl * GS) >> BSHIFT, nb - 1);
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-              const float sv = sc[gl][st * 64 + wave * 16 + n];
+              const float sv = scale_value<ST>(my_scl[st][blk]);
 #pragma unroll
               for (int i = 0; i < 4; ++i) tot[st][i] += sv * acc[st][gg][i];
             }
@@ -341,21 +397,56 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
         }
       }
     }
+  };
+  // corr holds whole-group sums, so with split-K a group must lie inside one super-step
+  // (the launcher keeps SK = 1 for blocks longer than a super-step).
+
+  auto chunk = [&](Slot& cur, Slot& ahead, int ci) {
+    stage_load(min(ci + 1, nchunks - 1));
+    wload(min(ci + 2, nchunks - 1), ahead);
+    compute(cur, ci);
     __syncthreads();
     if (ci + 1 < nchunks) stage_store();
     __syncthreads();
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int u = 0; u < SPC; ++u) wcur[st][u] = wnxt[st][u];
+  };
+  // three chunks per trip so that ring slots are fixed registers; a chunk past the end
+  // computes nothing and only re-reads the last chunk
+  for (int ci = 0; ci < nchunks; ci += 3) {
+    chunk(w0, w2, ci);
+    chunk(w1, w0, ci + 1);
+    chunk(w2, w1, ci + 2);
   }
 
   if (PERROW) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const float sv = scale_value<ST>(sbase(st)[grow[st]]);
+      const int nr = stream_rows(st);
+      const float sv = scale_value<ST>(
+          static_cast<const ST*>(stream_s(st))[static_cast<int64_t>(e) * nr + lrow[st]]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) tot[st][i] = sv * acc[st][0][i];
+    }
+  }
+
+  // ---- split-K: partial sums meet in LDS (the activation tile's space), in split order ----
+  if (SK > 1) {
+    float* red = reinterpret_cast<float*>(&xs[0][0]);  // [(SK-1) * CPB][NS * 4][64]
+    if (ks > 0) {
+      float* my = red + ((ks - 1) * CPB + cgl) * NS * 4 * 64;
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my[(st * 4 + i) * 64 + lane] = tot[st][i];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int q = 1; q < SK; ++q) {
+      const float* other = red + ((q - 1) * CPB + cgl) * NS * 4 * 64;
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[st][i] += other[(st * 4 + i) * 64 + lane];
     }
   }
 
@@ -363,8 +454,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
   float bias[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    const uint16_t* bp = static_cast<const uint16_t*>((st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b);
-    bias[st] = bp ? bf16_to_f32(bp[grow[st]]) : 0.f;
+    const uint16_t* bp = static_cast<const uint16_t*>(stream_b(st));
+    bias[st] = bp ? bf16_to_f32(bp[static_cast<int64_t>(e) * stream_rows(st) + lrow[st]]) : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -385,19 +476,47 @@ __global__ __launch_bounds__(256) void gemm_bf16_m16_kernel(GemmArgs g) {
   }
 }
 
-template <int BITS, typename ST, int MODE>
-static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  dim3 grid((g.ncols + 63) / 64, static_cast<unsigned>(max_tiles)), block(256);
+// Split-K ways from shapes only: enough wave work units to fill the chip a few times
+// over. Blocks longer than a super-step keep one split (their correction sums are whole).
+static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
+  const int ssk = bits == 4 ? 128 : 64;
+  if (g.bs > ssk) return 1;
+  const int64_t units = max_tiles * ((g.ncols + 15) / 16);
+  int sk = 1;
+  while (sk < 4 && units * sk < 12288) sk *= 2;
+  return sk;
+}
+
+// Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
+size_t gemm_bf16_lds(const GemmArgs& g, bool two_streams, bool scale_bf16, int sk) {
+  if (g.bs == 0) return 0;
+  return static_cast<size_t>(two_streams ? 2 : 1) * (4 / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
+}
+
+template <int BITS, typename ST, int MODE, int SK>
+static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  constexpr int CPB = 4 / SK;
+  dim3 grid((g.ncols + 16 * CPB - 1) / (16 * CPB), static_cast<unsigned>(max_tiles)), block(256);
+  const size_t lds = gemm_bf16_lds(g, MODE == kModeSwiglu, sizeof(ST) == 2, SK);
   switch (g.bs) {
-    case 0: gemm_bf16_m16_kernel<BITS, ST, MODE, 0><<<grid, block, 0, s>>>(g); break;
-    case 16: gemm_bf16_m16_kernel<BITS, ST, MODE, 16><<<grid, block, 0, s>>>(g); break;
-    case 32: gemm_bf16_m16_kernel<BITS, ST, MODE, 32><<<grid, block, 0, s>>>(g); break;
-    case 64: gemm_bf16_m16_kernel<BITS, ST, MODE, 64><<<grid, block, 0, s>>>(g); break;
-    case 128: gemm_bf16_m16_kernel<BITS, ST, MODE, 128><<<grid, block, 0, s>>>(g); break;
-    case 256: gemm_bf16_m16_kernel<BITS, ST, MODE, 256><<<grid, block, 0, s>>>(g); break;
-    default: gemm_bf16_m16_kernel<BITS, ST, MODE, 512><<<grid, block, 0, s>>>(g); break;
+    case 0: gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK><<<grid, block, lds, s>>>(g); break;
+    case 16: gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK><<<grid, block, lds, s>>>(g); break;
+    case 32: gemm_bf16_tile_kernel<BITS, ST, MODE, 32, SK><<<grid, block, lds, s>>>(g); break;
+    case 64: gemm_bf16_tile_kernel<BITS, ST, MODE, 64, SK><<<grid, block, lds, s>>>(g); break;
+    case 128: gemm_bf16_tile_kernel<BITS, ST, MODE, 128, SK><<<grid, block, lds, s>>>(g); break;
+    case 256: gemm_bf16_tile_kernel<BITS, ST, MODE, 256, 1><<<grid, block, lds, s>>>(g); break;
+    default: gemm_bf16_tile_kernel<BITS, ST, MODE, 512, 1><<<grid, block, lds, s>>>(g); break;
   }
   return hipGetLastError();
+}
+
+template <int BITS, typename ST, int MODE>
+static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  switch (choose_split(g, max_tiles, BITS)) {
+    case 1: return launch_sk<BITS, ST, MODE, 1>(g, max_tiles, s);
+    case 2: return launch_sk<BITS, ST, MODE, 2>(g, max_tiles, s);
+    default: return launch_sk<BITS, ST, MODE, 4>(g, max_tiles, s);
+  }
 }
 
 template <int BITS, typename ST>
