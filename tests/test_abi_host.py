@@ -179,3 +179,26 @@ def test_infinite_limit_and_defaults_marshal(lib):
     p = good(swiglu_limit=math.inf)
     assert math.isinf(p.swiglu_limit)
     assert status(p) == _lib.QMOE_OK
+
+
+def test_every_gpu_parity_case_passes_validation(lib):
+    """Each parameter block the GPU parity tests build is accepted by the host checks, so
+    that a GPU run never starts a case the library would refuse."""
+    import itertools
+
+    from synth import configs
+    from tests import test_gpu_parity as t
+    from tests.gpu_helpers import params_for
+
+    cases = [(cfg, T, 0, "route " + n) for n, (cfg, T) in t.ROUTE_CASES.items()]
+    cases += [(t.STAGE_CFGS[n] if m == 0 else t.TILE128_CFGS[n], 40 if m == 0 else 300, m,
+               "stage " + n) for n, m in t.STAGE_CASES]
+    for c in (configs.C1, configs.C2, configs.C3, configs.C4):
+        cases += [(c, T, 0, "forward") for T in c.T_points]
+    for b, bs in itertools.product(configs.C5_BITS, configs.C5_BLOCKS):
+        cases += [(configs.c5_point(b, bs), T, 0, "c5") for T in configs.C5.T_points]
+    bad = []
+    for cfg, T, m, what in cases:
+        if lib.qmoe_validate(params_for(cfg, T, tile_m=m)) != 0:
+            bad.append((what, cfg.name, T, m, lib.qmoe_last_error()))
+    assert not bad

@@ -156,25 +156,58 @@ STAGE_CFGS = {
     "relu-b8-perrow": configs.tiny(activation="relu", fusion=0, act_dtype="bf16", bits=8,
                                    block_size=0, H=256, I=128),
     "silu-f32": configs.tiny(activation="silu", fusion=0, H=128, I=64, fc1_bias=True),
+    "b4-bs256-interleaved": configs.tiny(fusion=1, act_dtype="bf16", scale_dtype="bf16",
+                                         block_size=256, H=768, I=160, fc1_bias=True),
+    "b8-bs512-shortblock": configs.tiny(fusion=2, bits=8, act_dtype="bf16", scale_dtype="bf16",
+                                        block_size=512, H=1152, I=544, E=4),
     "f32-interleaved-b8-bias": configs.tiny(fusion=1, bits=8, H=96, I=80, block_size=32,
                                             fc1_bias=True, fc2_bias=True, limit=3.0),
 }
 
 
-def _stage_inputs(name, T):
-    cfg = STAGE_CFGS[name]
+# 128-row tiles (the prefill-sized kernel): every scale layout and bit width, each gate/up
+# arrangement and the plain activations, K not a multiple of the kernel's K step (128 for
+# 4-bit, 64 for 8-bit), a short last scale block, and T large enough that experts fill
+# several tiles with a ragged last one.
+TILE128_CFGS = {
+    "c2-interleaved-b4-bs32-bias-clamp": configs.C2.with_(H=544, I=352, E=4),
+    "c3-separate-perrow-raggedK": configs.C3.with_(H=800, I=416, E=4, logit_skew=0.0),
+    "c4-b8-bs128-ragged-f32scale": configs.C4.with_(H=704, I=352, E=4),
+    "c5-b4-bs16": configs.c5_point(4, 16).with_(H=512, I=288, E=8),
+    "c5-b4-bs64-shortblock": configs.c5_point(4, 64).with_(H=544, I=224, E=8),
+    "c5-b4-bs128": configs.c5_point(4, 128).with_(H=512, I=256, E=8),
+    "c5-b8-bs16": configs.c5_point(8, 16).with_(H=512, I=256, E=8),
+    "c5-b8-bs32": configs.c5_point(8, 32).with_(H=480, I=224, E=8),
+    "c5-b8-bs64": configs.c5_point(8, 64).with_(H=512, I=256, E=8),
+    "b4-bs256-interleaved": configs.tiny(fusion=1, act_dtype="bf16", scale_dtype="bf16",
+                                         block_size=256, H=768, I=160, E=4, fc1_bias=True),
+    "b8-bs256-shortblock": configs.tiny(fusion=2, bits=8, act_dtype="bf16", scale_dtype="f32",
+                                        block_size=256, H=640, I=416, E=4),
+    "relu-b8-perrow": configs.tiny(activation="relu", fusion=0, act_dtype="bf16", bits=8,
+                                   block_size=0, H=352, I=160, E=4),
+    "identity-b4-perrow-bias": configs.tiny(activation="identity", fusion=0, act_dtype="bf16",
+                                            scale_dtype="bf16", block_size=0, H=256, I=192,
+                                            E=4, fc1_bias=True, fc2_bias=True),
+}
+
+STAGE_CASES = [(n, 0) for n in sorted(STAGE_CFGS)] + [(n, 128) for n in sorted(TILE128_CFGS)]
+
+
+def _stage_inputs(name, tile_m):
+    cfg = STAGE_CFGS[name] if tile_m == 0 else TILE128_CFGS[name]
     assert cfg.H % 32 == 0 or cfg.act_dtype == "f32"
+    T = 40 if tile_m == 0 else 300
     inp = gen.make_inputs(cfg, T)
-    p = params_for(cfg, T)
+    p = params_for(cfg, T, tile_m=tile_m)
     M = qm.qmoe_tile_m(p)
-    return cfg, inp, p, M
+    assert tile_m == 0 or M == tile_m
+    return cfg, T, inp, p, M
 
 
-@pytest.mark.parametrize("name", sorted(STAGE_CFGS))
-def test_fc1_stage(name):
-    T = 40
-    cfg, inp, p, M = _stage_inputs(name, T)
-    say("fc1", name, cfg.H, cfg.I, cfg.E, "M", M)
+@pytest.mark.parametrize("name,tile_m", STAGE_CASES)
+def test_fc1_stage(name, tile_m):
+    cfg, T, inp, p, M = _stage_inputs(name, tile_m)
+    say("fc1", name, cfg.H, cfg.I, cfg.E, "T", T, "M", M)
     ids, perm, sa, erow = oracle_layout(cfg, T, M)
     d = DeviceInputs(inp)
     rows = qm.qmoe_max_rows(p)
@@ -203,11 +236,10 @@ def test_fc1_stage(name):
     assert np.all(got[pads] == 0.0)
 
 
-@pytest.mark.parametrize("name", sorted(STAGE_CFGS))
-def test_fc2_stage(name):
-    T = 40
-    cfg, inp, p, M = _stage_inputs(name, T)
-    say("fc2", name)
+@pytest.mark.parametrize("name,tile_m", STAGE_CASES)
+def test_fc2_stage(name, tile_m):
+    cfg, T, inp, p, M = _stage_inputs(name, tile_m)
+    say("fc2", name, "T", T, "M", M)
     ids, perm, sa, erow = oracle_layout(cfg, T, M, seed=1)
     rows = qm.qmoe_max_rows(p)
     hin = gen.gen_stage_h(cfg, rows, sigma=3.0)
@@ -228,6 +260,9 @@ def test_fc2_stage(name):
     # y stays fp32 on both paths; the products of bf16 inputs are exact, so it is far
     # inside the bf16 bound
     assert err <= (1e-4 if cfg.act_dtype == "f32" else 1e-3)
+    # rows of tiles past the padded layout are never written
+    P = int(perm["padded_offsets"][-1])
+    assert np.all(got[P:] == 7.0)
 
 
 # --------------------------------------------------------------------------- combine

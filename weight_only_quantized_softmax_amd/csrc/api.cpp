@@ -49,8 +49,11 @@ int64_t n1_rows(const qmoe_params* p) {
   return (swiglu(p) && p->swiglu_fusion != 0) ? 2 * p->inter_size : p->inter_size;
 }
 
+// Rows per expert tile, from shapes only: 128-row MFMA tiles when an expert is expected
+// to receive at least 64 rows (prefill), 16-row weight-streaming tiles otherwise.
 int32_t default_tile_m(const qmoe_params* p) {
-  if (p->act_dtype == QMOE_BF16) return 16;
+  if (p->act_dtype == QMOE_BF16)
+    return (p->num_tokens * p->k >= 64 * p->num_experts) ? 128 : 16;
   const int64_t kmax = std::max(p->hidden_size, p->inter_size);
   int32_t m = 16;
   while (m > 1 && m * kmax * 4 > kF32LdsBytes) m >>= 1;
@@ -99,12 +102,13 @@ qmoe_status validate(const qmoe_params* p) {
   if (p->act_dtype == QMOE_BF16) {
     if (p->hidden_size % 32 || p->inter_size % 32)
       return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs hidden_size and inter_size multiples of 32");
-    if (m != 16) return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16 (got %d)", m);
+    if (m != 16 && m != 128)
+      return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16 or 128 (got %d)", m);
     // 32-bit buffer offsets: activations, h and one expert's stack must stay below 2 GiB
     const int64_t kmax = std::max(p->hidden_size, p->inter_size);
-    const int64_t rows_max = (p->num_tokens * p->k) / 16 + std::min<int64_t>(p->num_experts, p->num_tokens * p->k);
+    const int64_t rows_max = ((p->num_tokens * p->k) / m + std::min<int64_t>(p->num_experts, p->num_tokens * p->k)) * m;
     if (p->num_tokens * p->hidden_size * 2 >= (int64_t(1) << 31) ||
-        rows_max * 16 * p->inter_size * 2 >= (int64_t(1) << 31) ||
+        rows_max * p->inter_size * 2 >= (int64_t(1) << 31) ||
         2 * p->inter_size * kmax * p->expert_weight_bits / 8 >= (int64_t(1) << 31))
       return fail(QMOE_ERR_UNSUPPORTED, "bf16 path: a tensor or one expert's stack reaches 2 GiB");
     if (p->block_size) {
@@ -190,6 +194,15 @@ qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   return g;
 }
 
+// Kernel variant from the element types and the tile height (itself chosen from shapes).
+hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, hipStream_t s) {
+  const bool sbf = p->scale_dtype == QMOE_BF16;
+  const int bits = p->expert_weight_bits;
+  if (p->act_dtype != QMOE_BF16) return qmoe::launch_gemm_f32(g, mode, bits, sbf, max_tiles_of(p), s);
+  if (tile_m_of(p) == 128) return qmoe::launch_gemm_bf16_prefill(g, mode, bits, sbf, max_tiles_of(p), s);
+  return qmoe::launch_gemm_bf16(g, mode, bits, sbf, max_tiles_of(p), s);
+}
+
 qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
                     const int32_t* tiles, const int32_t* num_tiles, qmoe_stack fc1,
                     qmoe_stack fc3, void* h, hipStream_t s) {
@@ -213,11 +226,7 @@ qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_a
   g.ncols = static_cast<int>(p->inter_size);
   g.nb = p->block_size ? static_cast<int>((p->hidden_size + p->block_size - 1) / p->block_size) : 0;
   const int mode = swiglu(p) ? qmoe::kModeSwiglu : qmoe::kModePlainAct;
-  const bool sbf = p->scale_dtype == QMOE_BF16;
-  hipError_t e = p->act_dtype == QMOE_BF16
-                     ? qmoe::launch_gemm_bf16(g, mode, p->expert_weight_bits, sbf, max_tiles_of(p), s)
-                     : qmoe::launch_gemm_f32(g, mode, p->expert_weight_bits, sbf, max_tiles_of(p), s);
-  return device_status(e, "fc1 launch");
+  return device_status(launch_gemm(p, g, mode, s), "fc1 launch");
 }
 
 qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
@@ -235,12 +244,7 @@ qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
   g.N = static_cast<int>(p->hidden_size);
   g.ncols = static_cast<int>(p->hidden_size);
   g.nb = p->block_size ? static_cast<int>((p->inter_size + p->block_size - 1) / p->block_size) : 0;
-  const bool sbf = p->scale_dtype == QMOE_BF16;
-  hipError_t e =
-      p->act_dtype == QMOE_BF16
-          ? qmoe::launch_gemm_bf16(g, qmoe::kModeFc2, p->expert_weight_bits, sbf, max_tiles_of(p), s)
-          : qmoe::launch_gemm_f32(g, qmoe::kModeFc2, p->expert_weight_bits, sbf, max_tiles_of(p), s);
-  return device_status(e, "fc2 launch");
+  return device_status(launch_gemm(p, g, qmoe::kModeFc2, s), "fc2 launch");
 }
 
 qmoe_status need(const void* ptr, const char* name) {

@@ -1,0 +1,100 @@
+// Helpers shared by the bf16 grouped dequant GEMM kernels: raw buffer access, nibble and
+// byte decode to bfloat16, the cross-lane transpose and scale conversion.
+#pragma once
+
+#include "common.h"
+
+namespace qmoe {
+
+constexpr int kM = 16;  // rows of a decode tile
+constexpr int kRowPad = 8;  // bf16 elements of padding per LDS row (keeps 16 rows on distinct banks)
+
+// Raw buffer access: a descriptor (base, byte size) in scalar registers and a 32-bit byte
+// offset per lane; reads at or past the size return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every buffer: reads zeros
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// (v & mask) | magic in one gfx950 three-input bit operation.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  return __builtin_amdgcn_bitop3_b32(v, mask, magic, 0xEA);
+}
+
+__device__ __forceinline__ bf16x8 decode4(uint32_t w) {
+  // element order of the result: [e0, e4, e1, e5, e2, e6, e3, e7] of the 8 nibbles
+  const uint32_t magic = 0x43004300u, mask = 0x000F000Fu;
+  u32x4 r;
+  r[0] = and_or(w, mask, magic);
+  r[1] = and_or(w >> 4, mask, magic);
+  r[2] = and_or(w >> 8, mask, magic);
+  r[3] = and_or(w >> 12, mask, magic);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 decode8(u32x2 w) {
+  u32x4 r;
+  r[0] = pack_bf16_pair(static_cast<float>(w[0] & 0xFF), static_cast<float>((w[0] >> 8) & 0xFF));
+  r[1] = pack_bf16_pair(static_cast<float>((w[0] >> 16) & 0xFF), static_cast<float>(w[0] >> 24));
+  r[2] = pack_bf16_pair(static_cast<float>(w[1] & 0xFF), static_cast<float>((w[1] >> 8) & 0xFF));
+  r[3] = pack_bf16_pair(static_cast<float>((w[1] >> 16) & 0xFF), static_cast<float>(w[1] >> 24));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Reorders 8 bf16 activations [x0..x7] to [x0, x4, x1, x5, x2, x6, x3, x7] (the 4-bit
+// decode order) with four byte permutes.
+__device__ __forceinline__ u32x4 order_for_nibbles(u32x4 d) {
+  u32x4 o;
+  o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+  return o;
+}
+
+
+// Raw scale storage: bf16 scales stay 16-bit until they are used.
+template <typename ST>
+__device__ __forceinline__ float scale_value(ST v);
+template <>
+__device__ __forceinline__ float scale_value<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <>
+__device__ __forceinline__ float scale_value<float>(float v) { return v; }
+
+// 4x4 transpose of 32-bit words across the four 16-lane rows of a wave: afterwards word j
+// of row r holds what word r of row j held. gfx950 permlane32_swap exchanges the upper half
+// of its first operand with the lower half of its second; permlane16_swap exchanges the odd
+// rows of the first with the even rows of the second.
+__device__ __forceinline__ void transpose_rows4(u32x4& d) {
+  auto p02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  auto p13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  d[0] = p02[0];
+  d[2] = p02[1];
+  d[1] = p13[0];
+  d[3] = p13[1];
+  auto q01 = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+  auto q23 = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+  d[0] = q01[0];
+  d[1] = q01[1];
+  d[2] = q23[0];
+  d[3] = q23[1];
+}
+
+}  // namespace qmoe

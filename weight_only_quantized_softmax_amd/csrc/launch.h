@@ -58,6 +58,10 @@ hipError_t launch_permute(const int32_t* ids, int64_t A, int E, int M, int32_t* 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                             int64_t max_tiles, hipStream_t s);
 
+// bf16 activations, MFMA 128-row tiles (prefill-sized expert groups).
+hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                    int64_t max_tiles, hipStream_t s);
+
 // f32 activations, VALU kernel.
 hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                            int64_t max_tiles, hipStream_t s);
