@@ -9,7 +9,14 @@ the previous step.
 Default workload: the decode-shaped int4 layer (T=64, H=I=2880, E=32, k=4, 4-bit,
 block 32, bf16 scales, interleaved SwiGLU with alpha 1.702, beta 1, limit 7, bf16 biases).
 
-Prints one JSON line.
+Prints one JSON line. ``roofline.traffic`` is the dominant kernel's HBM bytes per launch
+from rocprofv3 FETCH_SIZE / WRITE_SIZE counter passes, each divided by what the same
+counter reads per byte of a plain device copy (``--calibrate-copy``); it is read from the
+counter summary committed under profiles/ and reported only while the kernel sources
+still hash to the value recorded there, else null.
+
+``--calibrate-copy MB`` instead runs a plain device-to-device copy of MB megabytes a few
+times (the known-size kernel the counters are calibrated on) and prints its size.
 """
 from __future__ import annotations
 
@@ -24,12 +31,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import hashlib  # noqa: E402
+
 import numpy as np  # noqa: E402
 
 METRIC = "tokens/s per QMoE layer + weight-stream HBM GB/s (decode T<=64; prefill T=4096)"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+CPU_SECONDS = 10.0     # minimum oracle time of the cpu_baseline sample
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "weight_only_quantized_softmax_amd", "csrc")
 
 
 def parse():
@@ -43,8 +55,56 @@ def parse():
     ap.add_argument("--block", type=int, default=32)
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens per oracle call")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     return ap.parse_args()
+
+
+def kernel_sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# dominant kernel of each path: the fc1 launch, by the file that holds it
+KERNEL_FILES = {"decode": ("gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"),
+                "prefill": ("gemm_prefill.hip", "gemm_common.h", "common.h", "launch.h"),
+                "f32": ("gemm_f32.hip", "common.h", "launch.h")}
+
+
+def committed_traffic(kind, workload):
+    """HBM bytes per launch from the committed counter summary of this kernel and workload,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_fc1_{kind}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256") != kernel_sources_sha(KERNEL_FILES[kind]):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mb, steps):
+    import torch
+    torch.cuda.set_device(0)
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(calibrate_copy_bytes=n, launches=steps)), flush=True)
 
 
 def workload(args):
@@ -89,6 +149,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return
+
     import torch
 
     import weight_only_quantized_softmax_amd as qm
@@ -102,15 +166,6 @@ def main():
     d = DeviceInputs(inp)
     p = params_for(cfg, T)
     qm.qmoe_validate(p)
-
-    per_copy = sum(t.numel() * t.element_size() for st in (d.fc1, d.fc2, d.fc3) if st
-                   for t in st if t is not None)
-    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(per_copy, 1)) + 1)
-    copies = min(copies, 64)
-    stacks = [(d.fc1, d.fc2, d.fc3)]
-    for _ in range(copies - 1):
-        stacks.append(tuple(None if st is None else tuple(None if t is None else t.clone() for t in st)
-                            for st in (d.fc1, d.fc2, d.fc3)))
 
     # stage buffers (the same kernels qmoe_forward launches, called one by one)
     A = T * cfg.k
@@ -131,25 +186,57 @@ def main():
     out = torch.empty((T, cfg.H), dtype=adt, device="cuda")
     stream = torch.cuda.current_stream()
 
+    # the routing of this batch fixes which experts are touched; rotate enough copies of the
+    # stacks that the touched bytes of the other copies exceed twice the 256 MB Infinity Cache
+    qm.qmoe_route(p, d.logits, ids, w, stream)
+    qm.qmoe_permute(p, ids, counts, offs, sa, pos, tl, nt, scratch, stream)
+    alg = algorithmic(cfg, T, counts.cpu().numpy())
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(alg["weight_bytes"], 1)) + 1)
+    copies = min(copies, 64)
+    stacks = [(d.fc1, d.fc2, d.fc3)]
+    for _ in range(copies - 1):
+        stacks.append(tuple(None if st is None else tuple(None if t is None else t.clone() for t in st)
+                            for st in (d.fc1, d.fc2, d.fc3)))
+    per_copy = sum(t.numel() * t.element_size() for st in (d.fc1, d.fc2, d.fc3) if st
+                   for t in st if t is not None)
+
+    # pre-marshalled C ABI calls, so that the host keeps ahead of the GPU at decode sizes
+    lib = qm._lib.load()
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    sid = stream.cuda_stream
+    st_args = [tuple(qm._stack(st, n) for st, n in zip(c, ("fc1", "fc2", "fc3"))) for c in stacks]
+    ws = qm.alloc_workspace(p)
+    wsn = ws.numel()
+    route = (p, ptr(d.logits), ptr(ids), ptr(w), sid)
+    perm = (p, ptr(ids), ptr(counts), ptr(offs), ptr(sa), ptr(pos), ptr(tl), ptr(nt),
+            ptr(scratch), scratch.numel(), sid)
+    comb = (p, ptr(y), ptr(pos), ptr(w), None, ptr(out), sid)
+
+    def run(status):
+        if status != 0:
+            qm.check(status)
+
     n_ev = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
 
     def step(i, timed):
-        fc1, fc2, fc3 = stacks[i % copies]
-        qm.qmoe_route(p, d.logits, ids, w, stream)
-        qm.qmoe_permute(p, ids, counts, offs, sa, pos, tl, nt, scratch, stream)
+        s1, s2, s3 = st_args[i % copies]
+        run(lib.qmoe_route(*route))
+        run(lib.qmoe_permute(*perm))
         if timed:
             ev[i][0].record(stream)
-        qm.qmoe_grouped_gemm_fc1_swiglu(p, d.x, sa, tl, nt, fc1, fc3, h, stream)
+        run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(d.x), ptr(sa), ptr(tl), ptr(nt), s1, s3,
+                                             ptr(h), sid))
         if timed:
             ev[i][1].record(stream)
             ev[i][2].record(stream)
-        qm.qmoe_grouped_gemm_fc2(p, h, tl, nt, fc2, y, stream)
+        run(lib.qmoe_grouped_gemm_fc2(p, ptr(h), ptr(tl), ptr(nt), s2, ptr(y), sid))
         if timed:
             ev[i][3].record(stream)
-        qm.qmoe_combine(p, y, pos, w, None, out, stream)
+        run(lib.qmoe_combine(*comb))
 
-    print(f"[bench] {copies} weight copies of {per_copy / 1e6:.1f} MB; warmup {args.warmup}",
+    print(f"[bench] {copies} weight copies of {per_copy / 1e6:.1f} MB "
+          f"({alg['weight_bytes'] / 1e6:.1f} MB touched); warmup {args.warmup}",
           file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i, False)
@@ -163,43 +250,54 @@ def main():
     fc1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     fc2_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
 
-    # whole-forward entry point, same inputs, for reference
-    ws = qm.alloc_workspace(p)
+    # the whole-forward entry point on the same inputs, for reference
+    xp, lp, op = ptr(d.x), ptr(d.logits), ptr(out)
+
+    def fwd(i):
+        s1, s2, s3 = st_args[i % copies]
+        run(lib.qmoe_forward(p, xp, lp, s1, s2, s3, None, op, ptr(ws), wsn, sid))
+
     for i in range(args.warmup):
-        fc1, fc2, fc3 = stacks[i % copies]
-        qm.qmoe_forward(p, d.x, d.logits, fc1, fc2, fc3, None, out, ws, stream)
+        fwd(i)
     torch.cuda.synchronize()
     f0 = time.perf_counter()
     for i in range(args.steps):
-        fc1, fc2, fc3 = stacks[i % copies]
-        qm.qmoe_forward(p, d.x, d.logits, fc1, fc2, fc3, None, out, ws, stream)
+        fwd(i)
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - f0) * 1e3 / args.steps
 
-    alg = algorithmic(cfg, T, counts.cpu().numpy())
     fc1_gbps = alg["fc1_bytes"] / (fc1_ms * 1e-3) / 1e9
     stream_gbps = alg["weight_bytes"] / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
+    kind = "f32" if cfg.act_dtype == "f32" else ("prefill" if qm.qmoe_tile_m(p) == 128 else "decode")
+    traffic = committed_traffic(kind, f"{cfg.name}_T{T}")
     decode = T <= 64
     if decode or alg["flops"] / alg["weight_bytes"] < 300:
         roof = dict(bound="hbm", achieved=round(fc1_gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(fc1_gbps / HBM_PEAK_GBPS, 4), traffic=None)
+                    frac=round(fc1_gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
     else:
         tf = alg["fc1_flops"] / (fc1_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic)
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        n = min(T, args.cpu_tokens)
         threads = min(16, os.cpu_count() or 1)
-        sel = np.arange(n)
-        print(f"[bench] cpu oracle on {n} tokens, {threads} threads", file=sys.stderr, flush=True)
+        chunk = min(T, args.cpu_tokens)
+        print(f"[bench] cpu oracle, {chunk}-token calls, {threads} threads, >= {CPU_SECONDS:.0f} s",
+              file=sys.stderr, flush=True)
+        done, calls, start = 0, 0, 0
         c0 = time.perf_counter()
-        oracle.forward(cfg, inp, sel=sel, nthreads=threads)
+        while time.perf_counter() - c0 < CPU_SECONDS:
+            sel = (start + np.arange(chunk)) % T
+            oracle.forward(cfg, inp, sel=sel, nthreads=threads)
+            done += chunk
+            calls += 1
+            start = (start + chunk) % T
         csec = time.perf_counter() - c0
-        cpu = dict(value=round(n / csec, 3), unit="tokens/s", cores=threads, kind="oracle",
-                   sample=f"first {n} of the {T} tokens of the same workload, fp64, {csec:.1f} s")
+        cpu = dict(value=round(done / csec, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"{calls} fp64 oracle forwards of {chunk} consecutive tokens of the same "
+                          f"T={T} workload (cycling through its tokens), {done} tokens in {csec:.1f} s")
 
     value = T / (ms_per_step * 1e-3)
     line = dict(
