@@ -185,6 +185,17 @@ TILE128_CFGS = {
                                         block_size=256, H=640, I=416, E=4),
     "relu-b8-perrow": configs.tiny(activation="relu", fusion=0, act_dtype="bf16", bits=8,
                                    block_size=0, H=352, I=160, E=4),
+    # per-row scales with K a whole number of K steps (128 k for 4-bit, 64 k for 8-bit):
+    # odd and even step counts, partial column blocks, every gate/up arrangement
+    "c3-separate-perrow-oddsteps": configs.C3.with_(H=384, I=256, E=4, logit_skew=0.0),
+    "perrow-b4-interleaved-bias": configs.tiny(fusion=1, act_dtype="bf16", scale_dtype="bf16",
+                                               block_size=0, H=512, I=384, E=4, fc1_bias=True,
+                                               fc2_bias=True, limit=7.0, alpha=1.702, beta=1.0),
+    "perrow-b8-concat-f32scale": configs.tiny(fusion=2, bits=8, act_dtype="bf16",
+                                              scale_dtype="f32", block_size=0, H=448, I=192, E=4,
+                                              fc1_bias=True),
+    "perrow-b4-silu": configs.tiny(activation="silu", fusion=0, act_dtype="bf16",
+                                   scale_dtype="bf16", block_size=0, H=256, I=128, E=4),
     "identity-b4-perrow-bias": configs.tiny(activation="identity", fusion=0, act_dtype="bf16",
                                             scale_dtype="bf16", block_size=0, H=256, I=192,
                                             E=4, fc1_bias=True, fc2_bias=True),

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_prefill.hip", "gemm_f32.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_f32.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -21,9 +21,23 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-I", os.path.join(HERE, "..", "include")]
 
 
+# the 128-row per-row-scale kernel keeps its 128 accumulators per lane in AGPRs: it runs one
+# wave per SIMD and needs the ordinary VGPRs for its operand and weight buffers
+NO_VGPR_FORM = {"gemm_prefill_rows.hip"}
+
+
+def _flags(src: str):
+    if src in NO_VGPR_FORM:
+        out = list(FLAGS)
+        i = out.index("-amdgpu-mfma-vgpr-form")
+        del out[i - 1:i + 1]
+        return out
+    return FLAGS
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *_flags(src), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

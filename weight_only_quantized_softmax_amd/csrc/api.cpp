@@ -1,6 +1,6 @@
 // C ABI of the QMoE library: host-side validation, workspace layout, variant choice
 // from shapes only, and launches on the caller's stream. See include/qmoe.h.
-#include "../../include/qmoe.h"
+#include "qmoe.h"
 
 #include <hip/hip_runtime.h>
 

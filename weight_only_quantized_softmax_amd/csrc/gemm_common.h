@@ -22,6 +22,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// with a wave-uniform scalar offset added to the lane offset (the range check covers the
+// lane offset)
+__device__ __forceinline__ u32x4 buf_load16s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+// 16 bytes per lane from the buffer straight into LDS: lane i's bytes land at
+// lds + 16 i (lds must be wave-uniform); out-of-range lanes write zeros
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, void* lds, uint32_t off, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           soff, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

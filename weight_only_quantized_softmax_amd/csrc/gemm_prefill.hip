@@ -383,6 +383,9 @@ static hipError_t launch_prefill_t(const GemmArgs& g, int mode, int64_t max_tile
 hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                     int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
+  // per-row scales over whole K steps take the kernel that loads activations into LDS directly
+  if (g.bs == 0 && g.K % (bits == 4 ? 128 : 64) == 0)
+    return launch_gemm_bf16_prefill_rows(g, mode, bits, scale_bf16, max_tiles, s);
   if (bits == 4)
     return scale_bf16 ? launch_prefill_t<4, uint16_t>(g, mode, max_tiles, s)
                       : launch_prefill_t<4, float>(g, mode, max_tiles, s);

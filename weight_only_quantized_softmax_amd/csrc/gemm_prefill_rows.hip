@@ -1,0 +1,327 @@
+// Grouped dequant GEMM, bf16 activations, 128-row tiles, one scale per output row: the
+// prefill shape whose expert groups fill large tiles and whose cost is the bf16 MFMA rate.
+//
+// ClikaRT "QMoEWoQ" page, class description: the expert weights stay quantized and are
+// decoded inside the GEMM dot. graiphic "QMoE" page: stacks [E, N, K/pack], per-row
+// scales when block_size is 0 ("the whole column shares one scaling factor").
+//
+// Workgroup: one 128-row tile of one expert by 256 weight rows (fused gate/up: 128 gate +
+// 128 up rows = 128 output columns; otherwise 256 output columns); four waves in a 2 x 2
+// grid of 64 rows x 128 weight rows each, 128 fp32 accumulators per lane, one wave per
+// SIMD (the register file holds the accumulators, two weight buffers and two operand sets).
+//   - Activations reach LDS without passing through registers: buffer loads with the LDS
+//     as destination, 16 bytes per lane, 16 lanes per 256-byte row segment, two stages
+//     (this K step and the next). The 16-byte granule q of row r sits at slot
+//     r * G + (q ^ key(r)) of its stage, so the 16 lanes that read one MFMA operand (16
+//     consecutive rows, one granule each) fall in distinct banks.
+//   - Each wave reads its 8 weight-row slices with one 16-byte raw buffer load per slice
+//     and K step, issued a whole step ahead into a second register buffer, and decodes
+//     them in registers: 4-bit codes become 128 + q by OR-ing the nibble into the exponent
+//     pattern of 128, 8-bit codes convert exactly. The 4-bit decode yields the elements of
+//     a dword in the order [e0 e4 e1 e5 e2 e6 e3 e7]; the activation fragment is permuted
+//     to match after its LDS read.
+//   - The zero point and the +128 offset leave through the row sums of the activations:
+//     acc - (c+z) * rowsum, scaled once per output row in the epilogue. The row sums come
+//     from v_dot2 on the fragments the waves already read (each wave sums half of its
+//     rows; the halves meet in LDS at the end).
+// One barrier per K step: the loads of step s+1 are issued before step s computes; the
+// activation loads are waited for after it, the weight loads where they are first used
+// (loads complete in issue order, so the wait counts past them).
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kRTM = 128;  // rows per tile
+constexpr int kRNB = 6;    // 16-row weight slices per wave
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_sum(uint32_t v, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
+}  // namespace
+
+template <int BITS, typename ST, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
+  constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
+  constexpr bool kTwo = (MODE == kModeSwiglu);
+  constexpr int NS = kTwo ? 2 : 1;
+  constexpr int NBS = kRNB / NS;                 // slices per stream
+  constexpr int SSK = BITS == 4 ? 128 : 64;      // K per step
+  constexpr int MPS = SSK / 32;                  // MFMA k-slices per step
+  constexpr int GPR = SSK / 8;                   // 16-byte granules per activation row
+  constexpr int NDMA = kRTM * GPR / 64 / 4;      // LDS-destination loads per wave per step
+  constexpr int BCOLS = 2 * NBS * 16;            // output columns per workgroup
+  constexpr int STAGE = kRTM * SSK;              // bf16 elements per LDS stage
+
+  // two stages as two arrays, so that the compiler can tell the stage being read from the
+  // stage being filled and does not wait for the fill before reading
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
+  __shared__ float rowsum[kRTM];
+  __shared__ uint32_t xoffs[NDMA][256];  // this thread's activation load offsets
+
+  const int tile = blockIdx.y;
+  if (tile >= *g.num_tiles) return;
+  const int e = g.tile_list[2 * tile];
+  const int valid = g.tile_list[2 * tile + 1];
+  const int64_t row0 = static_cast<int64_t>(tile) * kRTM;
+
+  const int tid = threadIdx.x;
+  // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int n = lane % 16, kq = lane / 16;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int col0 = blockIdx.x * BCOLS;
+  const int K = g.K;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
+  const int nss = (K + SSK - 1) / SSK;
+
+  auto local_row = [&](int st, int c) -> int {
+    if (!kTwo) return c;
+    if (g.fusion == 1) return 2 * c + st;
+    if (g.fusion == 2) return st * g.inter + c;
+    return c;
+  };
+  auto stream_rows = [&](int st) { return (kTwo && g.fusion == 0) ? g.inter : g.N; };
+  auto stream_w = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.w3 : g.w; };
+  auto stream_s = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s; };
+  auto stream_b = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b; };
+
+  // ---- weights: slice b of this wave is stream b / NBS, column group b % NBS. Each slice
+  // has its own descriptor (scalar registers) based at the slice's first stack row, so all
+  // slices share one lane offset. No clamping: rows past the stack fall outside the
+  // descriptor and read zeros, and columns past ncols are never stored. Lane (n, kq) reads
+  // the 16 bytes at 16 kq of the step's row segment: k = 32 kq .. +32 (4-bit) or
+  // 16 kq .. +16 (8-bit), dword j (4-bit) or dword pair j (8-bit) feeding k-slice j. ----
+  rsrc_t wres[kRNB];
+  const int lstep = (kTwo && g.fusion == 1) ? 2 : 1;  // stack rows between neighbouring columns
+#pragma unroll
+  for (int b = 0; b < kRNB; ++b) {
+    const int st = b / NBS;
+    const int nr = stream_rows(st);
+    const int r0 = local_row(st, col0 + wn * NBS * 16 + (b % NBS) * 16);  // row of lane n = 0
+    const int64_t left = static_cast<int64_t>(max(nr - r0, 0)) * row_bytes;
+    wres[b] = make_rsrc(stream_w(st) + (static_cast<int64_t>(e) * nr + r0) * row_bytes,
+                        static_cast<uint32_t>(left));
+  }
+  // the lane offset (range-checked) holds the row, the scalar offset the step along it
+  const uint32_t wlane = static_cast<uint32_t>(lstep * n) * row_bytes + 16u * kq;
+  auto wload = [&](int s, u32x4 (&w)[kRNB]) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s * SSK) * BITS / 8);
+#pragma unroll
+    for (int b = 0; b < kRNB; ++b)
+      w[b] = buf_load16s(wres[b], wlane, so);
+  };
+  // stack row of this lane's column of slice b, clamped into the stack (epilogue reads)
+  auto slice_row = [&](int b) {
+    return local_row(b / NBS, min(col0 + wn * NBS * 16 + (b % NBS) * 16 + n, g.ncols - 1));
+  };
+
+  // ---- activations: row-major stages; load i = wave + 4 t of a step fills slots
+  // 64 i .. 64 i + 63 ----
+  auto key = [](int r) { return GPR == 16 ? (r & 15) : ((r >> 1) & 7); };
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
+  // the offsets live in LDS (each thread reads back only what it wrote): registers are
+  // the scarce resource at two waves per SIMD
+#pragma unroll
+  for (int t = 0; t < NDMA; ++t) {
+    const int p = (wave + 4 * t) * 64 + lane;
+    const int r = p / GPR, q = (p % GPR) ^ key(r);
+    uint32_t off = kOutOfRange;  // padding rows land as zeros
+    if (r < valid) {
+      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
+      off = static_cast<uint32_t>((src * K + 8 * q) * 2);
+    }
+    xoffs[t][tid] = off;
+  }
+  auto xload = [&](int s, uint16_t* stage) {
+    // K is a whole number of steps (the launcher checks), so every granule is in its row
+    const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
+#pragma unroll
+    for (int t = 0; t < NDMA; ++t)
+      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t][tid], 2 * k0);
+    // the step-end wait counts the weight loads issued after these: none may move above
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // operand reads: row r = wm*64 + mt*16 + n has key(r) = key(n); granule q = 4 kq + j
+  // (4-bit) or 2 kq + j (8-bit), j in the lowest bit(s) of q, so the slot of k-slice j is
+  // that of k-slice 0 with j XOR-ed into its low bits; mt adds 16 rows.
+  const uint32_t abase =
+      static_cast<uint32_t>(((wm * 64 + n) * GPR + (((BITS == 4 ? 4 : 2) * kq) ^ key(n))) * 16);
+  auto aread = [&](const uint16_t* stage, int j, u32x4 (&xa)[4]) {
+    const uint32_t aj = abase ^ static_cast<uint32_t>(16 * j);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      xa[mt] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(stage) + aj +
+                                               mt * 16 * GPR * 16);
+  };
+
+  floatx4 acc[4][kRNB];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int b = 0; b < kRNB; ++b) acc[mt][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float rs[2] = {0.f, 0.f};  // partial row sums of slices 2*wn, 2*wn+1 of this wave's rows
+
+  auto decode = [&](const u32x4& wv, int j) -> bf16x8 {
+    if constexpr (BITS == 4) {
+      return decode4(wv[j]);
+    } else {
+      const u32x2 w2 = {wv[2 * j], wv[2 * j + 1]};
+      return decode8(w2);
+    }
+  };
+  auto compute = [&](const uint16_t* stage, const u32x4 (&w)[kRNB]) {
+    u32x4 xa[4], xn[4];
+    aread(stage, 0, xa);
+#pragma unroll
+    for (int j = 0; j < MPS; ++j) {
+      if (j + 1 < MPS) aread(stage, j + 1, xn);  // next k-slice's operands, in flight
+      if (BITS == 4) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
+      }
+      // row sums of slices 2 wn, 2 wn + 1 (wn is uniform across the wave)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 v = wn ? xa[2 + h] : xa[h];
+        rs[h] = dot2_sum(v[3], dot2_sum(v[2], dot2_sum(v[1], dot2_sum(v[0], rs[h]))));
+      }
+      bf16x8 bw = decode(w[0], j);
+#pragma unroll
+      for (int b = 0; b < kRNB; ++b) {
+        // the next slice's decode overlaps this slice's MFMAs
+        const bf16x8 bn = decode(w[b + 1 < kRNB ? b + 1 : b], j);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mt]),
+                                                               bw, acc[mt][b], 0, 0, 0);
+        bw = bn;
+      }
+      if (j + 1 < MPS) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) xa[mt] = xn[mt];
+      }
+    }
+  };
+
+  // ---- pipeline ----
+  // s_waitcnt immediate: vmcnt = the weight loads issued after a step's activation loads,
+  // expcnt and lgkmcnt left open
+  static_assert(kRNB < 64, "vmcnt holds 6 bits");
+  constexpr int kWaitX = (kRNB & 15) | ((kRNB >> 4) << 14) | (7 << 4) | (15 << 8);
+  u32x4 wa[kRNB], wb[kRNB];
+  xload(0, xs0);
+  wload(0, wa);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // whole pairs of steps (even steps read xs0 and wa, odd steps xs1 and wb), then an odd
+  // last step
+  const int npair = nss / 2;
+  for (int pi = 0; pi < npair; ++pi) {
+    const int s = 2 * pi;
+    xload(s + 1, xs1);
+    wload(s + 1, wb);
+    compute(xs0, wa);
+    __builtin_amdgcn_s_waitcnt(kWaitX);
+    __syncthreads();
+    if (s + 2 < nss) {
+      xload(s + 2, xs0);
+      wload(s + 2, wa);
+    }
+    compute(xs1, wb);
+    __builtin_amdgcn_s_waitcnt(kWaitX);
+    __syncthreads();
+  }
+  if (nss & 1) {
+    compute(xs0, wa);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // ---- row sums: reduce over the four k lane groups, meet in LDS ----
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v = rs[h];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (kq == 0) rowsum[wm * 64 + (2 * wn + h) * 16 + n] = -kCorr * v;
+  }
+  __syncthreads();
+
+  // ---- epilogue: scale per output row, bias, activation ----
+  float bias[kRNB], svr[kRNB];
+#pragma unroll
+  for (int b = 0; b < kRNB; ++b) {
+    const int st = b / NBS;
+    const int64_t idx = static_cast<int64_t>(e) * stream_rows(st) + slice_row(b);
+    const uint16_t* bp = static_cast<const uint16_t*>(stream_b(st));
+    bias[b] = bp ? bf16_to_f32(bp[idx]) : 0.f;
+    svr[b] = scale_value<ST>(static_cast<const ST*>(stream_s(st))[idx]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 64 + mt * 16 + 4 * kq + i;
+      const int64_t r = row0 + m;
+      const float rc = rowsum[m];
+#pragma unroll
+      for (int cb = 0; cb < NBS; ++cb) {
+        const int col = col0 + wn * NBS * 16 + cb * 16 + n;
+        if (col >= g.ncols) continue;
+        float z[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const int b = st * NBS + cb;
+          z[st] = svr[b] * (acc[mt][b][i] + rc) + bias[b];
+        }
+        if (MODE == kModeFc2) {
+          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];
+        } else {
+          float hv = 0.f;
+          if (m < valid)
+            hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
+                                       : plain_act(z[0], g.act);
+          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+        }
+      }
+    }
+  }
+}
+
+template <int BITS, typename ST, int MODE>
+static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  const int bcols = 2 * (kRNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
+  dim3 grid((g.ncols + bcols - 1) / bcols, static_cast<unsigned>(max_tiles)), block(256);
+  gemm_bf16_prefill_rows_kernel<BITS, ST, MODE><<<grid, block, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+template <int BITS, typename ST>
+static hipError_t launch_rows_t(const GemmArgs& g, int mode, int64_t max_tiles, hipStream_t s) {
+  if (mode == kModeSwiglu) return launch_rows_mode<BITS, ST, kModeSwiglu>(g, max_tiles, s);
+  if (mode == kModePlainAct) return launch_rows_mode<BITS, ST, kModePlainAct>(g, max_tiles, s);
+  return launch_rows_mode<BITS, ST, kModeFc2>(g, max_tiles, s);
+}
+
+hipError_t launch_gemm_bf16_prefill_rows(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                         int64_t max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  if (bits == 4)
+    return scale_bf16 ? launch_rows_t<4, uint16_t>(g, mode, max_tiles, s)
+                      : launch_rows_t<4, float>(g, mode, max_tiles, s);
+  return scale_bf16 ? launch_rows_t<8, uint16_t>(g, mode, max_tiles, s)
+                    : launch_rows_t<8, float>(g, mode, max_tiles, s);
+}
+
+}  // namespace qmoe
