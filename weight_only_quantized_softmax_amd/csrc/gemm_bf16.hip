@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
   const int64_t row0 = static_cast<int64_t>(tile) * kM;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
   const int ks = wave % SK, cgl = wave / SK;     // K split and column group of this wave
   const int col0 = blockIdx.x * CPB * 16;
@@ -167,38 +167,50 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
 
   // ---- prologue: first chunks in flight, scales of the workgroup's rows into LDS ----
   Slot w0, w1, w2;
+  // The scale rows of the workgroup's columns are one contiguous range per stream (one
+  // range in all for interleaved gate/up rows), 16-byte aligned because they start at a
+  // multiple of 16 rows. They are copied into LDS first, 16 bytes per lane with loads
+  // that target LDS, so that they arrive with the activations the prologue waits for.
+  const int nb = PERROW ? 1 : g.nb;
+  ST* scl = reinterpret_cast<ST*>(dyn);
+  const bool one_range = kTwo && g.fusion == 1;
+  if (!PERROW) {
+    const int rowb = nb * static_cast<int>(sizeof(ST));
+    const int nrange = one_range ? 1 : NS;
+    const int rows = (one_range ? 2 : 1) * CPB * 16;  // rows of one range
+#pragma unroll
+    for (int rg = 0; rg < NS; ++rg) {
+      if (rg >= nrange) break;
+      const int nr = stream_rows(rg);
+      const rsrc_t sres = make_rsrc(static_cast<const unsigned char*>(stream_s(rg)) +
+                                        static_cast<int64_t>(e) * nr * rowb,
+                                    static_cast<uint32_t>(nr) * rowb);
+      const uint32_t gstart = static_cast<uint32_t>(one_range ? 2 * col0 : local_row(rg, col0)) * rowb;
+      const int granules = rows * rowb / 16;
+      unsigned char* ldst = dyn + rg * rows * rowb;
+      for (int it = wave; it * 64 < granules; it += 4) {
+        if (it * 64 + lane < granules)
+          buf_load16_lds(sres, ldst + it * 1024, gstart + 16u * (it * 64 + lane), 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   stage_load(0);
   wload(0, w0);
   wload(min(1, nchunks - 1), w1);
-  const int nb = PERROW ? 1 : g.nb;
-  ST* scl = reinterpret_cast<ST*>(dyn);
-  if (!PERROW) {
-    constexpr int TPR = 256 / SROWS;  // threads per scale row
-    const int rowb = nb * static_cast<int>(sizeof(ST));
-    const int r = tid / TPR, part = tid % TPR;
-    const int st = __builtin_amdgcn_readfirstlane(r / (CPB * 16));  // uniform per wave
-    const int cc = min(col0 + r % (CPB * 16), g.ncols - 1);
-    const int nr = stream_rows(st);
-    const rsrc_t sres = make_rsrc(static_cast<const unsigned char*>(stream_s(st)) +
-                                      static_cast<int64_t>(e) * nr * rowb,
-                                  static_cast<uint32_t>(nr) * rowb);
-    const uint32_t sb = static_cast<uint32_t>(local_row(st, cc)) * rowb;
-    unsigned char* dst = dyn + r * rowb;
-    if ((rowb & 3) == 0) {
-#pragma unroll 8
-      for (int w = part; w < rowb / 4; w += TPR)
-        *reinterpret_cast<uint32_t*>(dst + 4 * w) = buf_load4(sres, sb + 4 * w);
-    } else {
-#pragma unroll 8
-      for (int h = part; h < rowb / 2; h += TPR)
-        *reinterpret_cast<uint16_t*>(dst + 2 * h) = buf_load2(sres, sb + 2 * h);
-    }
-  }
   stage_store();
+  // the scale copies were issued before the activation and weight loads, which complete
+  // in order: waiting until only the weight loads may be outstanding covers them
+  {
+    constexpr int kAfter = 2 * NS * SPW;
+    static_assert(kAfter < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8));
+  }
   __syncthreads();
   const ST* my_scl[NS];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) my_scl[st] = scl + (st * CPB * 16 + cgl * 16 + n) * nb;
+  for (int st = 0; st < NS; ++st)
+    my_scl[st] = scl + (one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
 
   floatx4 acc[NS][G];
   float tot[NS][4];
@@ -388,7 +400,7 @@ static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
   if (g.bs > ssk) return 1;
   const int64_t units = max_tiles * ((g.ncols + 15) / 16);
   int sk = 1;
-  while (sk < 4 && units * sk < 12288) sk *= 2;
+  while (sk < 4 && units * sk < 6144) sk *= 2;
   return sk;
 }
 
