@@ -1,4 +1,5 @@
-// Grouped dequant GEMM for bf16 activations on gfx950 MFMA (16x16x32 bf16, fp32 accumulate).
+// Grouped dequant GEMM for bf16 activations on gfx950 MFMA (16x16x32 bf16, fp32 accumulate),
+// 16-row tiles: the decode and mid-size shapes, bound by streaming the quantized weights.
 //
 // ClikaRT "QMoEWoQ" page, class description: the expert weights stay quantized and each
 // block is decoded inside the GEMM dot, never as a dense copy. graiphic "QMoE" page:
@@ -6,18 +7,17 @@
 //
 // Work unit of one wave: one 16-row tile of one expert x 16 output columns (x two weight
 // streams, gate and up, for fc1 with SwiGLU) over a range of K. A workgroup holds four
-// such waves; with split-K they share columns and divide K, and add their partial sums
-// in LDS at the end. Waves never synchronise otherwise: each streams its own weights and
-// loads its own activation fragments, both through raw buffer loads.
-// Each lane owns one output column n and one quarter kq of every 32-wide K step, and
-// decodes its 8 weights of the step in registers:
+// such waves; with split-K they share columns and divide K, and add their partial sums in
+// LDS at the end. Each lane owns one output column n and one quarter kq of every 32-wide
+// K step, and decodes its 8 weights of the step in registers:
 //   4-bit: each nibble q becomes the bfloat16 128+q by OR-ing it into the exponent
 //          pattern of 128 (exact), two nibbles per 32-bit register;
 //   8-bit: each byte becomes the exact bfloat16 q.
 // The MFMA therefore computes sum x*(c+q) with c = 128 (4-bit) or 0 (8-bit). The zero
-// point z and the offset c are removed by a second MFMA of the same activations against
-// the constant -(c+z) (exact in bfloat16), and each scale block's accumulator is
-// multiplied by the block's scale once. Per-row scales multiply the finished sum.
+// point z and the offset c leave through a second MFMA of the same activations against
+// the constant -(c+z) (exact in bfloat16), accumulated apart and added when a scale group
+// ends; each scale group's sum is multiplied by its block's scale once. Per-row scales
+// multiply the finished sum.
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -32,46 +32,46 @@ namespace qmoe {
 //   8-bit: a load holds 16 consecutive k; a super-step is 64 k and feeds two MFMAs; MFMA j
 //          takes bytes [8j, 8j+8) of every lane (k slots spread over the 64).
 // G > 1 splits an MFMA whose k slots span G scale blocks into G MFMAs, each with the
-// weights of the other blocks' lanes zeroed.
+// weights (and the correction constant) of the other blocks' lanes zeroed.
 //
 // Workgroup: four waves on one 16-row tile, as CPB groups of 16 output columns times SK
-// K-splits (CPB * SK = 4). K advances in chunks of 256 bytes of every weight row (four
-// super-steps); the split-K waves of a column group take the chunk's super-steps in turn
-// and add their partial sums in LDS at the end. Per chunk:
-//   - the tile's activations for the next chunk are loaded into registers, then stored
-//     to LDS (in the nibble order of the decode) with their block sums between two
-//     barriers at the end of the chunk;
-//   - the weights of the chunk two ahead are requested as one burst per wave into a
-//     three-slot register ring, so a row is read 256 contiguous bytes at a time and two
-//     chunks of weights stay in flight.
-// All scales of the workgroup's rows are staged in LDS once, at the start.
+// K-splits (CPB * SK = 4). K advances in chunks of 256 k (two 4-bit or four 8-bit
+// super-steps); the split-K waves of a column group take the chunk's super-steps in turn.
+// Chunk ci's activations and weights are requested two chunks ahead: the activations go
+// straight into LDS (loads that target LDS, 1 KB of row segments per load, a ring of three
+// 8 KB stages whose 16-byte granules are XOR-swizzled by row so that the 16 rows one MFMA
+// operand reads fall in distinct banks), the weights into a three-slot register ring.
+// One barrier per chunk. All scales of the workgroup's rows are copied into LDS once, at
+// the start. The small stages leave room for three or four workgroups per CU, which the
+// weight stream needs to keep enough loads in flight.
 template <int BITS, typename ST, int MODE, int BS, int SK>
 __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
   constexpr bool PERROW = BS == 0;
   constexpr bool XPOSE = BITS == 4 && BS > 0 && BS < 128;
   constexpr int G = BITS == 4 ? (BS == 16 ? 2 : 1) : (BS == 16 ? 4 : (BS == 32 ? 2 : 1));
-  constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
   constexpr bool kTwo = (MODE == kModeSwiglu);
   constexpr int NS = kTwo ? 2 : 1;              // weight streams per lane
-  constexpr int KC = BITS == 4 ? 512 : 256;     // K per chunk (256 bytes of every row)
+  constexpr int KC = 256;                       // K per chunk (128 or 256 bytes of every row)
   constexpr int SSK = BITS == 4 ? 128 : 64;     // K per super-step
-  constexpr int SPC = KC / SSK;                 // super-steps per chunk (4)
+  constexpr int SPC = KC / SSK;                 // super-steps per chunk (2 or 4)
+  static_assert(SK <= SPC, "a chunk holds at least one super-step per split");
   constexpr int SPW = SPC / SK;                 // super-steps per chunk of one wave
   constexpr int MPS = SSK / 32;                 // MFMAs per super-step
-  constexpr int NX = KC / 128;                  // activation uint4 staged per thread
   constexpr int CPB = 4 / SK;                   // 16-column groups per workgroup
-  constexpr int SROWS = NS * CPB * 16;          // scale rows staged per workgroup
-  // correction group: a scale block, or the part of one inside a K chunk
-  constexpr int GS = PERROW ? KC : (BS < KC ? BS : KC);
-  constexpr int GSHIFT = GS == 16 ? 4 : GS == 32 ? 5 : GS == 64 ? 6 : GS == 128 ? 7 : GS == 256 ? 8 : 9;
-  static_assert((1 << GSHIFT) == GS, "block length must be a power of two in [16, 512]");
+  constexpr int GPR = KC / 8;                   // 16-byte granules per chunk row (32)
+  constexpr int RPL = 64 / GPR;                 // tile rows per activation load (2)
+  constexpr int NDMA = kM / RPL / 4;            // activation loads per wave per chunk
+  constexpr int STAGE = kM * KC;                // bf16 elements of one LDS stage
   constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
-  constexpr int kMaxGroups = KC / 16;
-  constexpr int GLANES = GS / 8;                // staging lanes per correction group
+  // -(c+z) as a bf16 pair: 136 = 128 + 8 (4-bit), 128 = 0 + 128 (8-bit), both exact
+  constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;
 
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kM][KC + kRowPad];
-  __shared__ __attribute__((aligned(16))) float corr[kMaxGroups][kM];  // -(c+z)*sum(x) per group, row
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];   // scales, split-K partials
+  // three activation stages as three arrays, so that the compiler can tell the stage
+  // being read from the stages being filled
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // scales
 
   const int tile = blockIdx.y;
   if (tile >= *g.num_tiles) return;
@@ -123,54 +123,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
         w[st][v] = buf_load16(wres[st], woff[st] + static_cast<uint32_t>(ci * KC + SSK * (v * SK + ks)) * BITS / 8);
   };
 
-  // ---- activations: rows of this tile, staged K chunk by K chunk ----
+  // ---- activations: load t of wave w fills stage slots [64 (w + 4t), 64 (w + 4t) + 64):
+  // tile row r = (w + 4t) * RPL + lane / GPR, slot lane % GPR of the row holding logical
+  // granule (slot ^ key(r)) of the row's chunk segment ----
+  auto key = [](int r) { return r & 15; };
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
-  uint32_t xoff[NX];
+  uint32_t xoff[NDMA];
+  int xk[NDMA];  // first k of the lane's granule inside a chunk
 #pragma unroll
-  for (int i = 0; i < NX; ++i) {
-    const int f = tid + 256 * i;
-    const int m = f / (KC / 8), kk = (f % (KC / 8)) * 8;
-    if (m < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + m : g.sorted_assign[row0 + m] / g.topk;
-      xoff[i] = static_cast<uint32_t>((src * K + kk) * 2);
+  for (int t = 0; t < NDMA; ++t) {
+    const int r = (wave + 4 * t) * RPL + lane / GPR;
+    const int q = (lane % GPR) ^ key(r);
+    xk[t] = 8 * q;
+    if (r < valid) {
+      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
+      xoff[t] = static_cast<uint32_t>((src * K + 8 * q) * 2);
     } else {
-      xoff[i] = kOutOfRange;  // padding rows read zeros
+      xoff[t] = kOutOfRange;  // padding rows land as zeros
     }
   }
-  u32x4 sx[NX];
-  auto stage_load = [&](int ci) {
-    const int k0 = ci * KC;
+  auto xload = [&](int ci, uint16_t* stage) {
+    const int k0 = __builtin_amdgcn_readfirstlane(ci * KC);
 #pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int kk = ((tid + 256 * i) % (KC / 8)) * 8;
-      const u32x4 v = buf_load16(xres, xoff[i] + 2 * k0);
-      sx[i] = (k0 + kk < K) ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto stage_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int f = tid + 256 * i;
-      const int m = f / (KC / 8), kk = (f % (KC / 8)) * 8;
-      u32x4 d = sx[i];
-      float ps = bf16_to_f32(d[0] & 0xFFFFu) + __uint_as_float(d[0] & 0xFFFF0000u) +
-                 bf16_to_f32(d[1] & 0xFFFFu) + __uint_as_float(d[1] & 0xFFFF0000u) +
-                 bf16_to_f32(d[2] & 0xFFFFu) + __uint_as_float(d[2] & 0xFFFF0000u) +
-                 bf16_to_f32(d[3] & 0xFFFFu) + __uint_as_float(d[3] & 0xFFFF0000u);
-#pragma unroll
-      for (int o = 1; o < GLANES; o <<= 1) ps += __shfl_xor(ps, o);
-      if ((kk & (GS - 1)) == 0) corr[kk >> GSHIFT][m] = -kCorr * ps;
-      if (BITS == 4) d = order_for_nibbles(d);
-      *reinterpret_cast<u32x4*>(&xs[m][kk]) = d;
+    for (int t = 0; t < NDMA; ++t) {
+      // granules past K land as zeros too
+      const uint32_t off = (k0 + xk[t] < K) ? xoff[t] : kOutOfRange;
+      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, off, 2 * k0);
     }
   };
 
-  // ---- prologue: first chunks in flight, scales of the workgroup's rows into LDS ----
-  Slot w0, w1, w2;
+  // ---- prologue ----
   // The scale rows of the workgroup's columns are one contiguous range per stream (one
   // range in all for interleaved gate/up rows), 16-byte aligned because they start at a
-  // multiple of 16 rows. They are copied into LDS first, 16 bytes per lane with loads
-  // that target LDS, so that they arrive with the activations the prologue waits for.
+  // multiple of 16 rows. They are copied into LDS first, 16 bytes per lane with loads that
+  // target LDS.
   const int nb = PERROW ? 1 : g.nb;
   ST* scl = reinterpret_cast<ST*>(dyn);
   const bool one_range = kTwo && g.fusion == 1;
@@ -193,18 +179,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
           buf_load16_lds(sres, ldst + it * 1024, gstart + 16u * (it * 64 + lane), 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  stage_load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  Slot w0, w1, w2;
+  xload(0, xs0);
+  __builtin_amdgcn_sched_barrier(0);
   wload(0, w0);
+  if (nchunks > 1) xload(1, xs1);
+  __builtin_amdgcn_sched_barrier(0);
   wload(min(1, nchunks - 1), w1);
-  stage_store();
-  // the scale copies were issued before the activation and weight loads, which complete
-  // in order: waiting until only the weight loads may be outstanding covers them
+  // the scales and chunk 0's activations were issued first and loads complete in order:
+  // only chunk 0's weights and chunk 1's loads may still be pending
   {
-    constexpr int kAfter = 2 * NS * SPW;
-    static_assert(kAfter < 64, "vmcnt holds 6 bits");
-    __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8));
+    constexpr int kW2 = 2 * NS * SPW, kW2X = kW2 + NDMA;
+    static_assert(kW2X < 64, "vmcnt holds 6 bits");
+    if (nchunks > 1)
+      __builtin_amdgcn_s_waitcnt((kW2X & 15) | ((kW2X >> 4) << 14) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((kW2 & 15) | ((kW2 >> 4) << 14) | (7 << 4) | (15 << 8));
   }
   __syncthreads();
   const ST* my_scl[NS];
@@ -213,27 +205,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
     my_scl[st] = scl + (one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
 
   floatx4 acc[NS][G];
+  floatx4 cor[G];  // -(c+z) * the activation sums of the current scale groups
   float tot[NS][4];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
+  for (int gg = 0; gg < G; ++gg) {
+    cor[gg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) acc[st][gg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < NS; ++st) acc[st][gg] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[st][i] = 0.f;
-  }
   const bf16x8 zero = {};
+  const bf16x8 negc = __builtin_bit_cast(bf16x8, u32x4{kNegCorr, kNegCorr, kNegCorr, kNegCorr});
   const int lgrp2 = kq >> 1;
 
-  // Computes this wave's super-steps of chunk ci from slot w and the LDS tile.
-  auto compute = [&](Slot& w, int ci) {
+  // Computes this wave's super-steps of chunk ci from weight slot w and LDS stage xs.
+  auto compute = [&](Slot& w, const uint16_t* xs, int ci) {
     const int k0 = ci * KC;
-    if (PERROW && k0 < K && ks == 0) {
-      // the chunk's correction enters once per column group (split-K partials add up)
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[st][0][i] += corr[0][4 * kq + i];
-    }
 #pragma unroll
     for (int v = 0; v < SPW; ++v) {
       const int u = v * SK + ks;    // super-step inside the chunk
@@ -250,12 +240,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
       for (int j = 0; j < MPS; ++j) {
         const int kj = ksu + 32 * j;
         if (XPOSE && kj >= K) break;
-        int xo;  // this lane's 8 activations for MFMA j, offset inside the chunk
+        int q;  // logical granule of this lane's 8 activations for MFMA j, inside the chunk
         if (BITS == 4)
-          xo = XPOSE ? (SSK * u + 32 * j + 8 * kq) : (SSK * u + 32 * kq + 8 * j);
+          q = XPOSE ? (16 * u + 4 * j + kq) : (16 * u + 4 * kq + j);
         else
-          xo = SSK * u + 16 * kq + 8 * j;
-        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&xs[n][xo]);
+          q = 8 * u + 2 * kq + j;
+        u32x4 xr = *reinterpret_cast<const u32x4*>(xs + (n * GPR + (q ^ key(n))) * 8);
+        if (BITS == 4) xr = order_for_nibbles(xr);
+        const bf16x8 xa = __builtin_bit_cast(bf16x8, xr);
         bf16x8 bw[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -266,72 +258,75 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
             bw[st] = decode8(w2);
           }
         }
-        if (PERROW) {
-#pragma unroll
-          for (int st = 0; st < NS; ++st)
-            acc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw[st], acc[st][0], 0, 0, 0);
-          continue;
-        }
-        // where this MFMA's scale groups start and end
-        int first, last, gl0;
-        if (XPOSE) {
-          gl0 = (kj - k0) >> GSHIFT;
-          if (G == 1) {
-            first = (kj & (GS - 1)) == 0;
-            last = ((kj + 32) & (GS - 1)) == 0 || kj + 32 >= K;
+        // where this MFMA's scale groups end
+        int last = 0, gl0 = 0;
+        if (!PERROW) {
+          if (XPOSE) {
+            gl0 = kj >> BSHIFT;
+            last = G > 1 || ((kj + 32) & (BS - 1)) == 0 || kj + 32 >= K;
           } else {
-            first = last = 1;  // two blocks of 16 inside the 32
+            // the MFMA's k slots spread over the whole super-step; a block longer than a
+            // super-step is summed and scaled one super-step at a time
+            gl0 = ksu >> BSHIFT;
+            last = j == MPS - 1;
           }
-        } else {
-          // the MFMA's k slots spread over the whole super-step [ksu, ksu + SSK); with
-          // split-K each super-step is scaled on its own
-          gl0 = (ksu - k0) >> GSHIFT;
-          first = (j == 0) && (SK > 1 || (ksu & (GS - 1)) == 0);
-          last = (j == MPS - 1) && (SK > 1 || ((ksu + SSK) & (GS - 1)) == 0 || ksu + SSK >= K);
         }
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
-          const int gl = gl0 + gg;
           const bool mine = (G == 1) || (G == 2 ? (lgrp2 == gg) : (kq == gg));
-          if (first) {
-            const floatx4 c0 = *reinterpret_cast<const floatx4*>(&corr[gl][4 * kq]);
-#pragma unroll
-            for (int st = 0; st < NS; ++st) acc[st][gg] = c0;
-          }
+          cor[gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? negc : zero, cor[gg], 0, 0, 0);
 #pragma unroll
           for (int st = 0; st < NS; ++st)
             acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? bw[st] : zero,
                                                                   acc[st][gg], 0, 0, 0);
           if (last) {
-            const int blk = min((k0 + gl * GS) >> BSHIFT, nb - 1);
+            // the group's block: the two blocks of 16 inside one 4-bit MFMA are gl0 and
+            // gl0 + 1, the blocks of an 8-bit super-step gl0 + gg; otherwise the MFMA or
+            // super-step lies inside block gl0
+            const int blk = min(gl0 + (G > 1 ? gg : 0), nb - 1);
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
               const float sv = scale_value<ST>(my_scl[st][blk]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) tot[st][i] += sv * acc[st][gg][i];
+              for (int i = 0; i < 4; ++i) tot[st][i] += sv * (acc[st][gg][i] + cor[gg][i]);
+              acc[st][gg] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
+            cor[gg] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
     }
   };
-  // corr holds whole-group sums, so with split-K a group must lie inside one super-step
-  // (the launcher keeps SK = 1 for blocks longer than a super-step).
 
-  auto chunk = [&](Slot& cur, Slot& ahead, int ci) {
-    stage_load(min(ci + 1, nchunks - 1));
+  // s_waitcnt immediate: vmcnt = the loads issued after chunk ci + 1's activation loads
+  // (chunk ci + 1's weights, chunk ci + 2's activations and weights), expcnt and lgkmcnt
+  // left open
+  constexpr int kAfter = NDMA + 2 * NS * SPW;
+  static_assert(kAfter < 64, "vmcnt holds 6 bits");
+  constexpr int kWaitX = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+  // chunk ci computes from stage / slot ci % 3 and requests chunk ci + 2 into the third
+  auto chunk = [&](Slot& cur, const uint16_t* xcur, Slot& ahead, uint16_t* xahead, int ci) {
+    if (ci + 2 < nchunks) xload(ci + 2, xahead);
+    __builtin_amdgcn_sched_barrier(0);
     wload(min(ci + 2, nchunks - 1), ahead);
-    compute(cur, ci);
-    __syncthreads();
-    if (ci + 1 < nchunks) stage_store();
-    __syncthreads();
+    compute(cur, xcur, ci);
+    // chunk ci + 1's activations have landed once at most the later loads are pending.
+    // A bare barrier follows: every LDS read of chunk ci has returned (the MFMAs used
+    // it), and a workgroup fence would also wait for chunk ci + 2's loads.
+    if (ci + 2 < nchunks)
+      __builtin_amdgcn_s_waitcnt(kWaitX);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // three chunks per trip so that ring slots are fixed registers; a chunk past the end
-  // computes nothing and only re-reads the last chunk
+  // three chunks per trip so that ring slots and stages are fixed; a chunk past the end
+  // computes nothing and only re-reads the last chunk's weights
   for (int ci = 0; ci < nchunks; ci += 3) {
-    chunk(w0, w2, ci);
-    chunk(w1, w0, ci + 1);
-    chunk(w2, w1, ci + 2);
+    chunk(w0, xs0, w2, xs2, ci);
+    chunk(w1, xs1, w0, xs0, ci + 1);
+    chunk(w2, xs2, w1, xs1, ci + 2);
   }
 
   if (PERROW) {
@@ -341,13 +336,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
       const float sv = scale_value<ST>(
           static_cast<const ST*>(stream_s(st))[static_cast<int64_t>(e) * nr + lrow[st]]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tot[st][i] = sv * acc[st][0][i];
+      for (int i = 0; i < 4; ++i) tot[st][i] = sv * (acc[st][0][i] + cor[0][i]);
     }
   }
 
-  // ---- split-K: partial sums meet in LDS (the activation tile's space), in split order ----
+  // ---- split-K: partial sums meet in LDS (the first activation stage), in split order ----
   if (SK > 1) {
-    float* red = reinterpret_cast<float*>(&xs[0][0]);  // [(SK-1) * CPB][NS * 4][64]
+    float* red = reinterpret_cast<float*>(xs0);  // [(SK-1) * CPB][NS * 4][64]
     if (ks > 0) {
       float* my = red + ((ks - 1) * CPB + cgl) * NS * 4 * 64;
 #pragma unroll
@@ -394,13 +389,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
 }
 
 // Split-K ways from shapes only: enough wave work units to fill the chip a few times
-// over. Blocks longer than a super-step keep one split (their correction sums are whole).
+// over, at most the super-steps of a chunk. Blocks longer than a super-step keep one split
+// (their groups are summed one super-step at a time in the split's own order).
 static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
   const int ssk = bits == 4 ? 128 : 64;
   if (g.bs > ssk) return 1;
   const int64_t units = max_tiles * ((g.ncols + 15) / 16);
+  const int cap = 256 / ssk;
   int sk = 1;
-  while (sk < 4 && units * sk < 6144) sk *= 2;
+  while (sk < cap && units * sk < 6144) sk *= 2;
   return sk;
 }
 
@@ -432,7 +429,7 @@ static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t
   switch (choose_split(g, max_tiles, BITS)) {
     case 1: return launch_sk<BITS, ST, MODE, 1>(g, max_tiles, s);
     case 2: return launch_sk<BITS, ST, MODE, 2>(g, max_tiles, s);
-    default: return launch_sk<BITS, ST, MODE, 4>(g, max_tiles, s);
+    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4>(g, max_tiles, s);
   }
 }
 
