@@ -15,9 +15,9 @@
 //   8-bit: each byte becomes the exact bfloat16 q.
 // The MFMA therefore computes sum x*(c+q) with c = 128 (4-bit) or 0 (8-bit). The zero
 // point z and the offset c leave through a second MFMA of the same activations against
-// the constant -(c+z) (exact in bfloat16), accumulated apart and added when a scale group
-// ends; each scale group's sum is multiplied by its block's scale once. Per-row scales
-// multiply the finished sum.
+// the constant -(c+z) (exact in bfloat16) into the same accumulator; a scale group's
+// accumulator starts from zero and is multiplied by its block's scale once, when the
+// group ends. Per-row scales multiply the finished sum.
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -44,8 +44,11 @@ namespace qmoe {
 // One barrier per chunk. All scales of the workgroup's rows are copied into LDS once, at
 // the start. The small stages leave room for three or four workgroups per CU, which the
 // weight stream needs to keep enough loads in flight.
+constexpr int kDecWaves = 4;  // waves per workgroup
+
 template <int BITS, typename ST, int MODE, int BS, int SK>
-__global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
+  constexpr int NW = kDecWaves;
   constexpr bool PERROW = BS == 0;
   constexpr bool XPOSE = BITS == 4 && BS > 0 && BS < 128;
   constexpr int G = BITS == 4 ? (BS == 16 ? 2 : 1) : (BS == 16 ? 4 : (BS == 32 ? 2 : 1));
@@ -57,10 +60,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
   static_assert(SK <= SPC, "a chunk holds at least one super-step per split");
   constexpr int SPW = SPC / SK;                 // super-steps per chunk of one wave
   constexpr int MPS = SSK / 32;                 // MFMAs per super-step
-  constexpr int CPB = 4 / SK;                   // 16-column groups per workgroup
+  constexpr int CPB = NW / SK;                  // 16-column groups per workgroup
   constexpr int GPR = KC / 8;                   // 16-byte granules per chunk row (32)
   constexpr int RPL = 64 / GPR;                 // tile rows per activation load (2)
-  constexpr int NDMA = kM / RPL / 4;            // activation loads per wave per chunk
+  constexpr int NDMA = kM / RPL / NW;           // activation loads per wave per chunk
+  static_assert(NDMA >= 1, "every wave takes part in the activation loads");
   constexpr int STAGE = kM * KC;                // bf16 elements of one LDS stage
   constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
   // -(c+z) as a bf16 pair: 136 = 128 + 8 (4-bit), 128 = 0 + 128 (8-bit), both exact
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
   int xk[NDMA];  // first k of the lane's granule inside a chunk
 #pragma unroll
   for (int t = 0; t < NDMA; ++t) {
-    const int r = (wave + 4 * t) * RPL + lane / GPR;
+    const int r = (wave + NW * t) * RPL + lane / GPR;
     const int q = (lane % GPR) ^ key(r);
     xk[t] = 8 * q;
     if (r < valid) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
     for (int t = 0; t < NDMA; ++t) {
       // granules past K land as zeros too
       const uint32_t off = (k0 + xk[t] < K) ? xoff[t] : kOutOfRange;
-      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, off, 2 * k0);
+      buf_load16_lds(xres, stage + (wave + NW * t) * 64 * 8, off, 2 * k0);
     }
   };
 
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
       const uint32_t gstart = static_cast<uint32_t>(one_range ? 2 * col0 : local_row(rg, col0)) * rowb;
       const int granules = rows * rowb / 16;
       unsigned char* ldst = dyn + rg * rows * rowb;
-      for (int it = wave; it * 64 < granules; it += 4) {
+      for (int it = wave; it * 64 < granules; it += NW) {
         if (it * 64 + lane < granules)
           buf_load16_lds(sres, ldst + it * 1024, gstart + 16u * (it * 64 + lane), 0);
       }
@@ -205,14 +209,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
     my_scl[st] = scl + (one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
 
   floatx4 acc[NS][G];
-  floatx4 cor[G];  // -(c+z) * the activation sums of the current scale groups
   float tot[NS][4];
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    cor[gg] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-    for (int st = 0; st < NS; ++st) acc[st][gg] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int st = 0; st < NS; ++st) acc[st][gg] = zero4;
 #pragma unroll
   for (int st = 0; st < NS; ++st)
 #pragma unroll
@@ -258,27 +260,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
             bw[st] = decode8(w2);
           }
         }
-        // where this MFMA's scale groups end
-        int last = 0, gl0 = 0;
+        // where this MFMA's scale groups start and end
+        int first = 0, last = 0, gl0 = 0;
         if (!PERROW) {
           if (XPOSE) {
             gl0 = kj >> BSHIFT;
+            first = G > 1 || (kj & (BS - 1)) == 0;
             last = G > 1 || ((kj + 32) & (BS - 1)) == 0 || kj + 32 >= K;
           } else {
             // the MFMA's k slots spread over the whole super-step; a block longer than a
             // super-step is summed and scaled one super-step at a time
             gl0 = ksu >> BSHIFT;
+            first = j == 0;
             last = j == MPS - 1;
           }
         }
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
           const bool mine = (G == 1) || (G == 2 ? (lgrp2 == gg) : (kq == gg));
-          cor[gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? negc : zero, cor[gg], 0, 0, 0);
+          // each stream's accumulator takes the correction -(c+z) * sum x and the products;
+          // a group starts from zero
 #pragma unroll
-          for (int st = 0; st < NS; ++st)
+          for (int st = 0; st < NS; ++st) {
+            const floatx4 from = first ? zero4 : acc[st][gg];
+            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? negc : zero, from, 0, 0, 0);
             acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? bw[st] : zero,
                                                                   acc[st][gg], 0, 0, 0);
+          }
           if (last) {
             // the group's block: the two blocks of 16 inside one 4-bit MFMA are gl0 and
             // gl0 + 1, the blocks of an 8-bit super-step gl0 + gg; otherwise the MFMA or
@@ -288,10 +296,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
             for (int st = 0; st < NS; ++st) {
               const float sv = scale_value<ST>(my_scl[st][blk]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) tot[st][i] += sv * (acc[st][gg][i] + cor[gg][i]);
-              acc[st][gg] = floatx4{0.f, 0.f, 0.f, 0.f};
+              for (int i = 0; i < 4; ++i) tot[st][i] += sv * acc[st][gg][i];
             }
-            cor[gg] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
@@ -336,12 +342,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_tile_kernel(GemmArgs g) {
       const float sv = scale_value<ST>(
           static_cast<const ST*>(stream_s(st))[static_cast<int64_t>(e) * nr + lrow[st]]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tot[st][i] = sv * (acc[st][0][i] + cor[0][i]);
+      for (int i = 0; i < 4; ++i) tot[st][i] = sv * acc[st][0][i];
     }
   }
 
   // ---- split-K: partial sums meet in LDS (the first activation stage), in split order ----
   if (SK > 1) {
+    static_assert((SK - 1) * CPB * NS * 4 * 64 * 4 <= STAGE * 2, "split-K partials fit one stage");
     float* red = reinterpret_cast<float*>(xs0);  // [(SK-1) * CPB][NS * 4][64]
     if (ks > 0) {
       float* my = red + ((ks - 1) * CPB + cgl) * NS * 4 * 64;
@@ -404,13 +411,13 @@ static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
 // Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
 size_t gemm_bf16_lds(const GemmArgs& g, bool two_streams, bool scale_bf16, int sk) {
   if (g.bs == 0) return 0;
-  return static_cast<size_t>(two_streams ? 2 : 1) * (4 / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
+  return static_cast<size_t>(two_streams ? 2 : 1) * (kDecWaves / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
 }
 
 template <int BITS, typename ST, int MODE, int SK>
 static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  constexpr int CPB = 4 / SK;
-  dim3 grid((g.ncols + 16 * CPB - 1) / (16 * CPB), static_cast<unsigned>(max_tiles)), block(256);
+  constexpr int CPB = kDecWaves / SK;
+  dim3 grid((g.ncols + 16 * CPB - 1) / (16 * CPB), static_cast<unsigned>(max_tiles)), block(kDecWaves * 64);
   const size_t lds = gemm_bf16_lds(g, MODE == kModeSwiglu, sizeof(ST) == 2, SK);
   switch (g.bs) {
     case 0: gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK><<<grid, block, lds, s>>>(g); break;
