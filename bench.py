@@ -70,7 +70,7 @@ def kernel_sources_sha(files):
 
 # dominant kernel of each path: the fc1 launch, by the file that holds it
 KERNEL_FILES = {"decode": ("gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"),
-                "prefill": ("gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_common.h", "common.h", "launch.h"),
+                "prefill": ("gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_common.h", "common.h", "launch.h"),
                 "f32": ("gemm_f32.hip", "common.h", "launch.h")}
 
 

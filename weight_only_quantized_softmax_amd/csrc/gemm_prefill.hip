@@ -386,6 +386,9 @@ hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool 
   // per-row scales over whole K steps take the kernel that loads activations into LDS directly
   if (g.bs == 0 && g.K % (bits == 4 ? 128 : 64) == 0)
     return launch_gemm_bf16_prefill_rows(g, mode, bits, scale_bf16, max_tiles, s);
+  // block scales likewise, except 8-bit blocks shorter than a 64-wide K step
+  if (prefill_blk_supports(g, bits))
+    return launch_gemm_bf16_prefill_blk(g, mode, bits, scale_bf16, max_tiles, s);
   if (bits == 4)
     return scale_bf16 ? launch_prefill_t<4, uint16_t>(g, mode, max_tiles, s)
                       : launch_prefill_t<4, float>(g, mode, max_tiles, s);

@@ -67,6 +67,12 @@ hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool 
 hipError_t launch_gemm_bf16_prefill_rows(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                          int64_t max_tiles, hipStream_t s);
 
+// bf16 activations, MFMA 128-row tiles, one scale per output row and K-block, K a multiple
+// of 128 (4-bit) or 64 (8-bit); 8-bit blocks of at least 64.
+bool prefill_blk_supports(const GemmArgs& g, int bits);
+hipError_t launch_gemm_bf16_prefill_blk(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                        int64_t max_tiles, hipStream_t s);
+
 // f32 activations, VALU kernel.
 hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                            int64_t max_tiles, hipStream_t s);
