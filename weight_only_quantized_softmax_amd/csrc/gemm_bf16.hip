@@ -5,8 +5,9 @@
 // block is decoded inside the GEMM dot, never as a dense copy. graiphic "QMoE" page:
 // stack shapes [E, N, K/pack], scales per row or per K-block, activation attributes.
 //
-// Work unit of one wave: one 16-row tile of one expert x 16 output columns (x two weight
-// streams, gate and up, for fc1 with SwiGLU) over a range of K. A workgroup holds four
+// Work unit of one wave: one 16-row tile of one expert x two 16-row weight slices (gate
+// and up of 16 output columns for fc1 with SwiGLU, otherwise two neighbouring groups of 16
+// output columns) over a range of K. A workgroup holds four
 // such waves; with split-K they share columns and divide K, and add their partial sums in
 // LDS at the end. Each lane owns one output column n and one quarter kq of every 32-wide
 // K step, and decodes its 8 weights of the step in registers:
@@ -34,8 +35,8 @@ namespace qmoe {
 // G > 1 splits an MFMA whose k slots span G scale blocks into G MFMAs, each with the
 // weights (and the correction constant) of the other blocks' lanes zeroed.
 //
-// Workgroup: four waves on one 16-row tile, as CPB groups of 16 output columns times SK
-// K-splits (CPB * SK = 4). K advances in chunks of 256 k (two 4-bit or four 8-bit
+// Workgroup: four waves on one 16-row tile, as CPB column groups (one wave's columns)
+// times SK K-splits (CPB * SK = 4). K advances in chunks of 256 k (two 4-bit or four 8-bit
 // super-steps); the split-K waves of a column group take the chunk's super-steps in turn.
 // Chunk ci's activations and weights are requested two chunks ahead: the activations go
 // straight into LDS (loads that target LDS, 1 KB of row segments per load, a ring of three
@@ -53,14 +54,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   constexpr bool XPOSE = BITS == 4 && BS > 0 && BS < 128;
   constexpr int G = BITS == 4 ? (BS == 16 ? 2 : 1) : (BS == 16 ? 4 : (BS == 32 ? 2 : 1));
   constexpr bool kTwo = (MODE == kModeSwiglu);
-  constexpr int NS = kTwo ? 2 : 1;              // weight streams per lane
+  constexpr int NS = 2;                         // weight streams (16-row slices) per lane
+  constexpr int CW = kTwo ? 16 : 32;            // output columns per wave
   constexpr int KC = 256;                       // K per chunk (128 or 256 bytes of every row)
   constexpr int SSK = BITS == 4 ? 128 : 64;     // K per super-step
   constexpr int SPC = KC / SSK;                 // super-steps per chunk (2 or 4)
   static_assert(SK <= SPC, "a chunk holds at least one super-step per split");
   constexpr int SPW = SPC / SK;                 // super-steps per chunk of one wave
   constexpr int MPS = SSK / 32;                 // MFMAs per super-step
-  constexpr int CPB = NW / SK;                  // 16-column groups per workgroup
+  constexpr int CPB = NW / SK;                  // column groups per workgroup
   constexpr int GPR = KC / 8;                   // 16-byte granules per chunk row (32)
   constexpr int RPL = 64 / GPR;                 // tile rows per activation load (2)
   constexpr int NDMA = kM / RPL / NW;           // activation loads per wave per chunk
@@ -87,9 +89,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
   const int ks = wave % SK, cgl = wave / SK;     // K split and column group of this wave
-  const int col0 = blockIdx.x * CPB * 16;
-  const int col = col0 + cgl * 16 + n;
-  const bool col_ok = col < g.ncols;
+  const int col0 = blockIdx.x * CPB * CW;
+  // output column of stream st of this lane (SwiGLU: both streams feed one column)
+  auto col_of = [&](int st) { return col0 + cgl * CW + (kTwo ? 0 : 16 * st) + n; };
   const int K = g.K;
   const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
   const int nchunks = (K + KC - 1) / KC;
@@ -105,7 +107,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   auto stream_s = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s; };
   auto stream_b = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b; };
 
-  const int c = col_ok ? col : g.ncols - 1;
   rsrc_t wres[NS];
   uint32_t woff[NS];
   int lrow[NS];
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
     const int nr = stream_rows(st);
     wres[st] = make_rsrc(stream_w(st) + static_cast<int64_t>(e) * nr * row_bytes,
                          static_cast<uint32_t>(nr) * row_bytes);
-    lrow[st] = local_row(st, c);
+    lrow[st] = local_row(st, min(col_of(st), g.ncols - 1));  // clamped: stored only if valid
     woff[st] = static_cast<uint32_t>(lrow[st]) * row_bytes + 16 * kq;
   }
   // the weights of one wave for chunk ci: its SPW super-steps, in one burst
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   // target LDS.
   const int nb = PERROW ? 1 : g.nb;
   ST* scl = reinterpret_cast<ST*>(dyn);
-  const bool one_range = kTwo && g.fusion == 1;
+  // one range for interleaved gate/up rows and for two column groups
+  const bool one_range = !kTwo || g.fusion == 1;
   if (!PERROW) {
     const int rowb = nb * static_cast<int>(sizeof(ST));
     const int nrange = one_range ? 1 : NS;
@@ -175,7 +177,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
       const rsrc_t sres = make_rsrc(static_cast<const unsigned char*>(stream_s(rg)) +
                                         static_cast<int64_t>(e) * nr * rowb,
                                     static_cast<uint32_t>(nr) * rowb);
-      const uint32_t gstart = static_cast<uint32_t>(one_range ? 2 * col0 : local_row(rg, col0)) * rowb;
+      const int rstart = one_range ? (kTwo ? 2 * col0 : col0) : local_row(rg, col0);
+      const uint32_t gstart = static_cast<uint32_t>(rstart) * rowb;
       const int granules = rows * rowb / 16;
       unsigned char* ldst = dyn + rg * rows * rowb;
       for (int it = wave; it * 64 < granules; it += NW) {
@@ -206,7 +209,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   const ST* my_scl[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st)
-    my_scl[st] = scl + (one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
+    my_scl[st] = scl + (!kTwo ? cgl * 32 + 16 * st + n
+                        : one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
 
   floatx4 acc[NS][G];
   float tot[NS][4];
@@ -369,7 +373,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
     }
   }
 
-  if (!col_ok) return;
   float bias[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
@@ -380,17 +383,24 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * kq + i;
     const int64_t r = row0 + m;
-    if (MODE == kModeFc2) {
-      if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[0][i] + bias[0];
-    } else {
+    if (MODE == kModeSwiglu) {
+      const int col = col_of(0);
+      if (col >= g.ncols) continue;
       float h = 0.f;
-      if (m < valid) {
-        if (MODE == kModeSwiglu)
-          h = swiglu(tot[0][i] + bias[0], tot[NS - 1][i] + bias[NS - 1], g.alpha, g.beta, g.limit);
-        else
-          h = plain_act(tot[0][i] + bias[0], g.act);
-      }
+      if (m < valid) h = swiglu(tot[0][i] + bias[0], tot[1][i] + bias[1], g.alpha, g.beta, g.limit);
       static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
+    } else {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int col = col_of(st);
+        if (col >= g.ncols) continue;
+        if (MODE == kModeFc2) {
+          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[st][i] + bias[st];
+        } else {
+          const float h = m < valid ? plain_act(tot[st][i] + bias[st], g.act) : 0.f;
+          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
+        }
+      }
     }
   }
 }
@@ -398,10 +408,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs
 // Split-K ways from shapes only: enough wave work units to fill the chip a few times
 // over, at most the super-steps of a chunk. Blocks longer than a super-step keep one split
 // (their groups are summed one super-step at a time in the split's own order).
-static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
+static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits, int wave_cols) {
   const int ssk = bits == 4 ? 128 : 64;
   if (g.bs > ssk) return 1;
-  const int64_t units = max_tiles * ((g.ncols + 15) / 16);
+  const int64_t units = max_tiles * ((g.ncols + wave_cols - 1) / wave_cols);
   const int cap = 256 / ssk;
   int sk = 1;
   while (sk < cap && units * sk < 6144) sk *= 2;
@@ -409,16 +419,17 @@ static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits) {
 }
 
 // Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
-size_t gemm_bf16_lds(const GemmArgs& g, bool two_streams, bool scale_bf16, int sk) {
+size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk) {
   if (g.bs == 0) return 0;
-  return static_cast<size_t>(two_streams ? 2 : 1) * (kDecWaves / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
+  return static_cast<size_t>(2) * (kDecWaves / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
 }
 
 template <int BITS, typename ST, int MODE, int SK>
 static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   constexpr int CPB = kDecWaves / SK;
-  dim3 grid((g.ncols + 16 * CPB - 1) / (16 * CPB), static_cast<unsigned>(max_tiles)), block(kDecWaves * 64);
-  const size_t lds = gemm_bf16_lds(g, MODE == kModeSwiglu, sizeof(ST) == 2, SK);
+  const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
+  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles)), block(kDecWaves * 64);
+  const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK);
   switch (g.bs) {
     case 0: gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK><<<grid, block, lds, s>>>(g); break;
     case 16: gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK><<<grid, block, lds, s>>>(g); break;
@@ -433,7 +444,7 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 
 template <int BITS, typename ST, int MODE>
 static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  switch (choose_split(g, max_tiles, BITS)) {
+  switch (choose_split(g, max_tiles, BITS, MODE == kModeSwiglu ? 16 : 32)) {
     case 1: return launch_sk<BITS, ST, MODE, 1>(g, max_tiles, s);
     case 2: return launch_sk<BITS, ST, MODE, 2>(g, max_tiles, s);
     default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4>(g, max_tiles, s);

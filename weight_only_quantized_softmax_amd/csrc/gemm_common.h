@@ -111,4 +111,34 @@ __device__ __forceinline__ void transpose_rows4(u32x4& d) {
   d[3] = q23[1];
 }
 
+// Work order of the 128-row kernels. The hardware hands the workgroups of a 1-D grid to
+// the 8 XCDs in turn (workgroup i to XCD i % 8), and each XCD has its own L2. Workgroup i
+// takes item (i % 8) * per + i / 8 of the live items (per = ceil(live / 8)), so each XCD
+// works through one contiguous run of items. Items run in bands of kBand consecutive tiles
+// (one expert's tiles are consecutive): inside a band, column block by column block, the
+// band's tiles in turn. The workgroups an XCD runs at once then cover a few tiles times a
+// few dozen column blocks, and its L2 serves each weight block to every tile of the band
+// and each activation tile to every column block. Correct for any placement; the grid
+// must hold at least 8 * per workgroups (the launcher rounds columns x tiles up to a
+// multiple of 8).
+constexpr int kXcds = 8;
+constexpr int kBand = 4;
+__device__ __forceinline__ bool xcd_item(int num_tiles, int cblocks, int& tile, int& cb) {
+  const int live = num_tiles * cblocks;
+  const int per = (live + kXcds - 1) / kXcds;
+  const int hw = blockIdx.x;
+  const int k = hw / kXcds;
+  const int item = (hw % kXcds) * per + k;
+  if (k >= per || item >= live) return false;
+  const int band = item / (kBand * cblocks);
+  const int r = item - band * kBand * cblocks;
+  const int bt = min(kBand, num_tiles - band * kBand);  // tiles of this band
+  cb = r / bt;
+  tile = band * kBand + (r - cb * bt);
+  return true;
+}
+__host__ __device__ constexpr unsigned xcd_grid(int cblocks, int64_t max_tiles) {
+  return static_cast<unsigned>((cblocks * max_tiles + kXcds - 1) / kXcds * kXcds);
+}
+
 }  // namespace qmoe

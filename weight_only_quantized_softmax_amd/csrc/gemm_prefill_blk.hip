@@ -53,6 +53,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   constexpr int NBLK = BS < SSK ? SSK / BS : 1;   // scale blocks a step touches
   constexpr int SROWS = kBTM;                     // weight rows of the workgroup
   constexpr int SPT = (SROWS * NBLK + 255) / 256; // scales loaded per thread per step
+  // operands of the next k-slice read ahead, where the registers allow it (groups of one
+  // k-slice or one step)
+  constexpr bool PF = SINGLE || BS == SSK || (BITS == 8 && BS == 128);
   constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;  // -(c+z) bf16 pair
   static_assert(BITS == 4 || BS >= 64, "8-bit blocks shorter than 64 take the other kernel");
 
@@ -61,8 +64,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   __shared__ uint32_t xoffs[NDMA][256];
   __shared__ ST sring[2][SROWS * NBLK];  // scales of this step and the next
 
-  const int tile = blockIdx.y;
-  if (tile >= *g.num_tiles) return;
+  int tile, cblk;
+  if (!xcd_item(*g.num_tiles, (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
   const int e = g.tile_list[2 * tile];
   const int valid = g.tile_list[2 * tile + 1];
   const int64_t row0 = static_cast<int64_t>(tile) * kBTM;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
   const int wm = wave & 1, wn = wave >> 1;
-  const int col0 = blockIdx.x * BCOLS;
+  const int col0 = cblk * BCOLS;
   const int K = g.K;
   const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
   const int nss = K / SSK;  // the launcher checks that K is a whole number of steps
@@ -221,10 +224,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
       if (XPOSE) transpose_rows4(w[b]);
     }
     const ST* sc = sring[slot];
+    u32x4 xa[4], xn[4];
+    aread(stage, 0, xa);
 #pragma unroll
     for (int j = 0; j < MPS; ++j) {
-      u32x4 xa[4];
-      aread(stage, j, xa);
+      if (PF && j + 1 < MPS) aread(stage, j + 1, xn);  // next k-slice's operands, in flight
+      if (!PF && j > 0) aread(stage, j, xa);
       if (BITS == 4) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
@@ -282,6 +287,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
             for (int mt = 0; mt < 4; ++mt) pin(tot[mt][b]);
           }
         }
+      }
+      if (PF && j + 1 < MPS) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) xa[mt] = xn[mt];
       }
       // one k-slice at a time: operands and decodes hoisted from later slices would spill
       __builtin_amdgcn_sched_barrier(0);
@@ -366,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
 template <int BITS, typename ST, int MODE, int BS>
 static hipError_t launch_blk_bs(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = 2 * (kBNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
-  dim3 grid((g.ncols + bcols - 1) / bcols, static_cast<unsigned>(max_tiles)), block(256);
+  dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
   gemm_bf16_prefill_blk_kernel<BITS, ST, MODE, BS><<<grid, block, 0, s>>>(g);
   return hipGetLastError();
 }

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   __shared__ float rowsum[kRTM];
   __shared__ uint32_t xoffs[NDMA][256];  // this thread's activation load offsets
 
-  const int tile = blockIdx.y;
-  if (tile >= *g.num_tiles) return;
+  int tile, cblk;
+  if (!xcd_item(*g.num_tiles, (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
   const int e = g.tile_list[2 * tile];
   const int valid = g.tile_list[2 * tile + 1];
   const int64_t row0 = static_cast<int64_t>(tile) * kRTM;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
   const int wm = wave & 1, wn = wave >> 1;
-  const int col0 = blockIdx.x * BCOLS;
+  const int col0 = cblk * BCOLS;
   const int K = g.K;
   const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
   const int nss = (K + SSK - 1) / SSK;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
 template <int BITS, typename ST, int MODE>
 static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = 2 * (kRNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
-  dim3 grid((g.ncols + bcols - 1) / bcols, static_cast<unsigned>(max_tiles)), block(256);
+  dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
   gemm_bf16_prefill_rows_kernel<BITS, ST, MODE><<<grid, block, 0, s>>>(g);
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ struct GemmArgs {
 };
 
 // Dynamic LDS bytes of the bf16 GEMM (scales of a workgroup's rows, split-K partials).
-size_t gemm_bf16_lds(const GemmArgs& g, bool two_streams, bool scale_bf16, int sk);
+size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk);
 
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
                         int32_t* ids, float* w, hipStream_t s);
