@@ -397,16 +397,26 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
     return fail(QMOE_ERR_INVALID, "workspace %zu bytes < %zu", workspace_bytes, w.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t A = p->num_tokens * p->k;
-  QMOE_TRY(device_status(
-      qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
-                         static_cast<int>(p->num_experts), static_cast<int>(p->k),
-                         p->normalize_routing_weights, w.topk_ids, w.topk_w, s),
-      "route launch"));
-  QMOE_TRY(device_status(
-      qmoe::launch_permute(w.topk_ids, A, static_cast<int>(p->num_experts), tile_m_of(p), w.counts,
-                           w.offsets, w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles,
-                           w.perm_scratch, s),
-      "permute launch"));
+  if (qmoe::route_permute_fits(p->num_tokens, A)) {
+    QMOE_TRY(device_status(
+        qmoe::launch_route_permute(router_logits, p->act_dtype == QMOE_BF16,
+                                   static_cast<int>(p->num_tokens), static_cast<int>(p->num_experts),
+                                   static_cast<int>(p->k), p->normalize_routing_weights,
+                                   tile_m_of(p), w.topk_ids, w.topk_w, w.counts, w.offsets,
+                                   w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles, s),
+        "route+permute launch"));
+  } else {
+    QMOE_TRY(device_status(
+        qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                           static_cast<int>(p->num_experts), static_cast<int>(p->k),
+                           p->normalize_routing_weights, w.topk_ids, w.topk_w, s),
+        "route launch"));
+    QMOE_TRY(device_status(
+        qmoe::launch_permute(w.topk_ids, A, static_cast<int>(p->num_experts), tile_m_of(p), w.counts,
+                             w.offsets, w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles,
+                             w.perm_scratch, s),
+        "permute launch"));
+  }
   QMOE_TRY(run_fc1(p, input, w.sorted_assign, w.tiles, w.num_tiles, fc1, fc3, w.h, s));
   QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s));
   QMOE_TRY(device_status(

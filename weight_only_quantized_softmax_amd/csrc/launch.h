@@ -49,6 +49,16 @@ size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk);
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
                         int32_t* ids, float* w, hipStream_t s);
 
+// One launch for routing and grouping: batches of at most this many tokens (and at most
+// kPermFusedMax assignments).
+constexpr int64_t kRoutePermuteMaxT = 16;
+bool route_permute_fits(int64_t T, int64_t A);
+hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
+                                int M, int32_t* ids, float* w, int32_t* counts,
+                                int32_t* padded_offsets, int32_t* sorted_assign,
+                                int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles,
+                                hipStream_t s);
+
 size_t permute_scratch_bytes(int64_t A, int E);
 hipError_t launch_permute(const int32_t* ids, int64_t A, int E, int M, int32_t* counts,
                           int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
