@@ -49,37 +49,43 @@ __device__ __forceinline__ float dot2_sum(uint32_t v, float acc) {
 
 }  // namespace
 
-template <int BITS, typename ST, int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
+template <int BITS, int MODE>
+struct RowsShape {
+  static constexpr bool kTwo = (MODE == kModeSwiglu);
+  static constexpr int NS = kTwo ? 2 : 1;
+  static constexpr int NBS = kRNB / NS;                 // slices per stream
+  static constexpr int SSK = BITS == 4 ? 128 : 64;      // K per step
+  static constexpr int GPR = SSK / 8;                   // 16-byte granules per activation row
+  static constexpr int NDMA = kRTM * GPR / 64 / 4;      // LDS-destination loads per wave per step
+  static constexpr int BCOLS = 2 * NBS * 16;            // output columns per workgroup
+  static constexpr int STAGE = kRTM * SSK;              // bf16 elements per LDS stage
+};
+
+// One wave's share of a workgroup; WN (the wave's column half) is a template argument so
+// that every choice that depends on it is made at compile time.
+template <int BITS, typename ST, int MODE, int WN>
+__device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
+                                          uint16_t* xs0, uint16_t* xs1, float* rowsum) {
+  using S = RowsShape<BITS, MODE>;
   constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
-  constexpr bool kTwo = (MODE == kModeSwiglu);
-  constexpr int NS = kTwo ? 2 : 1;
-  constexpr int NBS = kRNB / NS;                 // slices per stream
-  constexpr int SSK = BITS == 4 ? 128 : 64;      // K per step
+  constexpr bool kTwo = S::kTwo;
+  constexpr int NS = S::NS;
+  constexpr int NBS = S::NBS;
+  constexpr int SSK = S::SSK;
   constexpr int MPS = SSK / 32;                  // MFMA k-slices per step
-  constexpr int GPR = SSK / 8;                   // 16-byte granules per activation row
-  constexpr int NDMA = kRTM * GPR / 64 / 4;      // LDS-destination loads per wave per step
-  constexpr int BCOLS = 2 * NBS * 16;            // output columns per workgroup
-  constexpr int STAGE = kRTM * SSK;              // bf16 elements per LDS stage
+  constexpr int GPR = S::GPR;
+  constexpr int NDMA = S::NDMA;
+  constexpr int BCOLS = S::BCOLS;
+  constexpr int wn = WN;
 
-  // two stages as two arrays, so that the compiler can tell the stage being read from the
-  // stage being filled and does not wait for the fill before reading
-  __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
-  __shared__ float rowsum[kRTM];
-  __shared__ uint32_t xoffs[NDMA][256];  // this thread's activation load offsets
-
-  int tile, cblk;
-  if (!xcd_item(*g.num_tiles, (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
   const int e = g.tile_list[2 * tile];
   const int valid = g.tile_list[2 * tile + 1];
   const int64_t row0 = static_cast<int64_t>(tile) * kRTM;
 
   const int tid = threadIdx.x;
-  // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1;
   const int col0 = cblk * BCOLS;
   const int K = g.K;
   const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
@@ -130,8 +136,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   // 64 i .. 64 i + 63 ----
   auto key = [](int r) { return GPR == 16 ? (r & 15) : ((r >> 1) & 7); };
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
-  // the offsets live in LDS (each thread reads back only what it wrote): registers are
-  // the scarce resource at two waves per SIMD
+  uint32_t xoffs[NDMA];  // this thread's activation load offsets, fixed over K
 #pragma unroll
   for (int t = 0; t < NDMA; ++t) {
     const int p = (wave + 4 * t) * 64 + lane;
@@ -141,14 +146,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
       const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
       off = static_cast<uint32_t>((src * K + 8 * q) * 2);
     }
-    xoffs[t][tid] = off;
+    xoffs[t] = off;
   }
   auto xload = [&](int s, uint16_t* stage) {
     // K is a whole number of steps (the launcher checks), so every granule is in its row
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
 #pragma unroll
     for (int t = 0; t < NDMA; ++t)
-      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t][tid], 2 * k0);
+      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t], 2 * k0);
     // the step-end wait counts the weight loads issued after these: none may move above
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -191,10 +196,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
       }
-      // row sums of slices 2 wn, 2 wn + 1 (wn is uniform across the wave)
+      // row sums of slices 2 wn, 2 wn + 1
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4 v = wn ? xa[2 + h] : xa[h];
+        const u32x4 v = xa[2 * wn + h];
         rs[h] = dot2_sum(v[3], dot2_sum(v[2], dot2_sum(v[1], dot2_sum(v[0], rs[h]))));
       }
       bf16x8 bw = decode(w[0], j);
@@ -297,6 +302,25 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
       }
     }
   }
+}
+
+template <int BITS, typename ST, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
+  using S = RowsShape<BITS, MODE>;
+  // two stages as two arrays, so that the compiler can tell the stage being read from the
+  // stage being filled and does not wait for the fill before reading
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[S::STAGE];
+  __shared__ float rowsum[kRTM];
+
+  int tile, cblk;
+  if (!xcd_item(*g.num_tiles, (g.ncols + S::BCOLS - 1) / S::BCOLS, tile, cblk)) return;
+  // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (wave >> 1)
+    rows_body<BITS, ST, MODE, 1>(g, tile, cblk, wave, xs0, xs1, rowsum);
+  else
+    rows_body<BITS, ST, MODE, 0>(g, tile, cblk, wave, xs0, xs1, rowsum);
 }
 
 template <int BITS, typename ST, int MODE>
