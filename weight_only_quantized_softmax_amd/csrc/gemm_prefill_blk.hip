@@ -55,13 +55,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   constexpr int SPT = (SROWS * NBLK + 255) / 256; // scales loaded per thread per step
   // operands of the next k-slice read ahead, where the registers allow it (groups of one
   // k-slice or one step)
-  constexpr bool PF = SINGLE || BS == SSK || (BITS == 8 && BS == 128);
+  constexpr bool PF = SINGLE || BS == SSK;
   constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;  // -(c+z) bf16 pair
   static_assert(BITS == 4 || BS >= 64, "8-bit blocks shorter than 64 take the other kernel");
 
   __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
-  __shared__ uint32_t xoffs[NDMA][256];
+  // activation load offsets (fixed over K): in registers where they fit, else in LDS, each
+  // thread reading back only what it wrote
+  constexpr bool XREG = SINGLE || BITS == 8;
+  __shared__ uint32_t xoffs_lds[XREG ? 1 : NDMA][256];
+  uint32_t xoffs_reg[NDMA];
+  auto xoff = [&](int t) -> uint32_t& { return XREG ? xoffs_reg[t] : xoffs_lds[t][threadIdx.x]; };
   __shared__ ST sring[2][SROWS * NBLK];  // scales of this step and the next
 
   int tile, cblk;
@@ -158,13 +163,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
       const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
       off = static_cast<uint32_t>((src * K + 8 * q) * 2);
     }
-    xoffs[t][tid] = off;
+    xoff(t) = off;
   }
   auto xload = [&](int s, uint16_t* stage) {
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
 #pragma unroll
     for (int t = 0; t < NDMA; ++t)
-      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t][tid], 2 * k0);
+      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoff(t), 2 * k0);
     // the step-end wait counts the loads issued after these: none may move above
     __builtin_amdgcn_sched_barrier(0);
   };
