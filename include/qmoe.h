@@ -53,6 +53,15 @@ typedef enum {
 
 typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1 } qmoe_dtype;
 
+/* Layout of the expert weight stacks (qmoe_params.weight_layout).
+   QMOE_LAYOUT_ROWS: the pages' layout, uint8 [E, N, K*bits/8], row-major.
+   QMOE_LAYOUT_TILES: the library's tiled layout, written by qmoe_pack_stack from a
+   ROWS stack (see there). Scales and biases keep their layout in both cases. */
+typedef enum { QMOE_LAYOUT_ROWS = 0, QMOE_LAYOUT_TILES = 1 } qmoe_layout;
+
+/* Which stack of a forward: fc1 (gate, or fused gate/up), fc2 (down), fc3 (separate up). */
+typedef enum { QMOE_FC1 = 1, QMOE_FC2 = 2, QMOE_FC3 = 3 } qmoe_which;
+
 /* activation_type of the graiphic "QMoE" page. gelu is not provided. */
 typedef enum {
   QMOE_ACT_SWIGLU = 0,
@@ -85,16 +94,56 @@ typedef struct {
      (qmoe_tile_m). Every call of one forward must use the same value. */
   int32_t tile_m;
   int32_t strict_blocks; /* non-zero: reject a K that block_size does not divide */
+  /* qmoe_layout of every weight stack handed to the GEMM and forward entry points.
+     QMOE_LAYOUT_TILES requires act_dtype QMOE_BF16. */
+  int32_t weight_layout;
 } qmoe_params;
 
 /* One quantized expert stack (graiphic QMoE fcN_experts_weights / fcN_scales / fcN_experts_bias).
-   weights: uint8 [E, N, K*bits/8]; scales: scale_dtype [E, N] (block_size 0) or
+   weights: uint8 [E, N, K*bits/8] (QMOE_LAYOUT_ROWS) or the tiled form from qmoe_pack_stack
+   (QMOE_LAYOUT_TILES); scales: scale_dtype [E, N] (block_size 0) or
    [E, N, ceil(K/block_size)]; bias: act_dtype [E, N] or NULL. */
 typedef struct {
   const void* weights;
   const void* scales;
   const void* bias;
 } qmoe_stack;
+
+/*
+ * Tiled weight layout (QMOE_LAYOUT_TILES). The weights of a stack are cut into tiles of
+ * 16 rows by S_K elements of K (S_K = 128 for 4-bit, 64 for 8-bit), 1024 bytes each; the
+ * GEMM kernels read one tile with one 16-byte load per lane of a 64-lane wavefront, from
+ * contiguous memory, in the order in which the matrix-core instructions consume it.
+ *   Streams: fc1 with swiglu and swiglu_fusion 1 or 2 has two streams of I rows (stream
+ *   0 the gate rows, stream 1 the up rows, wherever the fusion puts them in the ROWS
+ *   stack); every other stack has one stream of all its N rows.
+ *   Order: tile (e, s, b, t) -- expert e, stream s, rows [16b, 16b+16) of the stream,
+ *   K range [t*S_K, t*S_K + S_K) -- starts at byte 1024 * (((e*S + s)*NB + b)*KT + t),
+ *   NB = ceil(rows per stream / 16), KT = ceil(K / S_K).
+ *   Inside a tile, bytes [16l, 16l+16) belong to lane l = 16*q + n: row 16b + n of the
+ *   stream, and for each j < S_K/32 the eight elements k = t*S_K + 32j + 8q + i, i < 8:
+ *     4-bit: 32-bit word j (little-endian) holds element i in bits [4p, 4p+4) for
+ *            p = (0, 4, 1, 5, 2, 6, 3, 7)[i], i.e. its nibbles hold elements
+ *            (0, 2, 4, 6, 1, 3, 5, 7);
+ *     8-bit: byte 8j + i holds element i.
+ *   Elements past K and rows past the stream's end hold code 0 (their products meet
+ *   zero activations or are never stored).
+ */
+
+/* Bytes of the tiled form of stack `which` (qmoe_which) for these parameters; 0 when the
+   parameters are invalid or the stack does not exist for them (fc3 without separate up
+   rows). */
+size_t qmoe_packed_stack_size(const qmoe_params* p, int32_t which);
+
+/*
+ * Writes the tiled form of one ROWS-layout weight stack (graiphic "QMoE" page:
+ * fcN_experts_weights [E, N, K*bits/8]) into `packed` (qmoe_packed_stack_size bytes,
+ * caller-owned, 256-byte aligned, not overlapping `weights`). A one-time preparation of
+ * the weights, outside the forward; scales and biases are used as they are.
+ * p->weight_layout is ignored here.
+ */
+qmoe_status qmoe_pack_stack(const qmoe_params* p, int32_t which, const void* weights,
+                            void* packed, void* stream);
 
 /* Checks the parameters; QMOE_OK when every entry point accepts them. */
 qmoe_status qmoe_validate(const qmoe_params* p);

@@ -30,13 +30,13 @@ def host_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
     return as_f32(host(t), dtype).astype(np.float64)
 
 
-def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False):
+def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str = "rows"):
     return qm.make_params(T, cfg.H, cfg.I, cfg.E, cfg.k, expert_weight_bits=cfg.bits,
                           block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
                           activation=cfg.activation, normalize_routing_weights=cfg.normalize,
                           swiglu_alpha=cfg.alpha, swiglu_beta=cfg.beta, swiglu_limit=cfg.limit,
                           act_dtype=cfg.act_dtype, scale_dtype=cfg.scale_dtype, tile_m=tile_m,
-                          strict_blocks=strict)
+                          strict_blocks=strict, weight_layout=layout)
 
 
 class DeviceInputs:
@@ -53,6 +53,18 @@ class DeviceInputs:
         if inp.w3 is not None:
             self.fc3 = (dev(inp.w3), dev(inp.s3, s), dev(inp.b3, a) if inp.b3 is not None else None)
         self.shared = dev(inp.shared, a) if inp.shared is not None else None
+
+    def tiled(self, p):
+        """A copy whose weight stacks are in the tiled layout (qmoe_pack_stack), scales and
+        biases shared."""
+        t = object.__new__(DeviceInputs)
+        t.__dict__.update(self.__dict__)
+        for name in ("fc1", "fc2", "fc3"):
+            st = getattr(self, name)
+            if st is not None:
+                setattr(t, name, (qm.pack_stack(p, name, st[0]),) + tuple(st[1:]))
+        torch.cuda.synchronize()
+        return t
 
 
 def rms(a) -> float:

@@ -190,15 +190,18 @@ def test_every_gpu_parity_case_passes_validation(lib):
     from tests import test_gpu_parity as t
     from tests.gpu_helpers import params_for
 
-    cases = [(cfg, T, 0, "route " + n) for n, (cfg, T) in t.ROUTE_CASES.items()]
-    cases += [(t.STAGE_CFGS[n] if m == 0 else t.TILE128_CFGS[n], 40 if m == 0 else 300, m,
-               "stage " + n) for n, m in t.STAGE_CASES]
+    cases = [(cfg, T, 0, "rows", "route " + n) for n, (cfg, T) in t.ROUTE_CASES.items()]
+    cases += [(t.STAGE_CFGS[n] if m == 0 else t.TILE128_CFGS[n], 40 if m == 0 else 300, m, lay,
+               "stage " + n) for n, m, lay in t.STAGE_CASES]
     for c in (configs.C1, configs.C2, configs.C3, configs.C4):
-        cases += [(c, T, 0, "forward") for T in c.T_points]
+        cases += [(c, T, 0, "rows", "forward") for T in c.T_points]
+    for c in (configs.C2, configs.C3, configs.C4):
+        cases += [(c, T, 0, "tiles", "forward") for T in c.T_points]
     for b, bs in itertools.product(configs.C5_BITS, configs.C5_BLOCKS):
-        cases += [(configs.c5_point(b, bs), T, 0, "c5") for T in configs.C5.T_points]
+        cases += [(configs.c5_point(b, bs), T, 0, lay, "c5") for T in configs.C5.T_points
+                  for lay in ("rows", "tiles")]
     bad = []
-    for cfg, T, m, what in cases:
-        if lib.qmoe_validate(params_for(cfg, T, tile_m=m)) != 0:
-            bad.append((what, cfg.name, T, m, lib.qmoe_last_error()))
+    for cfg, T, m, lay, what in cases:
+        if lib.qmoe_validate(params_for(cfg, T, tile_m=m, layout=lay)) != 0:
+            bad.append((what, cfg.name, T, m, lay, lib.qmoe_last_error()))
     assert not bad

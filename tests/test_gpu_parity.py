@@ -201,26 +201,35 @@ TILE128_CFGS = {
                                             E=4, fc1_bias=True, fc2_bias=True),
 }
 
-STAGE_CASES = [(n, 0) for n in sorted(STAGE_CFGS)] + [(n, 128) for n in sorted(TILE128_CFGS)]
+# every case in the rows layout; the bf16 cases also in the tiled layout (qmoe_pack_stack)
+STAGE_CASES = ([(n, 0, "rows") for n in sorted(STAGE_CFGS)] +
+               [(n, 128, "rows") for n in sorted(TILE128_CFGS)] +
+               [(n, 0, "tiles") for n in sorted(STAGE_CFGS) if STAGE_CFGS[n].act_dtype == "bf16"] +
+               [(n, 128, "tiles") for n in sorted(TILE128_CFGS)])
 
 
-def _stage_inputs(name, tile_m):
+def _stage_inputs(name, tile_m, layout):
     cfg = STAGE_CFGS[name] if tile_m == 0 else TILE128_CFGS[name]
     assert cfg.H % 32 == 0 or cfg.act_dtype == "f32"
     T = 40 if tile_m == 0 else 300
     inp = gen.make_inputs(cfg, T)
-    p = params_for(cfg, T, tile_m=tile_m)
+    p = params_for(cfg, T, tile_m=tile_m, layout=layout)
     M = qm.qmoe_tile_m(p)
     assert tile_m == 0 or M == tile_m
     return cfg, T, inp, p, M
 
 
-@pytest.mark.parametrize("name,tile_m", STAGE_CASES)
-def test_fc1_stage(name, tile_m):
-    cfg, T, inp, p, M = _stage_inputs(name, tile_m)
-    say("fc1", name, cfg.H, cfg.I, cfg.E, "T", T, "M", M)
-    ids, perm, sa, erow = oracle_layout(cfg, T, M)
+def _device(inp, p):
     d = DeviceInputs(inp)
+    return d.tiled(p) if p.weight_layout == qm.QMOE_LAYOUT_TILES else d
+
+
+@pytest.mark.parametrize("name,tile_m,layout", STAGE_CASES)
+def test_fc1_stage(name, tile_m, layout):
+    cfg, T, inp, p, M = _stage_inputs(name, tile_m, layout)
+    say("fc1", name, layout, cfg.H, cfg.I, cfg.E, "T", T, "M", M)
+    ids, perm, sa, erow = oracle_layout(cfg, T, M)
+    d = _device(inp, p)
     rows = qm.qmoe_max_rows(p)
     sa_pad = np.full(rows, -1, np.int32)
     sa_pad[:len(sa)] = sa
@@ -247,16 +256,16 @@ def test_fc1_stage(name, tile_m):
     assert np.all(got[pads] == 0.0)
 
 
-@pytest.mark.parametrize("name,tile_m", STAGE_CASES)
-def test_fc2_stage(name, tile_m):
-    cfg, T, inp, p, M = _stage_inputs(name, tile_m)
-    say("fc2", name, "T", T, "M", M)
+@pytest.mark.parametrize("name,tile_m,layout", STAGE_CASES)
+def test_fc2_stage(name, tile_m, layout):
+    cfg, T, inp, p, M = _stage_inputs(name, tile_m, layout)
+    say("fc2", name, layout, "T", T, "M", M)
     ids, perm, sa, erow = oracle_layout(cfg, T, M, seed=1)
     rows = qm.qmoe_max_rows(p)
     hin = gen.gen_stage_h(cfg, rows, sigma=3.0)
     hin[sa.size:] = 0
     hin[:sa.size][sa < 0] = 0  # padding rows hold zeros, as fc1 writes them
-    d = DeviceInputs(inp)
+    d = _device(inp, p)
     tl = np.zeros((qm.qmoe_max_tiles(p), 2), np.int32)
     tl[:perm["num_tiles"]] = perm["tiles"]
     y = torch.full((rows, cfg.H), 7.0, dtype=torch.float32, device="cuda")
@@ -317,10 +326,10 @@ def test_combine_rounds_to_nearest_even():
 
 # --------------------------------------------------------------------------- end to end
 
-def forward_gpu(cfg, inp, d=None, reshape3d=False):
+def forward_gpu(cfg, inp, d=None, reshape3d=False, layout="rows"):
     T = inp.x.shape[0]
-    d = d or DeviceInputs(inp)
-    p = params_for(cfg, T)
+    p = params_for(cfg, T, layout=layout)
+    d = d or _device(inp, p)
     x = d.x.view(1, T, cfg.H) if reshape3d else d.x
     sh = d.shared.view(1, T, cfg.H) if (reshape3d and d.shared is not None) else d.shared
     out = qm.forward(p, x, d.logits, d.fc1, d.fc2, d.fc3, sh)
@@ -328,10 +337,10 @@ def forward_gpu(cfg, inp, d=None, reshape3d=False):
     return out.reshape(T, cfg.H), d
 
 
-def check_forward(cfg, T, sample=None, shared=False, seed=0):
-    say("forward", cfg.name, "T", T, "bits", cfg.bits, "bs", cfg.block_size)
+def check_forward(cfg, T, sample=None, shared=False, seed=0, layout="rows"):
+    say("forward", cfg.name, layout, "T", T, "bits", cfg.bits, "bs", cfg.block_size)
     inp = gen.make_inputs(cfg, T, seed=seed, shared=shared)
-    out, d = forward_gpu(cfg, inp)
+    out, d = forward_gpu(cfg, inp, layout=layout)
     got = host_f64(out, cfg.act_dtype)
     # routing and grouping of every token, bit for bit
     ids_g, _ = run_route(cfg, inp.logits, T)
@@ -379,6 +388,27 @@ def test_forward_c4_many_experts_sampled():
 @pytest.mark.parametrize("T", configs.C5.T_points)
 def test_forward_c5_sweep(T, bs, bits):
     check_forward(configs.c5_point(bits, bs), T, sample=6)
+
+
+# the tiled weight layout end to end: every workload
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_forward_tiled_c2_decode(T):
+    check_forward(configs.C2, T, shared=(T == 8), layout="tiles")
+
+
+def test_forward_tiled_c3_prefill_sampled():
+    check_forward(configs.C3, 4096, sample=12, layout="tiles")
+
+
+def test_forward_tiled_c4_many_experts_sampled():
+    check_forward(configs.C4, 512, sample=16, layout="tiles")
+
+
+@pytest.mark.parametrize("bits", configs.C5_BITS)
+@pytest.mark.parametrize("bs", configs.C5_BLOCKS)
+@pytest.mark.parametrize("T", [256, 4096])
+def test_forward_tiled_c5_sweep(T, bs, bits):
+    check_forward(configs.c5_point(bits, bs), T, sample=6, layout="tiles")
 
 
 def test_forward_deterministic_and_3d_input():

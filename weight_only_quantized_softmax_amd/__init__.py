@@ -13,15 +13,19 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (ACT, QMOE_BF16, QMOE_ERR_DTYPE, QMOE_ERR_SHAPE, QMOE_ERR_UNBOUND, QMOE_F32,
-                   QmoeError, QmoeParams, QmoeStack, check, load)
+from ._lib import (ACT, QMOE_BF16, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SHAPE,
+                   QMOE_ERR_UNBOUND, QMOE_F32, QMOE_FC1, QMOE_FC2, QMOE_FC3, QMOE_LAYOUT_ROWS,
+                   QMOE_LAYOUT_TILES, QmoeError, QmoeParams, QmoeStack, check, load)
 
 __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "forward", "QmoeError", "QmoeParams"]
+           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack", "forward",
+           "QmoeError", "QmoeParams"]
 
 _DT = {"f32": QMOE_F32, "bf16": QMOE_BF16}
+_LAYOUT = {"rows": QMOE_LAYOUT_ROWS, "tiles": QMOE_LAYOUT_TILES}
+_WHICH = {"fc1": QMOE_FC1, "fc2": QMOE_FC2, "fc3": QMOE_FC3}
 _TORCH_DT = {QMOE_F32: torch.float32, QMOE_BF16: torch.bfloat16}
 
 Stack = Optional[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]]
@@ -33,7 +37,7 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                 swiglu_alpha: float = 1.0, swiglu_beta: float = 0.0,
                 swiglu_limit: float = math.inf, act_dtype: str = "bf16",
                 scale_dtype: str = "bf16", tile_m: int = 0,
-                strict_blocks: bool = False) -> QmoeParams:
+                strict_blocks: bool = False, weight_layout: str = "rows") -> QmoeParams:
     return QmoeParams(num_tokens=num_tokens, hidden_size=hidden_size, inter_size=inter_size,
                       num_experts=num_experts, k=k, expert_weight_bits=expert_weight_bits,
                       block_size=block_size, swiglu_fusion=swiglu_fusion,
@@ -42,7 +46,8 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                       swiglu_alpha=swiglu_alpha, swiglu_beta=swiglu_beta,
                       swiglu_limit=swiglu_limit, act_dtype=_DT[act_dtype],
                       scale_dtype=_DT[scale_dtype], tile_m=tile_m,
-                      strict_blocks=int(bool(strict_blocks)))
+                      strict_blocks=int(bool(strict_blocks)),
+                      weight_layout=_LAYOUT[weight_layout])
 
 
 def _ptr(t: Optional[torch.Tensor], name: str):
@@ -147,6 +152,26 @@ def qmoe_forward(p, input, router_logits, fc1: Stack, fc2: Stack, fc3: Stack, sh
                               _stack(fc1, "fc1"), _stack(fc2, "fc2"), _stack(fc3, "fc3"),
                               _ptr(shared_output, "shared_output"), _ptr(output, "output"),
                               _ptr(workspace, "workspace"), nbytes, _stream(stream)))
+
+
+def qmoe_packed_stack_size(p: QmoeParams, which: str) -> int:
+    return int(load().qmoe_packed_stack_size(p, _WHICH[which]))
+
+
+def qmoe_pack_stack(p: QmoeParams, which: str, weights, packed, stream=None) -> None:
+    check(load().qmoe_pack_stack(p, _WHICH[which], _ptr(weights, "weights"),
+                                 _ptr(packed, "packed"), _stream(stream)))
+
+
+def pack_stack(p: QmoeParams, which: str, weights: torch.Tensor, stream=None) -> torch.Tensor:
+    """The tiled form of a rows-layout weight stack, in a new uint8 device tensor."""
+    n = qmoe_packed_stack_size(p, which)
+    if n == 0:
+        check(load().qmoe_validate(p))
+        raise QmoeError(QMOE_ERR_INVALID, f"stack {which} does not exist for these parameters")
+    packed = torch.empty(n, dtype=torch.uint8, device=weights.device)
+    qmoe_pack_stack(p, which, weights, packed, stream)
+    return packed
 
 
 def alloc_workspace(p: QmoeParams, device="cuda") -> torch.Tensor:

@@ -13,6 +13,8 @@ STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED",
                 6: "DEVICE"}
 
 QMOE_F32, QMOE_BF16 = 0, 1
+QMOE_LAYOUT_ROWS, QMOE_LAYOUT_TILES = 0, 1
+QMOE_FC1, QMOE_FC2, QMOE_FC3 = 1, 2, 3
 ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
 
 
@@ -25,7 +27,7 @@ class QmoeParams(ctypes.Structure):
                 ("swiglu_alpha", ctypes.c_float), ("swiglu_beta", ctypes.c_float),
                 ("swiglu_limit", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("scale_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("strict_blocks", ctypes.c_int32)]
+                ("strict_blocks", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class QmoeStack(ctypes.Structure):
@@ -36,7 +38,7 @@ class QmoeStack(ctypes.Structure):
 EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_last_error")
+           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_last_error")
 
 _lib = None
 
@@ -69,6 +71,9 @@ def load() -> ctypes.CDLL:
     L.qmoe_combine.argtypes, L.qmoe_combine.restype = [P, vp, vp, vp, vp, vp, vp], st
     L.qmoe_forward.argtypes = [P, vp, vp, QmoeStack, QmoeStack, QmoeStack, vp, vp, vp, sz, vp]
     L.qmoe_forward.restype = st
+    L.qmoe_packed_stack_size.argtypes = [P, ctypes.c_int32]
+    L.qmoe_packed_stack_size.restype = sz
+    L.qmoe_pack_stack.argtypes, L.qmoe_pack_stack.restype = [P, ctypes.c_int32, vp, vp, vp], st
     L.qmoe_last_error.argtypes, L.qmoe_last_error.restype = [], ctypes.c_char_p
     _lib = L
     return L

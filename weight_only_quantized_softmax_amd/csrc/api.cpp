@@ -89,6 +89,10 @@ qmoe_status validate(const qmoe_params* p) {
     return fail(QMOE_ERR_DTYPE, "act_dtype %d unknown", p->act_dtype);
   if (p->scale_dtype != QMOE_F32 && p->scale_dtype != QMOE_BF16)
     return fail(QMOE_ERR_DTYPE, "scale_dtype %d unknown", p->scale_dtype);
+  if (p->weight_layout != QMOE_LAYOUT_ROWS && p->weight_layout != QMOE_LAYOUT_TILES)
+    return fail(QMOE_ERR_INVALID, "weight_layout %d unknown", p->weight_layout);
+  if (p->weight_layout == QMOE_LAYOUT_TILES && p->act_dtype != QMOE_BF16)
+    return fail(QMOE_ERR_UNSUPPORTED, "the tiled weight layout serves bf16 activations only");
   const int pack = 8 / p->expert_weight_bits;
   if (p->hidden_size % pack || p->inter_size % pack)
     return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be multiples of %d", pack);
@@ -178,6 +182,40 @@ Workspace carve(const qmoe_params* p, char* base) {
   return w;
 }
 
+// Tiled layout of stack `which`; false when the stack does not exist for these parameters.
+bool pack_args(const qmoe_params* p, int32_t which, qmoe::PackArgs& a) {
+  a.E = static_cast<int>(p->num_experts);
+  a.bits = p->expert_weight_bits;
+  a.fusion = 0;
+  a.S = 1;
+  if (which == QMOE_FC1) {
+    a.K = static_cast<int>(p->hidden_size);
+    a.rows = static_cast<int>(p->inter_size);
+    a.N = static_cast<int>(n1_rows(p));
+    if (swiglu(p) && p->swiglu_fusion != 0) {
+      a.S = 2;
+      a.fusion = p->swiglu_fusion;
+    }
+  } else if (which == QMOE_FC3) {
+    if (!has_fc3(p)) return false;
+    a.K = static_cast<int>(p->hidden_size);
+    a.rows = a.N = static_cast<int>(p->inter_size);
+  } else if (which == QMOE_FC2) {
+    a.K = static_cast<int>(p->inter_size);
+    a.rows = a.N = static_cast<int>(p->hidden_size);
+  } else {
+    return false;
+  }
+  const int ssk = p->expert_weight_bits == 4 ? 128 : 64;
+  a.NB = (a.rows + 15) / 16;
+  a.KT = (a.K + ssk - 1) / ssk;
+  return true;
+}
+
+size_t packed_bytes(const qmoe::PackArgs& a) {
+  return static_cast<size_t>(a.E) * a.S * a.NB * a.KT * 1024;
+}
+
 qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   qmoe::GemmArgs g{};
   g.topk = static_cast<int>(p->k);
@@ -191,7 +229,15 @@ qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   g.limit = (p->swiglu_limit > 0.f) ? p->swiglu_limit : INFINITY;
   g.inter = static_cast<int>(p->inter_size);
   g.M = tile_m_of(p);
+  g.packed = p->weight_layout == QMOE_LAYOUT_TILES;
   return g;
+}
+
+// Tile counts of the tiled layout for a GEMM over K with `rows` rows per stream.
+void set_tiles(const qmoe_params* p, qmoe::GemmArgs& g, int rows) {
+  const int ssk = p->expert_weight_bits == 4 ? 128 : 64;
+  g.kt = (g.K + ssk - 1) / ssk;
+  g.nbk = (rows + 15) / 16;
 }
 
 // Kernel variant from the element types and the tile height (itself chosen from shapes).
@@ -225,6 +271,7 @@ qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_a
   g.N = static_cast<int>(n1_rows(p));
   g.ncols = static_cast<int>(p->inter_size);
   g.nb = p->block_size ? static_cast<int>((p->hidden_size + p->block_size - 1) / p->block_size) : 0;
+  set_tiles(p, g, static_cast<int>(p->inter_size));
   const int mode = swiglu(p) ? qmoe::kModeSwiglu : qmoe::kModePlainAct;
   return device_status(launch_gemm(p, g, mode, s), "fc1 launch");
 }
@@ -244,6 +291,7 @@ qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
   g.N = static_cast<int>(p->hidden_size);
   g.ncols = static_cast<int>(p->hidden_size);
   g.nb = p->block_size ? static_cast<int>((p->inter_size + p->block_size - 1) / p->block_size) : 0;
+  set_tiles(p, g, static_cast<int>(p->hidden_size));
   return device_status(launch_gemm(p, g, qmoe::kModeFc2, s), "fc2 launch");
 }
 
@@ -425,6 +473,35 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                            static_cast<int>(p->hidden_size), static_cast<int>(p->k), s),
       "combine launch"));
   return ok();
+}
+
+size_t qmoe_packed_stack_size(const qmoe_params* p, int32_t which) {
+  if (validate(p) != QMOE_OK) return 0;
+  qmoe::PackArgs a{};
+  if (!pack_args(p, which, a)) return 0;
+  return packed_bytes(a);
+}
+
+qmoe_status qmoe_pack_stack(const qmoe_params* p, int32_t which, const void* weights,
+                            void* packed, void* stream) {
+  QMOE_TRY(validate(p));
+  qmoe::PackArgs a{};
+  if (!pack_args(p, which, a))
+    return fail(QMOE_ERR_INVALID, "stack %d does not exist for these parameters", which);
+  QMOE_TRY(need(weights, "weights"));
+  QMOE_TRY(need(packed, "packed"));
+  if (reinterpret_cast<uintptr_t>(packed) % 256)
+    return fail(QMOE_ERR_INVALID, "packed must be 256-byte aligned");
+  const size_t nbytes = packed_bytes(a);
+  const size_t src_bytes = static_cast<size_t>(a.E) * a.N * a.K * a.bits / 8;
+  const char* w0 = static_cast<const char*>(weights);
+  const char* p0 = static_cast<const char*>(packed);
+  if (p0 < w0 + src_bytes && w0 < p0 + nbytes)
+    return fail(QMOE_ERR_INVALID, "packed overlaps weights");
+  return device_status(qmoe::launch_pack_stack(static_cast<const uint8_t*>(weights),
+                                               static_cast<uint8_t*>(packed), a,
+                                               static_cast<hipStream_t>(stream)),
+                       "pack launch");
 }
 
 const char* qmoe_last_error(void) { return g_error.c_str(); }

@@ -1,471 +1,13 @@
-// Grouped dequant GEMM for bf16 activations on gfx950 MFMA (16x16x32 bf16, fp32 accumulate),
-// 16-row tiles: the decode and mid-size shapes, bound by streaming the quantized weights.
-//
-// ClikaRT "QMoEWoQ" page, class description: the expert weights stay quantized and each
-// block is decoded inside the GEMM dot, never as a dense copy. graiphic "QMoE" page:
-// stack shapes [E, N, K/pack], scales per row or per K-block, activation attributes.
-//
-// Work unit of one wave: one 16-row tile of one expert x two 16-row weight slices (gate
-// and up of 16 output columns for fc1 with SwiGLU, otherwise two neighbouring groups of 16
-// output columns) over a range of K. A workgroup holds four
-// such waves; with split-K they share columns and divide K, and add their partial sums in
-// LDS at the end. Each lane owns one output column n and one quarter kq of every 32-wide
-// K step, and decodes its 8 weights of the step in registers:
-//   4-bit: each nibble q becomes the bfloat16 128+q by OR-ing it into the exponent
-//          pattern of 128 (exact), two nibbles per 32-bit register;
-//   8-bit: each byte becomes the exact bfloat16 q.
-// The MFMA therefore computes sum x*(c+q) with c = 128 (4-bit) or 0 (8-bit). The zero
-// point z and the offset c leave through a second MFMA of the same activations against
-// the constant -(c+z) (exact in bfloat16) into the same accumulator; a scale group's
-// accumulator starts from zero and is multiplied by its block's scale once, when the
-// group ends. Per-row scales multiply the finished sum.
-#include "common.h"
-#include "gemm_common.h"
-#include "launch.h"
+// 16-row grouped dequant GEMM (decode shapes), rows weight layout; the tiled layout's
+// instances live in gemm_bf16_tiled.hip, so that the two halves compile in parallel.
+#include "gemm_bf16_kernel.h"
 
 namespace qmoe {
 
-// Layout of one lane's 16-byte weight load and of the MFMA steps built from it.
-//   4-bit: a load holds 32 consecutive k of the lane's row; a "super-step" of 128 k is the
-//          four loads of lanes kq = 0..3 and feeds four MFMAs. Without the transpose, MFMA j
-//          takes word j of every lane (k slots spread over the 128); with it (scale blocks of
-//          16..64), MFMA j takes the 32 consecutive k [32j, 32j+32) of the super-step.
-//   8-bit: a load holds 16 consecutive k; a super-step is 64 k and feeds two MFMAs; MFMA j
-//          takes bytes [8j, 8j+8) of every lane (k slots spread over the 64).
-// G > 1 splits an MFMA whose k slots span G scale blocks into G MFMAs, each with the
-// weights (and the correction constant) of the other blocks' lanes zeroed.
-//
-// Workgroup: four waves on one 16-row tile, as CPB column groups (one wave's columns)
-// times SK K-splits (CPB * SK = 4). K advances in chunks of 256 k (two 4-bit or four 8-bit
-// super-steps); the split-K waves of a column group take the chunk's super-steps in turn.
-// Chunk ci's activations and weights are requested two chunks ahead: the activations go
-// straight into LDS (loads that target LDS, 1 KB of row segments per load, a ring of three
-// 8 KB stages whose 16-byte granules are XOR-swizzled by row so that the 16 rows one MFMA
-// operand reads fall in distinct banks), the weights into a three-slot register ring.
-// One barrier per chunk. All scales of the workgroup's rows are copied into LDS once, at
-// the start. The small stages leave room for three or four workgroups per CU, which the
-// weight stream needs to keep enough loads in flight.
-constexpr int kDecWaves = 4;  // waves per workgroup
-
-template <int BITS, typename ST, int MODE, int BS, int SK>
-__global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
-  constexpr int NW = kDecWaves;
-  constexpr bool PERROW = BS == 0;
-  constexpr bool XPOSE = BITS == 4 && BS > 0 && BS < 128;
-  constexpr int G = BITS == 4 ? (BS == 16 ? 2 : 1) : (BS == 16 ? 4 : (BS == 32 ? 2 : 1));
-  constexpr bool kTwo = (MODE == kModeSwiglu);
-  constexpr int NS = 2;                         // weight streams (16-row slices) per lane
-  constexpr int CW = kTwo ? 16 : 32;            // output columns per wave
-  constexpr int KC = 256;                       // K per chunk (128 or 256 bytes of every row)
-  constexpr int SSK = BITS == 4 ? 128 : 64;     // K per super-step
-  constexpr int SPC = KC / SSK;                 // super-steps per chunk (2 or 4)
-  static_assert(SK <= SPC, "a chunk holds at least one super-step per split");
-  constexpr int SPW = SPC / SK;                 // super-steps per chunk of one wave
-  constexpr int MPS = SSK / 32;                 // MFMAs per super-step
-  constexpr int CPB = NW / SK;                  // column groups per workgroup
-  constexpr int GPR = KC / 8;                   // 16-byte granules per chunk row (32)
-  constexpr int RPL = 64 / GPR;                 // tile rows per activation load (2)
-  constexpr int NDMA = kM / RPL / NW;           // activation loads per wave per chunk
-  static_assert(NDMA >= 1, "every wave takes part in the activation loads");
-  constexpr int STAGE = kM * KC;                // bf16 elements of one LDS stage
-  constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
-  // -(c+z) as a bf16 pair: 136 = 128 + 8 (4-bit), 128 = 0 + 128 (8-bit), both exact
-  constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;
-
-  // three activation stages as three arrays, so that the compiler can tell the stage
-  // being read from the stages being filled
-  __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // scales
-
-  const int tile = blockIdx.y;
-  if (tile >= *g.num_tiles) return;
-  const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
-  const int64_t row0 = static_cast<int64_t>(tile) * kM;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int n = lane % 16, kq = lane / 16;
-  const int ks = wave % SK, cgl = wave / SK;     // K split and column group of this wave
-  const int col0 = blockIdx.x * CPB * CW;
-  // output column of stream st of this lane (SwiGLU: both streams feed one column)
-  auto col_of = [&](int st) { return col0 + cgl * CW + (kTwo ? 0 : 16 * st) + n; };
-  const int K = g.K;
-  const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
-  const int nchunks = (K + KC - 1) / KC;
-
-  auto local_row = [&](int st, int c) -> int {
-    if (!kTwo) return c;
-    if (g.fusion == 1) return 2 * c + st;
-    if (g.fusion == 2) return st * g.inter + c;
-    return c;
-  };
-  auto stream_rows = [&](int st) { return (kTwo && g.fusion == 0) ? g.inter : g.N; };
-  auto stream_w = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.w3 : g.w; };
-  auto stream_s = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s; };
-  auto stream_b = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b; };
-
-  rsrc_t wres[NS];
-  uint32_t woff[NS];
-  int lrow[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const int nr = stream_rows(st);
-    wres[st] = make_rsrc(stream_w(st) + static_cast<int64_t>(e) * nr * row_bytes,
-                         static_cast<uint32_t>(nr) * row_bytes);
-    lrow[st] = local_row(st, min(col_of(st), g.ncols - 1));  // clamped: stored only if valid
-    woff[st] = static_cast<uint32_t>(lrow[st]) * row_bytes + 16 * kq;
-  }
-  // the weights of one wave for chunk ci: its SPW super-steps, in one burst
-  typedef u32x4 Slot[NS][SPW];
-  auto wload = [&](int ci, Slot& w) {
-#pragma unroll
-    for (int v = 0; v < SPW; ++v)
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-        w[st][v] = buf_load16(wres[st], woff[st] + static_cast<uint32_t>(ci * KC + SSK * (v * SK + ks)) * BITS / 8);
-  };
-
-  // ---- activations: load t of wave w fills stage slots [64 (w + 4t), 64 (w + 4t) + 64):
-  // tile row r = (w + 4t) * RPL + lane / GPR, slot lane % GPR of the row holding logical
-  // granule (slot ^ key(r)) of the row's chunk segment ----
-  auto key = [](int r) { return r & 15; };
-  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
-  uint32_t xoff[NDMA];
-  int xk[NDMA];  // first k of the lane's granule inside a chunk
-#pragma unroll
-  for (int t = 0; t < NDMA; ++t) {
-    const int r = (wave + NW * t) * RPL + lane / GPR;
-    const int q = (lane % GPR) ^ key(r);
-    xk[t] = 8 * q;
-    if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
-      xoff[t] = static_cast<uint32_t>((src * K + 8 * q) * 2);
-    } else {
-      xoff[t] = kOutOfRange;  // padding rows land as zeros
-    }
-  }
-  auto xload = [&](int ci, uint16_t* stage) {
-    const int k0 = __builtin_amdgcn_readfirstlane(ci * KC);
-#pragma unroll
-    for (int t = 0; t < NDMA; ++t) {
-      // granules past K land as zeros too
-      const uint32_t off = (k0 + xk[t] < K) ? xoff[t] : kOutOfRange;
-      buf_load16_lds(xres, stage + (wave + NW * t) * 64 * 8, off, 2 * k0);
-    }
-  };
-
-  // ---- prologue ----
-  // The scale rows of the workgroup's columns are one contiguous range per stream (one
-  // range in all for interleaved gate/up rows), 16-byte aligned because they start at a
-  // multiple of 16 rows. They are copied into LDS first, 16 bytes per lane with loads that
-  // target LDS.
-  const int nb = PERROW ? 1 : g.nb;
-  ST* scl = reinterpret_cast<ST*>(dyn);
-  // one range for interleaved gate/up rows and for two column groups
-  const bool one_range = !kTwo || g.fusion == 1;
-  if (!PERROW) {
-    const int rowb = nb * static_cast<int>(sizeof(ST));
-    const int nrange = one_range ? 1 : NS;
-    const int rows = (one_range ? 2 : 1) * CPB * 16;  // rows of one range
-#pragma unroll
-    for (int rg = 0; rg < NS; ++rg) {
-      if (rg >= nrange) break;
-      const int nr = stream_rows(rg);
-      const rsrc_t sres = make_rsrc(static_cast<const unsigned char*>(stream_s(rg)) +
-                                        static_cast<int64_t>(e) * nr * rowb,
-                                    static_cast<uint32_t>(nr) * rowb);
-      const int rstart = one_range ? (kTwo ? 2 * col0 : col0) : local_row(rg, col0);
-      const uint32_t gstart = static_cast<uint32_t>(rstart) * rowb;
-      const int granules = rows * rowb / 16;
-      unsigned char* ldst = dyn + rg * rows * rowb;
-      for (int it = wave; it * 64 < granules; it += NW) {
-        if (it * 64 + lane < granules)
-          buf_load16_lds(sres, ldst + it * 1024, gstart + 16u * (it * 64 + lane), 0);
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  Slot w0, w1, w2;
-  xload(0, xs0);
-  __builtin_amdgcn_sched_barrier(0);
-  wload(0, w0);
-  if (nchunks > 1) xload(1, xs1);
-  __builtin_amdgcn_sched_barrier(0);
-  wload(min(1, nchunks - 1), w1);
-  // the scales and chunk 0's activations were issued first and loads complete in order:
-  // only chunk 0's weights and chunk 1's loads may still be pending
-  {
-    constexpr int kW2 = 2 * NS * SPW, kW2X = kW2 + NDMA;
-    static_assert(kW2X < 64, "vmcnt holds 6 bits");
-    if (nchunks > 1)
-      __builtin_amdgcn_s_waitcnt((kW2X & 15) | ((kW2X >> 4) << 14) | (7 << 4) | (15 << 8));
-    else
-      __builtin_amdgcn_s_waitcnt((kW2 & 15) | ((kW2 >> 4) << 14) | (7 << 4) | (15 << 8));
-  }
-  __syncthreads();
-  const ST* my_scl[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st)
-    my_scl[st] = scl + (!kTwo ? cgl * 32 + 16 * st + n
-                        : one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
-
-  floatx4 acc[NS][G];
-  float tot[NS][4];
-  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg)
-#pragma unroll
-    for (int st = 0; st < NS; ++st) acc[st][gg] = zero4;
-#pragma unroll
-  for (int st = 0; st < NS; ++st)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tot[st][i] = 0.f;
-  const bf16x8 zero = {};
-  const bf16x8 negc = __builtin_bit_cast(bf16x8, u32x4{kNegCorr, kNegCorr, kNegCorr, kNegCorr});
-  const int lgrp2 = kq >> 1;
-
-  // Computes this wave's super-steps of chunk ci from weight slot w and LDS stage xs.
-  auto compute = [&](Slot& w, const uint16_t* xs, int ci) {
-    const int k0 = ci * KC;
-#pragma unroll
-    for (int v = 0; v < SPW; ++v) {
-      const int u = v * SK + ks;    // super-step inside the chunk
-      const int ksu = k0 + SSK * u; // its first k
-      if (ksu >= K) break;
-      u32x4 wv[NS];
-#pragma unroll
-      for (int st = 0; st < NS; ++st) wv[st] = w[st][v];
-      if (XPOSE) {
-#pragma unroll
-        for (int st = 0; st < NS; ++st) transpose_rows4(wv[st]);
-      }
-#pragma unroll
-      for (int j = 0; j < MPS; ++j) {
-        const int kj = ksu + 32 * j;
-        if (XPOSE && kj >= K) break;
-        int q;  // logical granule of this lane's 8 activations for MFMA j, inside the chunk
-        if (BITS == 4)
-          q = XPOSE ? (16 * u + 4 * j + kq) : (16 * u + 4 * kq + j);
-        else
-          q = 8 * u + 2 * kq + j;
-        u32x4 xr = *reinterpret_cast<const u32x4*>(xs + (n * GPR + (q ^ key(n))) * 8);
-        if (BITS == 4) xr = order_for_nibbles(xr);
-        const bf16x8 xa = __builtin_bit_cast(bf16x8, xr);
-        bf16x8 bw[NS];
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if (BITS == 4) {
-            bw[st] = decode4(wv[st][j]);
-          } else {
-            u32x2 w2 = {wv[st][2 * j], wv[st][2 * j + 1]};
-            bw[st] = decode8(w2);
-          }
-        }
-        // where this MFMA's scale groups start and end
-        int first = 0, last = 0, gl0 = 0;
-        if (!PERROW) {
-          if (XPOSE) {
-            gl0 = kj >> BSHIFT;
-            first = G > 1 || (kj & (BS - 1)) == 0;
-            last = G > 1 || ((kj + 32) & (BS - 1)) == 0 || kj + 32 >= K;
-          } else {
-            // the MFMA's k slots spread over the whole super-step; a block longer than a
-            // super-step is summed and scaled one super-step at a time
-            gl0 = ksu >> BSHIFT;
-            first = j == 0;
-            last = j == MPS - 1;
-          }
-        }
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-          const bool mine = (G == 1) || (G == 2 ? (lgrp2 == gg) : (kq == gg));
-          // each stream's accumulator takes the correction -(c+z) * sum x and the products;
-          // a group starts from zero
-#pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const floatx4 from = first ? zero4 : acc[st][gg];
-            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? negc : zero, from, 0, 0, 0);
-            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? bw[st] : zero,
-                                                                  acc[st][gg], 0, 0, 0);
-          }
-          if (last) {
-            // the group's block: the two blocks of 16 inside one 4-bit MFMA are gl0 and
-            // gl0 + 1, the blocks of an 8-bit super-step gl0 + gg; otherwise the MFMA or
-            // super-step lies inside block gl0
-            const int blk = min(gl0 + (G > 1 ? gg : 0), nb - 1);
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-              const float sv = scale_value<ST>(my_scl[st][blk]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) tot[st][i] += sv * acc[st][gg][i];
-            }
-          }
-        }
-      }
-    }
-  };
-
-  // s_waitcnt immediate: vmcnt = the loads issued after chunk ci + 1's activation loads
-  // (chunk ci + 1's weights, chunk ci + 2's activations and weights), expcnt and lgkmcnt
-  // left open
-  constexpr int kAfter = NDMA + 2 * NS * SPW;
-  static_assert(kAfter < 64, "vmcnt holds 6 bits");
-  constexpr int kWaitX = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
-  // chunk ci computes from stage / slot ci % 3 and requests chunk ci + 2 into the third
-  auto chunk = [&](Slot& cur, const uint16_t* xcur, Slot& ahead, uint16_t* xahead, int ci) {
-    if (ci + 2 < nchunks) xload(ci + 2, xahead);
-    __builtin_amdgcn_sched_barrier(0);
-    wload(min(ci + 2, nchunks - 1), ahead);
-    compute(cur, xcur, ci);
-    // chunk ci + 1's activations have landed once at most the later loads are pending.
-    // A bare barrier follows: every LDS read of chunk ci has returned (the MFMAs used
-    // it), and a workgroup fence would also wait for chunk ci + 2's loads.
-    if (ci + 2 < nchunks)
-      __builtin_amdgcn_s_waitcnt(kWaitX);
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // three chunks per trip so that ring slots and stages are fixed; a chunk past the end
-  // computes nothing and only re-reads the last chunk's weights
-  for (int ci = 0; ci < nchunks; ci += 3) {
-    chunk(w0, xs0, w2, xs2, ci);
-    chunk(w1, xs1, w0, xs0, ci + 1);
-    chunk(w2, xs2, w1, xs1, ci + 2);
-  }
-
-  if (PERROW) {
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const int nr = stream_rows(st);
-      const float sv = scale_value<ST>(
-          static_cast<const ST*>(stream_s(st))[static_cast<int64_t>(e) * nr + lrow[st]]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tot[st][i] = sv * acc[st][0][i];
-    }
-  }
-
-  // ---- split-K: partial sums meet in LDS (the first activation stage), in split order ----
-  if (SK > 1) {
-    static_assert((SK - 1) * CPB * NS * 4 * 64 * 4 <= STAGE * 2, "split-K partials fit one stage");
-    float* red = reinterpret_cast<float*>(xs0);  // [(SK-1) * CPB][NS * 4][64]
-    if (ks > 0) {
-      float* my = red + ((ks - 1) * CPB + cgl) * NS * 4 * 64;
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) my[(st * 4 + i) * 64 + lane] = tot[st][i];
-    }
-    __syncthreads();
-    if (ks > 0) return;
-#pragma unroll
-    for (int q = 1; q < SK; ++q) {
-      const float* other = red + ((q - 1) * CPB + cgl) * NS * 4 * 64;
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tot[st][i] += other[(st * 4 + i) * 64 + lane];
-    }
-  }
-
-  float bias[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const uint16_t* bp = static_cast<const uint16_t*>(stream_b(st));
-    bias[st] = bp ? bf16_to_f32(bp[static_cast<int64_t>(e) * stream_rows(st) + lrow[st]]) : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * kq + i;
-    const int64_t r = row0 + m;
-    if (MODE == kModeSwiglu) {
-      const int col = col_of(0);
-      if (col >= g.ncols) continue;
-      float h = 0.f;
-      if (m < valid) h = swiglu(tot[0][i] + bias[0], tot[1][i] + bias[1], g.alpha, g.beta, g.limit);
-      static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
-    } else {
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int col = col_of(st);
-        if (col >= g.ncols) continue;
-        if (MODE == kModeFc2) {
-          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[st][i] + bias[st];
-        } else {
-          const float h = m < valid ? plain_act(tot[st][i] + bias[st], g.act) : 0.f;
-          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
-        }
-      }
-    }
-  }
-}
-
-// Split-K ways from shapes only: enough wave work units to fill the chip a few times
-// over, at most the super-steps of a chunk. Blocks longer than a super-step keep one split
-// (their groups are summed one super-step at a time in the split's own order).
-static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits, int wave_cols) {
-  const int ssk = bits == 4 ? 128 : 64;
-  if (g.bs > ssk) return 1;
-  const int64_t units = max_tiles * ((g.ncols + wave_cols - 1) / wave_cols);
-  const int cap = 256 / ssk;
-  int sk = 1;
-  while (sk < cap && units * sk < 6144) sk *= 2;
-  return sk;
-}
-
-// Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
-size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk) {
-  if (g.bs == 0) return 0;
-  return static_cast<size_t>(2) * (kDecWaves / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
-}
-
-template <int BITS, typename ST, int MODE, int SK>
-static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  constexpr int CPB = kDecWaves / SK;
-  const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
-  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles)), block(kDecWaves * 64);
-  const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK);
-  switch (g.bs) {
-    case 0: gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK><<<grid, block, lds, s>>>(g); break;
-    case 16: gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK><<<grid, block, lds, s>>>(g); break;
-    case 32: gemm_bf16_tile_kernel<BITS, ST, MODE, 32, SK><<<grid, block, lds, s>>>(g); break;
-    case 64: gemm_bf16_tile_kernel<BITS, ST, MODE, 64, SK><<<grid, block, lds, s>>>(g); break;
-    case 128: gemm_bf16_tile_kernel<BITS, ST, MODE, 128, SK><<<grid, block, lds, s>>>(g); break;
-    case 256: gemm_bf16_tile_kernel<BITS, ST, MODE, 256, 1><<<grid, block, lds, s>>>(g); break;
-    default: gemm_bf16_tile_kernel<BITS, ST, MODE, 512, 1><<<grid, block, lds, s>>>(g); break;
-  }
-  return hipGetLastError();
-}
-
-template <int BITS, typename ST, int MODE>
-static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  switch (choose_split(g, max_tiles, BITS, MODE == kModeSwiglu ? 16 : 32)) {
-    case 1: return launch_sk<BITS, ST, MODE, 1>(g, max_tiles, s);
-    case 2: return launch_sk<BITS, ST, MODE, 2>(g, max_tiles, s);
-    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4>(g, max_tiles, s);
-  }
-}
-
-template <int BITS, typename ST>
-static hipError_t launch_mode(const GemmArgs& g, int mode, int64_t max_tiles, hipStream_t s) {
-  if (mode == kModeSwiglu) return launch_bmode<BITS, ST, kModeSwiglu>(g, max_tiles, s);
-  if (mode == kModePlainAct) return launch_bmode<BITS, ST, kModePlainAct>(g, max_tiles, s);
-  return launch_bmode<BITS, ST, kModeFc2>(g, max_tiles, s);
-}
-
 hipError_t launch_gemm_bf16(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                             int64_t max_tiles, hipStream_t s) {
-  if (max_tiles <= 0) return hipSuccess;
-  if (bits == 4)
-    return scale_bf16 ? launch_mode<4, uint16_t>(g, mode, max_tiles, s)
-                      : launch_mode<4, float>(g, mode, max_tiles, s);
-  return scale_bf16 ? launch_mode<8, uint16_t>(g, mode, max_tiles, s)
-                    : launch_mode<8, float>(g, mode, max_tiles, s);
+  if (g.packed) return launch_gemm_bf16_tiled(g, mode, bits, scale_bf16, max_tiles, s);
+  return launch_gemm_bf16_layout<false>(g, mode, bits, scale_bf16, max_tiles, s);
 }
 
 }  // namespace qmoe

@@ -383,10 +383,11 @@ static hipError_t launch_prefill_t(const GemmArgs& g, int mode, int64_t max_tile
 hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                     int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  // per-row scales over whole K steps take the kernel that loads activations into LDS directly
-  if (g.bs == 0 && g.K % (bits == 4 ? 128 : 64) == 0)
+  // per-row scales over whole K steps (any K in the tiled layout) take the kernel that
+  // loads activations into LDS directly
+  if (g.bs == 0 && (g.packed || g.K % (bits == 4 ? 128 : 64) == 0))
     return launch_gemm_bf16_prefill_rows(g, mode, bits, scale_bf16, max_tiles, s);
-  // block scales likewise, except 8-bit blocks shorter than a 64-wide K step
+  // block scales likewise, except 8-bit rows-layout blocks shorter than a 64-wide K step
   if (prefill_blk_supports(g, bits))
     return launch_gemm_bf16_prefill_blk(g, mode, bits, scale_bf16, max_tiles, s);
   if (bits == 4)

@@ -63,7 +63,7 @@ struct RowsShape {
 
 // One wave's share of a workgroup; WN (the wave's column half) is a template argument so
 // that every choice that depends on it is made at compile time.
-template <int BITS, typename ST, int MODE, int WN>
+template <int BITS, typename ST, int MODE, int WN, bool PK>
 __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
                                           uint16_t* xs0, uint16_t* xs1, float* rowsum) {
   using S = RowsShape<BITS, MODE>;
@@ -108,24 +108,37 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   // descriptor and read zeros, and columns past ncols are never stored. Lane (n, kq) reads
   // the 16 bytes at 16 kq of the step's row segment: k = 32 kq .. +32 (4-bit) or
   // 16 kq .. +16 (8-bit), dword j (4-bit) or dword pair j (8-bit) feeding k-slice j. ----
+  // Tiled layout (PK): the slice is one contiguous sequence of 1 KB tiles, one per step,
+  // lane l reading bytes 16 l of each; a block past the stream reads zeros.
   rsrc_t wres[kRNB];
   const int lstep = (kTwo && g.fusion == 1) ? 2 : 1;  // stack rows between neighbouring columns
 #pragma unroll
   for (int b = 0; b < kRNB; ++b) {
     const int st = b / NBS;
     const int nr = stream_rows(st);
-    const int r0 = local_row(st, col0 + wn * NBS * 16 + (b % NBS) * 16);  // row of lane n = 0
-    const int64_t left = static_cast<int64_t>(max(nr - r0, 0)) * row_bytes;
-    wres[b] = make_rsrc(stream_w(st) + (static_cast<int64_t>(e) * nr + r0) * row_bytes,
-                        static_cast<uint32_t>(left));
+    const int c0 = col0 + wn * NBS * 16 + (b % NBS) * 16;  // column of lane n = 0
+    if (PK) {
+      const int ns = (kTwo && g.fusion != 0) ? 2 : 1, si = (kTwo && g.fusion != 0) ? st : 0;
+      const int rb = c0 / 16;
+      const int64_t tile0 = ((static_cast<int64_t>(e) * ns + si) * g.nbk + rb) * g.kt;
+      wres[b] = make_rsrc(stream_w(st) + tile0 * 1024,
+                          rb < g.nbk ? static_cast<uint32_t>(g.kt) * 1024u : 0u);
+    } else {
+      const int r0 = local_row(st, c0);
+      const int64_t left = static_cast<int64_t>(max(nr - r0, 0)) * row_bytes;
+      wres[b] = make_rsrc(stream_w(st) + (static_cast<int64_t>(e) * nr + r0) * row_bytes,
+                          static_cast<uint32_t>(left));
+    }
   }
-  // the lane offset (range-checked) holds the row, the scalar offset the step along it
-  const uint32_t wlane = static_cast<uint32_t>(lstep * n) * row_bytes + 16u * kq;
+  // rows layout: the lane offset (range-checked) holds the row, the scalar offset the
+  // step along it; tiled: the lane offset holds both (tiles past K read zeros)
+  const uint32_t wlane = PK ? 16u * lane : static_cast<uint32_t>(lstep * n) * row_bytes + 16u * kq;
   auto wload = [&](int s, u32x4 (&w)[kRNB]) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s * SSK) * BITS / 8);
 #pragma unroll
     for (int b = 0; b < kRNB; ++b)
-      w[b] = buf_load16s(wres[b], wlane, so);
+      w[b] = PK ? buf_load16(wres[b], wlane + static_cast<uint32_t>(s) * 1024u)
+                : buf_load16s(wres[b], wlane, so);
   };
   // stack row of this lane's column of slice b, clamped into the stack (epilogue reads)
   auto slice_row = [&](int b) {
@@ -137,10 +150,14 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   auto key = [](int r) { return GPR == 16 ? (r & 15) : ((r >> 1) & 7); };
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
   uint32_t xoffs[NDMA];  // this thread's activation load offsets, fixed over K
+  auto granule = [&](int t) {  // logical granule of load t of this lane
+    const int p = (wave + 4 * t) * 64 + lane;
+    return (p % GPR) ^ key(p / GPR);
+  };
 #pragma unroll
   for (int t = 0; t < NDMA; ++t) {
     const int p = (wave + 4 * t) * 64 + lane;
-    const int r = p / GPR, q = (p % GPR) ^ key(r);
+    const int r = p / GPR, q = granule(t);
     uint32_t off = kOutOfRange;  // padding rows land as zeros
     if (r < valid) {
       const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
@@ -149,22 +166,31 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     xoffs[t] = off;
   }
   auto xload = [&](int s, uint16_t* stage) {
-    // K is a whole number of steps (the launcher checks), so every granule is in its row
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
+    if (PK && k0 + SSK > K) {
+      // the last step of a K that is not a whole number of steps (tiled layout only):
+      // granules past K land as zeros
 #pragma unroll
-    for (int t = 0; t < NDMA; ++t)
-      buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t], 2 * k0);
+      for (int t = 0; t < NDMA; ++t)
+        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8,
+                       k0 + 8 * granule(t) < K ? xoffs[t] : kOutOfRange, 2 * k0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t)
+        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t], 2 * k0);
+    }
     // the step-end wait counts the weight loads issued after these: none may move above
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // operand reads: row r = wm*64 + mt*16 + n has key(r) = key(n); granule q = 4 kq + j
-  // (4-bit) or 2 kq + j (8-bit), j in the lowest bit(s) of q, so the slot of k-slice j is
-  // that of k-slice 0 with j XOR-ed into its low bits; mt adds 16 rows.
-  const uint32_t abase =
-      static_cast<uint32_t>(((wm * 64 + n) * GPR + (((BITS == 4 ? 4 : 2) * kq) ^ key(n))) * 16);
+  // (4-bit rows layout) or 2 kq + j (8-bit rows layout), j in the lowest bit(s) of q, or
+  // q = 4 j + kq (tiled layout, k-slice j = k [32j, 32j + 32)), j above the bits of kq; in
+  // each case the slot of k-slice j is that of k-slice 0 with j XOR-ed in; mt adds 16 rows.
+  const int q0 = PK ? kq : (BITS == 4 ? 4 : 2) * kq;
+  const uint32_t abase = static_cast<uint32_t>(((wm * 64 + n) * GPR + (q0 ^ key(n))) * 16);
   auto aread = [&](const uint16_t* stage, int j, u32x4 (&xa)[4]) {
-    const uint32_t aj = abase ^ static_cast<uint32_t>(16 * j);
+    const uint32_t aj = abase ^ static_cast<uint32_t>((PK ? 64 : 16) * j);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       xa[mt] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(stage) + aj +
@@ -192,7 +218,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
 #pragma unroll
     for (int j = 0; j < MPS; ++j) {
       if (j + 1 < MPS) aread(stage, j + 1, xn);  // next k-slice's operands, in flight
-      if (BITS == 4) {
+      if (BITS == 4 && !PK) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
       }
@@ -304,7 +330,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   }
 }
 
-template <int BITS, typename ST, int MODE>
+template <int BITS, typename ST, int MODE, bool PK>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
   using S = RowsShape<BITS, MODE>;
   // two stages as two arrays, so that the compiler can tell the stage being read from the
@@ -318,16 +344,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (wave >> 1)
-    rows_body<BITS, ST, MODE, 1>(g, tile, cblk, wave, xs0, xs1, rowsum);
+    rows_body<BITS, ST, MODE, 1, PK>(g, tile, cblk, wave, xs0, xs1, rowsum);
   else
-    rows_body<BITS, ST, MODE, 0>(g, tile, cblk, wave, xs0, xs1, rowsum);
+    rows_body<BITS, ST, MODE, 0, PK>(g, tile, cblk, wave, xs0, xs1, rowsum);
 }
 
 template <int BITS, typename ST, int MODE>
 static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = 2 * (kRNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
-  gemm_bf16_prefill_rows_kernel<BITS, ST, MODE><<<grid, block, 0, s>>>(g);
+  if (g.packed)
+    gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true><<<grid, block, 0, s>>>(g);
+  else
+    gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, false><<<grid, block, 0, s>>>(g);
   return hipGetLastError();
 }
 

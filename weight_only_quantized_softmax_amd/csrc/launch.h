@@ -41,7 +41,18 @@ struct GemmArgs {
   float alpha, beta, limit;
   int M;                       // tile rows
   int64_t a_rows;              // rows of the tensor at a (T for fc1, padded rows for fc2)
+  // tiled weight layout (qmoe_pack_stack): 0 = rows [E, N, K*bits/8]
+  int packed;
+  int kt;                      // tiles along K (ceil(K / S_K))
+  int nbk;                     // 16-row blocks per stream
 };
+
+// Tiled layout of one stack: S streams of `rows` rows each, N rows per expert in the
+// rows-layout source.
+struct PackArgs {
+  int E, S, rows, N, K, bits, fusion, NB, KT;
+};
+hipError_t launch_pack_stack(const uint8_t* src, uint8_t* dst, const PackArgs& a, hipStream_t s);
 
 // Dynamic LDS bytes of the bf16 GEMM (scales of a workgroup's rows, split-K partials).
 size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk);
@@ -68,20 +79,27 @@ hipError_t launch_permute(const int32_t* ids, int64_t A, int E, int M, int32_t* 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                             int64_t max_tiles, hipStream_t s);
 
+hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                  int64_t max_tiles, hipStream_t s);
+
 // bf16 activations, MFMA 128-row tiles (prefill-sized expert groups).
 hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                     int64_t max_tiles, hipStream_t s);
 
 // bf16 activations, MFMA 128-row tiles, one scale per output row, K a multiple of 128
-// (4-bit) or 64 (8-bit): activations loaded straight into LDS.
+// (4-bit) or 64 (8-bit) in the rows layout, any K in the tiled layout: activations loaded
+// straight into LDS.
 hipError_t launch_gemm_bf16_prefill_rows(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                          int64_t max_tiles, hipStream_t s);
 
-// bf16 activations, MFMA 128-row tiles, one scale per output row and K-block, K a multiple
-// of 128 (4-bit) or 64 (8-bit); 8-bit blocks of at least 64.
+// bf16 activations, MFMA 128-row tiles, one scale per output row and K-block. Rows layout:
+// K a multiple of 128 (4-bit) or 64 (8-bit), 8-bit blocks of at least 64; tiled layout:
+// any block size and K.
 bool prefill_blk_supports(const GemmArgs& g, int bits);
 hipError_t launch_gemm_bf16_prefill_blk(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                         int64_t max_tiles, hipStream_t s);
+hipError_t launch_gemm_bf16_prefill_blk_tiled(const GemmArgs& g, int mode, int bits,
+                                              bool scale_bf16, int64_t max_tiles, hipStream_t s);
 
 // f32 activations, VALU kernel.
 hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
