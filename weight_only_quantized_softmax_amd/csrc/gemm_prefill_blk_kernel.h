@@ -183,6 +183,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
     const int p = (wave + 4 * t) * 64 + lane;
     return (p % GPR) ^ key(p / GPR);
   };
+  // the same for every load t: 4t * 64 / GPR rows later is a multiple of the key's period
+  const int gq = granule(0);
 #pragma unroll
   for (int t = 0; t < NDMA; ++t) {
     const int p = (wave + 4 * t) * 64 + lane;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
 #pragma unroll
       for (int t = 0; t < NDMA; ++t)
         buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8,
-                       k0 + 8 * granule(t) < K ? xoff(t) : kOutOfRange, 2 * k0);
+                       k0 + 8 * gq < K ? xoff(t) : kOutOfRange, 2 * k0);
     } else {
 #pragma unroll
       for (int t = 0; t < NDMA; ++t)

@@ -38,7 +38,7 @@ namespace qmoe {
 namespace {
 
 constexpr int kRTM = 128;  // rows per tile
-constexpr int kRNB = 6;    // 16-row weight slices per wave
+constexpr bool kRPF = true;  // read the next k-slice's operands ahead
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -49,23 +49,37 @@ __device__ __forceinline__ float dot2_sum(uint32_t v, float acc) {
 
 }  // namespace
 
+// Wave grid: WM waves along the tile's rows times 4 / WM along its columns; each wave holds
+// NB 16-row weight slices against its 128 / WM rows. More rows per wave share each decoded
+// weight among more MFMAs (the decode is the kernel's main VALU cost): fc1 with SwiGLU
+// takes 1 x 4 waves of 128 rows x 4 slices; the single-stream modes 2 x 2 waves of 64 rows
+// x 6 slices, where the registers also hold the activation load offsets.
 template <int BITS, int MODE>
 struct RowsShape {
   static constexpr bool kTwo = (MODE == kModeSwiglu);
+  static constexpr int WM = kTwo ? 1 : 2;
+  static constexpr int NB = kTwo ? 4 : 6;
+  static constexpr bool XREG = WM == 2;                 // activation offsets in registers
+  // explicit instruction order inside a k-slice (each MFMA followed by two VALU
+  // instructions, operand reads first): measured neutral to negative, left off
+  static constexpr bool SGB = false;
   static constexpr int NS = kTwo ? 2 : 1;
-  static constexpr int NBS = kRNB / NS;                 // slices per stream
+  static constexpr int NBS = NB / NS;                   // slices per stream
   static constexpr int SSK = BITS == 4 ? 128 : 64;      // K per step
   static constexpr int GPR = SSK / 8;                   // 16-byte granules per activation row
   static constexpr int NDMA = kRTM * GPR / 64 / 4;      // LDS-destination loads per wave per step
-  static constexpr int BCOLS = 2 * NBS * 16;            // output columns per workgroup
+  static constexpr int WNC = 4 / WM;                    // waves along the columns
+  static constexpr int MT = kRTM / 16 / WM;             // 16-row MFMA tiles per wave
+  static constexpr int BCOLS = WNC * NBS * 16;          // output columns per workgroup
   static constexpr int STAGE = kRTM * SSK;              // bf16 elements per LDS stage
 };
 
-// One wave's share of a workgroup; WN (the wave's column half) is a template argument so
-// that every choice that depends on it is made at compile time.
+// One wave's share of a workgroup; WN (the wave's column position) is a template argument
+// so that every choice that depends on it is made at compile time.
 template <int BITS, typename ST, int MODE, int WN, bool PK>
 __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
-                                          uint16_t* xs0, uint16_t* xs1, float* rowsum) {
+                                          uint16_t* xs0, uint16_t* xs1, float* rowsum,
+                                          uint32_t* xoffs_lds) {
   using S = RowsShape<BITS, MODE>;
   constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
   constexpr bool kTwo = S::kTwo;
@@ -76,7 +90,13 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   constexpr int GPR = S::GPR;
   constexpr int NDMA = S::NDMA;
   constexpr int BCOLS = S::BCOLS;
+  constexpr int MT = S::MT;
+  constexpr int kRWM = S::WM;
+  constexpr int kRNB = S::NB;
+  constexpr bool kRXREG = S::XREG;
+  constexpr int kRSGB = S::SGB ? 1 : 0;
   constexpr int wn = WN;
+  static_assert(MT == 2 * S::WNC, "each wave sums the rows of two MFMA tiles");
 
   const int e = g.tile_list[2 * tile];
   const int valid = g.tile_list[2 * tile + 1];
@@ -85,7 +105,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int n = lane % 16, kq = lane / 16;
-  const int wm = wave & 1;
+  const int wm = wave % kRWM;
   const int col0 = cblk * BCOLS;
   const int K = g.K;
   const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
@@ -149,11 +169,19 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   // 64 i .. 64 i + 63 ----
   auto key = [](int r) { return GPR == 16 ? (r & 15) : ((r >> 1) & 7); };
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
-  uint32_t xoffs[NDMA];  // this thread's activation load offsets, fixed over K
+  // this thread's activation load offsets, fixed over K: in registers where they fit,
+  // else in LDS (each thread reads back only what it wrote)
+  uint32_t xoffs_reg[kRXREG ? NDMA : 1];
+  auto xoff = [&](int t) -> uint32_t& {
+    if constexpr (kRXREG) return xoffs_reg[t];
+    else return xoffs_lds[t * 256 + threadIdx.x];
+  };
   auto granule = [&](int t) {  // logical granule of load t of this lane
     const int p = (wave + 4 * t) * 64 + lane;
     return (p % GPR) ^ key(p / GPR);
   };
+  // the same for every load t: 4t * 64 / GPR rows later is a multiple of the key's period
+  const int gq = granule(0);
 #pragma unroll
   for (int t = 0; t < NDMA; ++t) {
     const int p = (wave + 4 * t) * 64 + lane;
@@ -163,7 +191,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
       const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
       off = static_cast<uint32_t>((src * K + 8 * q) * 2);
     }
-    xoffs[t] = off;
+    xoff(t) = off;
   }
   auto xload = [&](int s, uint16_t* stage) {
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
@@ -173,11 +201,11 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
 #pragma unroll
       for (int t = 0; t < NDMA; ++t)
         buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8,
-                       k0 + 8 * granule(t) < K ? xoffs[t] : kOutOfRange, 2 * k0);
+                       k0 + 8 * gq < K ? xoff(t) : kOutOfRange, 2 * k0);
     } else {
 #pragma unroll
       for (int t = 0; t < NDMA; ++t)
-        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t], 2 * k0);
+        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoff(t), 2 * k0);
     }
     // the step-end wait counts the weight loads issued after these: none may move above
     __builtin_amdgcn_sched_barrier(0);
@@ -188,18 +216,18 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   // q = 4 j + kq (tiled layout, k-slice j = k [32j, 32j + 32)), j above the bits of kq; in
   // each case the slot of k-slice j is that of k-slice 0 with j XOR-ed in; mt adds 16 rows.
   const int q0 = PK ? kq : (BITS == 4 ? 4 : 2) * kq;
-  const uint32_t abase = static_cast<uint32_t>(((wm * 64 + n) * GPR + (q0 ^ key(n))) * 16);
-  auto aread = [&](const uint16_t* stage, int j, u32x4 (&xa)[4]) {
+  const uint32_t abase = static_cast<uint32_t>(((wm * MT * 16 + n) * GPR + (q0 ^ key(n))) * 16);
+  auto aread = [&](const uint16_t* stage, int j, u32x4 (&xa)[MT]) {
     const uint32_t aj = abase ^ static_cast<uint32_t>((PK ? 64 : 16) * j);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
       xa[mt] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(stage) + aj +
                                                mt * 16 * GPR * 16);
   };
 
-  floatx4 acc[4][kRNB];
+  floatx4 acc[MT][kRNB];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int b = 0; b < kRNB; ++b) acc[mt][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   float rs[2] = {0.f, 0.f};  // partial row sums of slices 2*wn, 2*wn+1 of this wave's rows
@@ -213,14 +241,19 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     }
   };
   auto compute = [&](const uint16_t* stage, const u32x4 (&w)[kRNB]) {
-    u32x4 xa[4], xn[4];
+    u32x4 xa[MT];
+    [[maybe_unused]] u32x4 xn[MT];
     aread(stage, 0, xa);
 #pragma unroll
     for (int j = 0; j < MPS; ++j) {
-      if (j + 1 < MPS) aread(stage, j + 1, xn);  // next k-slice's operands, in flight
+      if constexpr (kRPF) {
+        if (j + 1 < MPS) aread(stage, j + 1, xn);  // next k-slice's operands, in flight
+      } else {
+        if (j > 0) aread(stage, j, xa);
+      }
       if (BITS == 4 && !PK) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
+        for (int mt = 0; mt < MT; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
       }
       // row sums of slices 2 wn, 2 wn + 1
 #pragma unroll
@@ -232,17 +265,30 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
 #pragma unroll
       for (int b = 0; b < kRNB; ++b) {
         // the next slice's decode overlaps this slice's MFMAs
-        const bf16x8 bn = decode(w[b + 1 < kRNB ? b + 1 : b], j);
+        bf16x8 bn = bw;
+        if (b + 1 < kRNB) bn = decode(w[b + 1], j);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
           acc[mt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mt]),
                                                                bw, acc[mt][b], 0, 0, 0);
         bw = bn;
       }
-      if (j + 1 < MPS) {
+      if constexpr (kRPF) {
+        if (j + 1 < MPS) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) xa[mt] = xn[mt];
+          for (int mt = 0; mt < MT; ++mt) xa[mt] = xn[mt];
+        }
       }
+      if constexpr (kRSGB == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);  // LDS reads
+#pragma unroll
+        for (int i = 0; i < MT * kRNB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+      }
+      // one k-slice at a time: operands and decodes hoisted from later slices would spill
+      if (MT > 4 || kRSGB) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -285,7 +331,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     float v = rs[h];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
-    if (kq == 0) rowsum[wm * 64 + (2 * wn + h) * 16 + n] = -kCorr * v;
+    if (kq == 0) rowsum[wm * MT * 16 + (2 * wn + h) * 16 + n] = -kCorr * v;
   }
   __syncthreads();
 
@@ -300,10 +346,10 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     svr[b] = scale_value<ST>(static_cast<const ST*>(stream_s(st))[idx]);
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = wm * 64 + mt * 16 + 4 * kq + i;
+      const int m = wm * MT * 16 + mt * 16 + 4 * kq + i;
       const int64_t r = row0 + m;
       const float rc = rowsum[m];
 #pragma unroll
@@ -338,20 +384,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   __shared__ __attribute__((aligned(16))) uint16_t xs0[S::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[S::STAGE];
   __shared__ float rowsum[kRTM];
+  __shared__ uint32_t xoffs_lds[S::XREG ? 1 : S::NDMA * 256];
 
   int tile, cblk;
   if (!xcd_item(*g.num_tiles, (g.ncols + S::BCOLS - 1) / S::BCOLS, tile, cblk)) return;
   // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (wave >> 1)
-    rows_body<BITS, ST, MODE, 1, PK>(g, tile, cblk, wave, xs0, xs1, rowsum);
-  else
-    rows_body<BITS, ST, MODE, 0, PK>(g, tile, cblk, wave, xs0, xs1, rowsum);
+  switch (wave / S::WM) {
+    case 0: rows_body<BITS, ST, MODE, 0, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 1: rows_body<BITS, ST, MODE, 1, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 2: if constexpr (S::WNC > 2) rows_body<BITS, ST, MODE, 2, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    default: if constexpr (S::WNC > 3) rows_body<BITS, ST, MODE, 3, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+  }
 }
 
 template <int BITS, typename ST, int MODE>
 static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  const int bcols = 2 * (kRNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
+  const int bcols = RowsShape<BITS, MODE>::BCOLS;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
   if (g.packed)
     gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true><<<grid, block, 0, s>>>(g);
