@@ -3,9 +3,10 @@
 A step is one whole forward (route, permute, fc1+SwiGLU, fc2, combine) over one batch of
 synthetic tokens: one call of the library's qmoe_forward C entry point, which launches the
 kernels (routing and grouping as one kernel at small batches). The same stages are also
-run one C entry point at a time, with HIP events around the two GEMMs, for the kernel
-times and the roofline of the fc1 kernel (``staged_ms_per_step`` is that loop's step
-time). Inputs are resident in HBM before the timed region. Several device copies of the expert stacks are rotated
+run one C entry point at a time, the two GEMM kernels recording their own start and end
+on HIP events (qmoe_time_next_gemm), for the kernel times and the roofline of the fc1
+kernel (``staged_ms_per_step`` is that loop's step time). Inputs are resident in HBM
+before the timed region. Several device copies of the expert stacks are rotated
 from step to step so that the 256 MB Infinity Cache cannot serve a step's weights from
 the previous step.
 
@@ -111,6 +112,42 @@ def calibrate_copy(mb, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps(dict(calibrate_copy_bytes=n, launches=steps)), flush=True)
+
+
+class TimingEvents:
+    """HIP events for kernel timing, created with hipEventDisableSystemFence: recording one
+    then skips the system-scope cache writeback a default event performs, which would
+    otherwise be timed as part of the kernel (a few microseconds at decode sizes). Called
+    through the HIP runtime that torch has already loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        self.hip = ctypes.CDLL(path)
+        self.ct = ctypes
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                      ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+            self.ev.append(e.value)
+
+    def _ok(self, rc):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with error {rc}")
+
+    def ms(self, i, j):
+        out = self.ct.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(self.ev[i]),
+                                              self.ct.c_void_p(self.ev[j])))
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.ev = []
 
 
 def workload(args):
@@ -225,23 +262,22 @@ def main():
         if status != 0:
             qm.check(status)
 
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    # HIP events that the fc1 and fc2 kernels record their own start and end on
+    # (qmoe_time_next_gemm: hipExtLaunchKernel events)
+    tev = TimingEvents(4 * args.steps)
+    evp = [tev.ev[4 * i:4 * i + 4] for i in range(args.steps)]
 
     def step(i, timed):
         s1, s2, s3 = st_args[i % copies]
         run(lib.qmoe_route(*route))
         run(lib.qmoe_permute(*perm))
         if timed:
-            ev[i][0].record(stream)
+            run(lib.qmoe_time_next_gemm(evp[i][0], evp[i][1]))
         run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(d.x), ptr(sa), ptr(tl), ptr(nt), s1, s3,
                                              ptr(h), sid))
         if timed:
-            ev[i][1].record(stream)
-            ev[i][2].record(stream)
+            run(lib.qmoe_time_next_gemm(evp[i][2], evp[i][3]))
         run(lib.qmoe_grouped_gemm_fc2(p, ptr(h), ptr(tl), ptr(nt), s2, ptr(y), sid))
-        if timed:
-            ev[i][3].record(stream)
         run(lib.qmoe_combine(*comb))
 
     print(f"[bench] {copies} weight copies of {per_copy / 1e6:.1f} MB "
@@ -256,8 +292,9 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     staged_ms = (t1 - t0) * 1e3 / args.steps
-    fc1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    fc2_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    fc1_ms = float(np.mean([tev.ms(4 * i, 4 * i + 1) for i in range(args.steps)]))
+    fc2_ms = float(np.mean([tev.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
+    tev.close()
 
     # the timed step: the whole-forward entry point (one C call per step, the same kernels
     # with routing and grouping in one launch at small batches)

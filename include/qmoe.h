@@ -20,7 +20,8 @@
  *
  * Conventions shared by every entry point:
  *  - Every array argument is a DEVICE pointer owned by the caller, row-major and
- *    densely packed. The library allocates nothing and keeps no state between calls.
+ *    densely packed. The library allocates nothing and keeps no state between calls
+ *    (apart from the measurement hook of qmoe_time_next_gemm).
  *  - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued
  *    asynchronously on it; no call synchronises with the host.
  *  - Parameters are validated on the host before anything is enqueued; on a
@@ -249,6 +250,17 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                          qmoe_stack fc1, qmoe_stack fc2, qmoe_stack fc3,
                          const void* shared_output, void* output, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement hook, not a step of the method. The next grouped-GEMM kernel that the calling
+ * thread launches -- the one launch of qmoe_grouped_gemm_fc1_swiglu or
+ * qmoe_grouped_gemm_fc2, or the first of qmoe_forward's two -- records its own start and
+ * end on these HIP events (hipEvent_t, created by the caller, timing enabled; either may
+ * be NULL), as hipExtLaunchKernel does, so that hipEventElapsedTime(start, stop) is that
+ * kernel's duration alone, without the dispatch gap a separately recorded event holds.
+ * The hook is then cleared; (NULL, NULL) clears a pending hook. Thread-local; never fails.
+ */
+qmoe_status qmoe_time_next_gemm(void* start_event, void* stop_event);
 
 /* Message of the last failing call on this thread (library-owned, valid until the next
    call on this thread); "" after a successful call. */

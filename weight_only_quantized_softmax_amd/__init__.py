@@ -20,7 +20,8 @@ from ._lib import (ACT, QMOE_BF16, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SH
 __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack", "forward",
+           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
+           "qmoe_time_next_gemm", "forward",
            "QmoeError", "QmoeParams"]
 
 _DT = {"f32": QMOE_F32, "bf16": QMOE_BF16}
@@ -172,6 +173,13 @@ def pack_stack(p: QmoeParams, which: str, weights: torch.Tensor, stream=None) ->
     packed = torch.empty(n, dtype=torch.uint8, device=weights.device)
     qmoe_pack_stack(p, which, weights, packed, stream)
     return packed
+
+
+def qmoe_time_next_gemm(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:
+    """The calling thread's next grouped-GEMM launch records its own start and end on these
+    events (each already recorded once, so that it exists)."""
+    ev = lambda e: None if e is None else e.cuda_event  # noqa: E731
+    check(load().qmoe_time_next_gemm(ev(start), ev(stop)))
 
 
 def alloc_workspace(p: QmoeParams, device="cuda") -> torch.Tensor:

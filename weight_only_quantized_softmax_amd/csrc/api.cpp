@@ -15,6 +15,7 @@
 namespace {
 
 thread_local std::string g_error;
+thread_local qmoe::GemmTiming g_timing;
 
 qmoe_status fail(qmoe_status st, const char* fmt, ...) {
   char buf[512];
@@ -35,6 +36,22 @@ qmoe_status device_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(QMOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
+
+}  // namespace
+
+namespace qmoe {
+
+void set_gemm_timing(hipEvent_t start, hipEvent_t stop) { g_timing = GemmTiming{start, stop}; }
+
+GemmTiming take_gemm_timing() {
+  const GemmTiming t = g_timing;
+  g_timing = GemmTiming{};
+  return t;
+}
+
+}  // namespace qmoe
+
+namespace {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -502,6 +519,12 @@ qmoe_status qmoe_pack_stack(const qmoe_params* p, int32_t which, const void* wei
                                                static_cast<uint8_t*>(packed), a,
                                                static_cast<hipStream_t>(stream)),
                        "pack launch");
+}
+
+qmoe_status qmoe_time_next_gemm(void* start_event, void* stop_event) {
+  qmoe::set_gemm_timing(static_cast<hipEvent_t>(start_event),
+                        static_cast<hipEvent_t>(stop_event));
+  return ok();
 }
 
 const char* qmoe_last_error(void) { return g_error.c_str(); }

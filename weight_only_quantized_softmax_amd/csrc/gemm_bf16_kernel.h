@@ -47,14 +47,14 @@ namespace qmoe {
 // One barrier per chunk. All scales of the workgroup's rows are copied into LDS once, at
 // the start. The small stages leave room for three or four workgroups per CU, which the
 // weight stream needs to keep enough loads in flight.
-constexpr int kDecWaves = 4;  // waves per workgroup
+constexpr int kDecWaves = 4;  // waves per workgroup (eight for large tiled-layout grids)
 
 // PK: the weights come in the tiled layout (qmoe_pack_stack): each lane's 16 bytes of a
 // super-step are one contiguous 1 KB tile of its 16-row slice, already in MFMA order
 // (word j of lane (n, q) holds k = 32j + 8q .. +8 of row n, nibbles in decode order).
-template <int BITS, typename ST, int MODE, int BS, int SK, bool PK>
-__global__ __launch_bounds__(kDecWaves * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
-  constexpr int NW = kDecWaves;
+template <int BITS, typename ST, int MODE, int BS, int SK, bool PK, int NW_>
+__global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
+  constexpr int NW = NW_;
   constexpr bool PERROW = BS == 0;
   constexpr int SSK0 = BITS == 4 ? 128 : 64;
   // KORD: MFMA j of a super-step takes the 32 consecutive k [32j, 32j + 32) (tiled layout,
@@ -448,35 +448,56 @@ static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits, int wave
 }
 
 // Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
-inline size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk) {
+inline size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk, int nw = kDecWaves) {
   if (g.bs == 0) return 0;
-  return static_cast<size_t>(2) * (kDecWaves / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
+  return static_cast<size_t>(2) * (nw / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
 }
 
-template <int BITS, typename ST, int MODE, int SK, bool PK>
+template <int BITS, typename ST, int MODE, int SK, bool PK, int NW>
 static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  constexpr int CPB = kDecWaves / SK;
+  constexpr int CPB = NW / SK;
   const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
-  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles)), block(kDecWaves * 64);
-  const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK);
+  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles)), block(NW * 64);
+  const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK, NW);
   switch (g.bs) {
-    case 0: gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK, PK><<<grid, block, lds, s>>>(g); break;
-    case 16: gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK, PK><<<grid, block, lds, s>>>(g); break;
-    case 32: gemm_bf16_tile_kernel<BITS, ST, MODE, 32, SK, PK><<<grid, block, lds, s>>>(g); break;
-    case 64: gemm_bf16_tile_kernel<BITS, ST, MODE, 64, SK, PK><<<grid, block, lds, s>>>(g); break;
-    case 128: gemm_bf16_tile_kernel<BITS, ST, MODE, 128, SK, PK><<<grid, block, lds, s>>>(g); break;
-    case 256: gemm_bf16_tile_kernel<BITS, ST, MODE, 256, 1, PK><<<grid, block, lds, s>>>(g); break;
-    default: gemm_bf16_tile_kernel<BITS, ST, MODE, 512, 1, PK><<<grid, block, lds, s>>>(g); break;
+    case 0: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK, PK, NW>, grid, block, lds, s, g); break;
+    case 16: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK, PK, NW>, grid, block, lds, s, g); break;
+    case 32: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 32, SK, PK, NW>, grid, block, lds, s, g); break;
+    case 64: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 64, SK, PK, NW>, grid, block, lds, s, g); break;
+    case 128: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 128, SK, PK, NW>, grid, block, lds, s, g); break;
+    case 256: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 256, 1, PK, NW>, grid, block, lds, s, g); break;
+    default: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 512, 1, PK, NW>, grid, block, lds, s, g); break;
   }
   return hipGetLastError();
 }
 
+// Eight waves per workgroup (twice the columns over the same activation stages, so more
+// weight loads in flight per CU) for 4-bit tiled-layout grids that still give every CU at
+// least two such workgroups, with split-K of at most 2 and the scales of two workgroups
+// within the CU's LDS. (8-bit stacks run slower with eight waves.)
+template <int BITS, int MODE>
+static bool use_eight_waves(const GemmArgs& g, int64_t max_tiles, int sk, bool scale_bf16) {
+  constexpr int kCUs = 256;
+  if (BITS != 4 || !g.packed || sk > 2) return false;
+  const int wg_cols = (8 / sk) * (MODE == kModeSwiglu ? 16 : 32);
+  const int64_t wgs = max_tiles * ((g.ncols + wg_cols - 1) / wg_cols);
+  const size_t lds = gemm_bf16_lds(g, scale_bf16, sk, 8) + 3 * kM * 256 * 2;
+  return wgs >= 2 * kCUs && 2 * lds <= 160 * 1024;
+}
+
 template <int BITS, typename ST, int MODE, bool PK>
 static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  switch (choose_split(g, max_tiles, BITS, MODE == kModeSwiglu ? 16 : 32)) {
-    case 1: return launch_sk<BITS, ST, MODE, 1, PK>(g, max_tiles, s);
-    case 2: return launch_sk<BITS, ST, MODE, 2, PK>(g, max_tiles, s);
-    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4, PK>(g, max_tiles, s);
+  const int sk = choose_split(g, max_tiles, BITS, MODE == kModeSwiglu ? 16 : 32);
+  if constexpr (PK && BITS == 4) {
+    if (use_eight_waves<BITS, MODE>(g, max_tiles, sk, sizeof(ST) == 2)) {
+      if (sk == 1) return launch_sk<BITS, ST, MODE, 1, PK, 8>(g, max_tiles, s);
+      return launch_sk<BITS, ST, MODE, 2, PK, 8>(g, max_tiles, s);
+    }
+  }
+  switch (sk) {
+    case 1: return launch_sk<BITS, ST, MODE, 1, PK, kDecWaves>(g, max_tiles, s);
+    case 2: return launch_sk<BITS, ST, MODE, 2, PK, kDecWaves>(g, max_tiles, s);
+    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4, PK, kDecWaves>(g, max_tiles, s);
   }
 }
 

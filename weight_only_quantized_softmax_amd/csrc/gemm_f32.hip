@@ -128,11 +128,11 @@ static hipError_t launch_f32_t(const GemmArgs& g, int mode, int64_t max_tiles, h
   dim3 grid((g.ncols + waves - 1) / waves, static_cast<unsigned>(max_tiles)), block(64 * waves);
   const size_t lds = static_cast<size_t>(g.M) * g.K * sizeof(float);
   if (mode == kModeSwiglu)
-    gemm_f32_kernel<BITS, ST, kModeSwiglu><<<grid, block, lds, s>>>(g);
+    launch_gemm_kernel(gemm_f32_kernel<BITS, ST, kModeSwiglu>, grid, block, lds, s, g);
   else if (mode == kModePlainAct)
-    gemm_f32_kernel<BITS, ST, kModePlainAct><<<grid, block, lds, s>>>(g);
+    launch_gemm_kernel(gemm_f32_kernel<BITS, ST, kModePlainAct>, grid, block, lds, s, g);
   else
-    gemm_f32_kernel<BITS, ST, kModeFc2><<<grid, block, lds, s>>>(g);
+    launch_gemm_kernel(gemm_f32_kernel<BITS, ST, kModeFc2>, grid, block, lds, s, g);
   return hipGetLastError();
 }
 

@@ -362,13 +362,13 @@ static hipError_t launch_prefill_mode(const GemmArgs& g, int64_t max_tiles, hipS
   const int bcols = wn * (prefill_nb(BITS, g.bs) / (MODE == kModeSwiglu ? 2 : 1)) * 16;
   dim3 grid(static_cast<unsigned>(max_tiles), (g.ncols + bcols - 1) / bcols), block(256);
   switch (g.bs) {
-    case 0: gemm_bf16_prefill_kernel<BITS, ST, MODE, 0><<<grid, block, 0, s>>>(g); break;
-    case 16: gemm_bf16_prefill_kernel<BITS, ST, MODE, 16><<<grid, block, 0, s>>>(g); break;
-    case 32: gemm_bf16_prefill_kernel<BITS, ST, MODE, 32><<<grid, block, 0, s>>>(g); break;
-    case 64: gemm_bf16_prefill_kernel<BITS, ST, MODE, 64><<<grid, block, 0, s>>>(g); break;
-    case 128: gemm_bf16_prefill_kernel<BITS, ST, MODE, 128><<<grid, block, 0, s>>>(g); break;
-    case 256: gemm_bf16_prefill_kernel<BITS, ST, MODE, 256><<<grid, block, 0, s>>>(g); break;
-    default: gemm_bf16_prefill_kernel<BITS, ST, MODE, 512><<<grid, block, 0, s>>>(g); break;
+    case 0: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 0>, grid, block, 0, s, g); break;
+    case 16: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 16>, grid, block, 0, s, g); break;
+    case 32: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 32>, grid, block, 0, s, g); break;
+    case 64: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 64>, grid, block, 0, s, g); break;
+    case 128: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 128>, grid, block, 0, s, g); break;
+    case 256: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 256>, grid, block, 0, s, g); break;
+    default: launch_gemm_kernel(gemm_bf16_prefill_kernel<BITS, ST, MODE, 512>, grid, block, 0, s, g); break;
   }
   return hipGetLastError();
 }

@@ -422,7 +422,7 @@ template <int BITS, typename ST, int MODE, int BS, bool PK>
 static hipError_t launch_blk_bs(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = 2 * (kBNB / (MODE == kModeSwiglu ? 2 : 1)) * 16;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
-  gemm_bf16_prefill_blk_kernel<BITS, ST, MODE, BS, PK><<<grid, block, 0, s>>>(g);
+  launch_gemm_kernel(gemm_bf16_prefill_blk_kernel<BITS, ST, MODE, BS, PK>, grid, block, 0, s, g);
   return hipGetLastError();
 }
 

@@ -403,9 +403,9 @@ static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStre
   const int bcols = RowsShape<BITS, MODE>::BCOLS;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
   if (g.packed)
-    gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true><<<grid, block, 0, s>>>(g);
+    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true>, grid, block, 0, s, g);
   else
-    gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, false><<<grid, block, 0, s>>>(g);
+    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, false>, grid, block, 0, s, g);
   return hipGetLastError();
 }
 

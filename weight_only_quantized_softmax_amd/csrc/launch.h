@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,15 +48,32 @@ struct GemmArgs {
   int nbk;                     // 16-row blocks per stream
 };
 
+// Measurement hook: HIP events that the calling thread's next grouped-GEMM launch records
+// its own start and end on (hipExtLaunchKernel). take_gemm_timing returns them and clears
+// the hook.
+struct GemmTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+void set_gemm_timing(hipEvent_t start, hipEvent_t stop);
+GemmTiming take_gemm_timing();
+
+// Every grouped-GEMM kernel is launched through this: one GemmArgs by value.
+inline hipError_t launch_gemm_kernel(void (*kernel)(GemmArgs), dim3 grid, dim3 block,
+                                     size_t lds, hipStream_t s, GemmArgs g) {
+  void* args[] = {&g};
+  const GemmTiming t = take_gemm_timing();
+  if (t.start != nullptr || t.stop != nullptr)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s,
+                              t.start, t.stop, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s);
+}
+
 // Tiled layout of one stack: S streams of `rows` rows each, N rows per expert in the
 // rows-layout source.
 struct PackArgs {
   int E, S, rows, N, K, bits, fusion, NB, KT;
 };
 hipError_t launch_pack_stack(const uint8_t* src, uint8_t* dst, const PackArgs& a, hipStream_t s);
-
-// Dynamic LDS bytes of the bf16 GEMM (scales of a workgroup's rows, split-K partials).
-size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk);
 
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
                         int32_t* ids, float* w, hipStream_t s);
