@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens per oracle call")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
+    ap.add_argument("--tile-m", type=int, default=0,
+                    help="rows per expert tile (0 = the library's choice for the shapes)")
     ap.add_argument("--layout", default="tiles", choices=["tiles", "rows"],
                     help="weight layout handed to the GEMMs: tiled (packed once, before any "
                          "timing) or the pages' rows layout")
@@ -208,7 +210,7 @@ def main():
     inp = gen.make_inputs(cfg, T)
     d = DeviceInputs(inp)
     layout = args.layout if cfg.act_dtype == "bf16" else "rows"  # tiles serve bf16 activations
-    p = params_for(cfg, T, layout=layout)
+    p = params_for(cfg, T, tile_m=args.tile_m, layout=layout)
     qm.qmoe_validate(p)
 
     # stage buffers (the same kernels qmoe_forward launches, called one by one)
@@ -355,7 +357,8 @@ def main():
         data="synthetic",
         config=dict(workload=f"{cfg.name} T={T}", T=T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k,
                     bits=cfg.bits, block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
-                    weight_layout=layout, weight_copies=copies, touched_experts=alg["touched"]),
+                    weight_layout=layout, tile_m=qm.qmoe_tile_m(p), weight_copies=copies,
+                    touched_experts=alg["touched"]),
         roofline=roof,
         cpu_baseline=cpu,
         weight_stream_GBps=round(stream_gbps, 1),

@@ -92,7 +92,8 @@ typedef struct {
   int32_t act_dtype;    /* qmoe_dtype of x, router logits, biases, shared_output, output */
   int32_t scale_dtype;  /* qmoe_dtype of the scales */
   /* Rows per expert tile of the grouping. 0 = the library's choice for these shapes
-     (qmoe_tile_m). Every call of one forward must use the same value. */
+     (qmoe_tile_m). bf16 activations take 16, 32 or 128; fp32 activations 1 to 16 rows
+     that fit the kernel's LDS. Every call of one forward must use the same value. */
   int32_t tile_m;
   int32_t strict_blocks; /* non-zero: reject a K that block_size does not divide */
   /* qmoe_layout of every weight stack handed to the GEMM and forward entry points.

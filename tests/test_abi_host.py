@@ -109,6 +109,20 @@ def test_f32_tile_fits_lds(lib):
         _lib.QMOE_ERR_UNSUPPORTED
 
 
+def test_default_tile_heights(lib):
+    # 128 rows from 64 expected rows per expert, 32 from 12, else 16 (bf16 activations)
+    from synth import configs
+    from tests.gpu_helpers import params_for
+
+    c2, c3, c4 = configs.C2, configs.C3, configs.C4
+    c5 = configs.c5_point(4, 32)
+    for cfg, T, want in [(c2, 1, 16), (c2, 64, 16), (c3, 4096, 128), (c4, 512, 32),
+                         (c5, 1, 16), (c5, 256, 32), (c5, 4096, 128)]:
+        assert lib.qmoe_tile_m(params_for(cfg, T)) == want, (cfg.name, T)
+    assert status(good(tile_m=32)) == _lib.QMOE_OK
+    assert status(good(tile_m=64)) == _lib.QMOE_ERR_UNSUPPORTED
+
+
 def test_max_rows_and_tiles(lib):
     p = good(num_tokens=64)  # T*k = 256, M = 16, E = 32
     assert lib.qmoe_tile_m(p) == 16
@@ -191,8 +205,7 @@ def test_every_gpu_parity_case_passes_validation(lib):
     from tests.gpu_helpers import params_for
 
     cases = [(cfg, T, 0, "rows", "route " + n) for n, (cfg, T) in t.ROUTE_CASES.items()]
-    cases += [(t.STAGE_CFGS[n] if m == 0 else t.TILE128_CFGS[n], 40 if m == 0 else 300, m, lay,
-               "stage " + n) for n, m, lay in t.STAGE_CASES]
+    cases += [t.stage_cfg(n, m) + (m, lay, "stage " + n) for n, m, lay in t.STAGE_CASES]
     for c in (configs.C1, configs.C2, configs.C3, configs.C4):
         cases += [(c, T, 0, "rows", "forward") for T in c.T_points]
     for c in (configs.C2, configs.C3, configs.C4):

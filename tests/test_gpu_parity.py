@@ -201,17 +201,25 @@ TILE128_CFGS = {
                                             E=4, fc1_bias=True, fc2_bias=True),
 }
 
-# every case in the rows layout; the bf16 cases also in the tiled layout (qmoe_pack_stack)
+# every case in the rows layout at the library's tile height; the bf16 cases at both
+# weight-streaming tile heights (16 rows, and 32 rows of two MFMA row blocks) and in both
+# weight layouts (the tiled one from qmoe_pack_stack); the 128-row cases in both layouts
+_BF16_STAGE = [n for n in sorted(STAGE_CFGS) if STAGE_CFGS[n].act_dtype == "bf16"]
 STAGE_CASES = ([(n, 0, "rows") for n in sorted(STAGE_CFGS)] +
-               [(n, 128, "rows") for n in sorted(TILE128_CFGS)] +
-               [(n, 0, "tiles") for n in sorted(STAGE_CFGS) if STAGE_CFGS[n].act_dtype == "bf16"] +
-               [(n, 128, "tiles") for n in sorted(TILE128_CFGS)])
+               [(n, m, lay) for n in _BF16_STAGE for m in (16, 32) for lay in ("rows", "tiles")] +
+               [(n, 128, lay) for n in sorted(TILE128_CFGS) for lay in ("rows", "tiles")])
+
+
+def stage_cfg(name, tile_m):
+    """The config and token count of a stage case."""
+    if tile_m == 128:
+        return TILE128_CFGS[name], 300
+    return STAGE_CFGS[name], 40
 
 
 def _stage_inputs(name, tile_m, layout):
-    cfg = STAGE_CFGS[name] if tile_m == 0 else TILE128_CFGS[name]
+    cfg, T = stage_cfg(name, tile_m)
     assert cfg.H % 32 == 0 or cfg.act_dtype == "f32"
-    T = 40 if tile_m == 0 else 300
     inp = gen.make_inputs(cfg, T)
     p = params_for(cfg, T, tile_m=tile_m, layout=layout)
     M = qm.qmoe_tile_m(p)

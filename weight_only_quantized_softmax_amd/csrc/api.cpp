@@ -67,10 +67,14 @@ int64_t n1_rows(const qmoe_params* p) {
 }
 
 // Rows per expert tile, from shapes only: 128-row MFMA tiles when an expert is expected
-// to receive at least 64 rows (prefill), 16-row weight-streaming tiles otherwise.
+// to receive at least 64 rows (prefill); 32-row weight-streaming tiles from 12 expected rows
+// on, so that an expert's 17-32 rows read its weights once, not twice; 16-row tiles below.
 int32_t default_tile_m(const qmoe_params* p) {
-  if (p->act_dtype == QMOE_BF16)
-    return (p->num_tokens * p->k >= 64 * p->num_experts) ? 128 : 16;
+  if (p->act_dtype == QMOE_BF16) {
+    const int64_t a = p->num_tokens * p->k;
+    if (a >= 64 * p->num_experts) return 128;
+    return a >= 12 * p->num_experts ? 32 : 16;
+  }
   const int64_t kmax = std::max(p->hidden_size, p->inter_size);
   int32_t m = 16;
   while (m > 1 && m * kmax * 4 > kF32LdsBytes) m >>= 1;
@@ -123,8 +127,8 @@ qmoe_status validate(const qmoe_params* p) {
   if (p->act_dtype == QMOE_BF16) {
     if (p->hidden_size % 32 || p->inter_size % 32)
       return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs hidden_size and inter_size multiples of 32");
-    if (m != 16 && m != 128)
-      return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16 or 128 (got %d)", m);
+    if (m != 16 && m != 32 && m != 128)
+      return fail(QMOE_ERR_UNSUPPORTED, "bf16 path needs tile_m 16, 32 or 128 (got %d)", m);
     // 32-bit buffer offsets: activations, h and one expert's stack must stay below 2 GiB
     const int64_t kmax = std::max(p->hidden_size, p->inter_size);
     const int64_t rows_max = ((p->num_tokens * p->k) / m + std::min<int64_t>(p->num_experts, p->num_tokens * p->k)) * m;

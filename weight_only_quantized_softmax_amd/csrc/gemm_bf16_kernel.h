@@ -52,9 +52,10 @@ constexpr int kDecWaves = 4;  // waves per workgroup (eight for large tiled-layo
 // PK: the weights come in the tiled layout (qmoe_pack_stack): each lane's 16 bytes of a
 // super-step are one contiguous 1 KB tile of its 16-row slice, already in MFMA order
 // (word j of lane (n, q) holds k = 32j + 8q .. +8 of row n, nibbles in decode order).
-template <int BITS, typename ST, int MODE, int BS, int SK, bool PK, int NW_>
+template <int BITS, typename ST, int MODE, int BS, int SK, bool PK, int NW_, int MR>
 __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   constexpr int NW = NW_;
+  constexpr int TM = MR * kM;                   // rows of a tile: MR MFMA row blocks of 16
   constexpr bool PERROW = BS == 0;
   constexpr int SSK0 = BITS == 4 ? 128 : 64;
   // KORD: MFMA j of a super-step takes the 32 consecutive k [32j, 32j + 32) (tiled layout,
@@ -75,9 +76,9 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   constexpr int CPB = NW / SK;                  // column groups per workgroup
   constexpr int GPR = KC / 8;                   // 16-byte granules per chunk row (32)
   constexpr int RPL = 64 / GPR;                 // tile rows per activation load (2)
-  constexpr int NDMA = kM / RPL / NW;           // activation loads per wave per chunk
+  constexpr int NDMA = TM / RPL / NW;           // activation loads per wave per chunk
   static_assert(NDMA >= 1, "every wave takes part in the activation loads");
-  constexpr int STAGE = kM * KC;                // bf16 elements of one LDS stage
+  constexpr int STAGE = TM * KC;                // bf16 elements of one LDS stage
   constexpr int BSHIFT = BS == 16 ? 4 : BS == 32 ? 5 : BS == 64 ? 6 : BS == 128 ? 7 : BS == 256 ? 8 : 9;
   // -(c+z) as a bf16 pair: 136 = 128 + 8 (4-bit), 128 = 0 + 128 (8-bit), both exact
   constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;
@@ -89,11 +90,14 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // scales
 
-  const int tile = blockIdx.y;
+  // a grouping tile of g.M rows is covered by g.M / TM workgroup rows of TM rows each
+  const int nsub = g.M / TM;
+  const int tile = blockIdx.y / nsub, sub = blockIdx.y % nsub;
   if (tile >= *g.num_tiles) return;
   const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
-  const int64_t row0 = static_cast<int64_t>(tile) * kM;
+  const int valid = min(max(g.tile_list[2 * tile + 1] - sub * TM, 0), TM);
+  if (MODE == kModeFc2 && valid == 0) return;  // no output rows (fc1 writes zero rows)
+  const int64_t row0 = static_cast<int64_t>(tile) * g.M + sub * TM;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -239,19 +243,27 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
     my_scl[st] = scl + (!kTwo ? cgl * 32 + 16 * st + n
                         : one_range ? 2 * (cgl * 16 + n) + st : st * CPB * 16 + cgl * 16 + n) * nb;
 
-  floatx4 acc[NS][G];
-  float tot[NS][4];
+  floatx4 acc[MR][NS][G];
+  float tot[MR][NS][4];
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg)
+  for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-    for (int st = 0; st < NS; ++st) acc[st][gg] = zero4;
+    for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
+      for (int st = 0; st < NS; ++st) acc[mr][st][gg] = zero4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tot[st][i] = 0.f;
+  for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[mr][st][i] = 0.f;
   const bf16x8 zero = {};
-  const bf16x8 negc = __builtin_bit_cast(bf16x8, u32x4{kNegCorr, kNegCorr, kNegCorr, kNegCorr});
+  // the correction operand stays in its registers for the whole loop (opaque to the
+  // compiler, which would otherwise rebuild it before every use)
+  u32x4 negc_bits = {kNegCorr, kNegCorr, kNegCorr, kNegCorr};
+  asm volatile("" : "+v"(negc_bits));
+  const bf16x8 negc = __builtin_bit_cast(bf16x8, negc_bits);
   const int lgrp2 = kq >> 1;
 
   // Computes this wave's super-steps of chunk ci from weight slot w and LDS stage xs.
@@ -278,9 +290,13 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
           q = KORD ? (16 * u + 4 * j + kq) : (16 * u + 4 * kq + j);
         else
           q = KORD ? (8 * u + 4 * j + kq) : (8 * u + 2 * kq + j);
-        u32x4 xr = *reinterpret_cast<const u32x4*>(xs + (n * GPR + (q ^ key(n))) * 8);
-        if (BITS == 4 && !PK) xr = order_for_nibbles(xr);
-        const bf16x8 xa = __builtin_bit_cast(bf16x8, xr);
+        bf16x8 xa[MR];
+#pragma unroll
+        for (int mr = 0; mr < MR; ++mr) {
+          u32x4 xr = *reinterpret_cast<const u32x4*>(xs + ((16 * mr + n) * GPR + (q ^ key(n))) * 8);
+          if (BITS == 4 && !PK) xr = order_for_nibbles(xr);
+          xa[mr] = __builtin_bit_cast(bf16x8, xr);
+        }
         bf16x8 bw[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -314,22 +330,32 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
           // each stream's accumulator takes the correction -(c+z) * sum x and the products;
           // a group starts from zero
 #pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const floatx4 from = first ? zero4 : acc[st][gg];
-            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? negc : zero, from, 0, 0, 0);
-            acc[st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, mine ? bw[st] : zero,
-                                                                  acc[st][gg], 0, 0, 0);
-          }
+          for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+              const floatx4 from = first ? zero4 : acc[mr][st][gg];
+              acc[mr][st][gg] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mr], mine ? negc : zero, from, 0, 0, 0);
+              acc[mr][st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  xa[mr], mine ? bw[st] : zero, acc[mr][st][gg], 0, 0, 0);
+            }
           if (last) {
             // the group's block: the two blocks of 16 inside one 4-bit MFMA are gl0 and
             // gl0 + 1, the blocks of an 8-bit super-step gl0 + gg; otherwise the MFMA or
             // super-step lies inside block gl0
-            const int blk = min(gl0 + (G > 1 ? gg : 0), nb - 1);
+            // (the k-slice lies below K, so a single-block group's index is below nb; in
+            // k-slice order it is written as the chunk's first block plus a constant, so
+            // the scale reads take immediate LDS offsets)
+            int blk = XPOSE ? (k0 >> BSHIFT) + u * (SSK >> BSHIFT) + ((32 * j) >> BSHIFT) + gg
+                            : gl0 + (G > 1 ? gg : 0);
+            if (G > 1) blk = min(blk, nb - 1);
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
               const float sv = scale_value<ST>(my_scl[st][blk]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) tot[st][i] += sv * acc[st][gg][i];
+              for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[mr][st][i] += sv * acc[mr][st][gg][i];
             }
           }
         }
@@ -375,30 +401,37 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
       const float sv = scale_value<ST>(
           static_cast<const ST*>(stream_s(st))[static_cast<int64_t>(e) * nr + lrow[st]]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tot[st][i] = sv * acc[st][0][i];
+      for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[mr][st][i] = sv * acc[mr][st][0][i];
     }
   }
 
   // ---- split-K: partial sums meet in LDS (the first activation stage), in split order ----
   if (SK > 1) {
-    static_assert((SK - 1) * CPB * NS * 4 * 64 * 4 <= STAGE * 2, "split-K partials fit one stage");
-    float* red = reinterpret_cast<float*>(xs0);  // [(SK-1) * CPB][NS * 4][64]
+    constexpr int kPart = MR * NS * 4;  // partial sums per lane
+    static_assert((SK - 1) * CPB * kPart * 64 * 4 <= STAGE * 2, "split-K partials fit one stage");
+    float* red = reinterpret_cast<float*>(xs0);  // [(SK-1) * CPB][kPart][64]
     if (ks > 0) {
-      float* my = red + ((ks - 1) * CPB + cgl) * NS * 4 * 64;
+      float* my = red + ((ks - 1) * CPB + cgl) * kPart * 64;
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) my[(st * 4 + i) * 64 + lane] = tot[st][i];
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) my[((mr * NS + st) * 4 + i) * 64 + lane] = tot[mr][st][i];
     }
     __syncthreads();
     if (ks > 0) return;
 #pragma unroll
     for (int q = 1; q < SK; ++q) {
-      const float* other = red + ((q - 1) * CPB + cgl) * NS * 4 * 64;
+      const float* other = red + ((q - 1) * CPB + cgl) * kPart * 64;
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tot[st][i] += other[(st * 4 + i) * 64 + lane];
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[mr][st][i] += other[((mr * NS + st) * 4 + i) * 64 + lane];
     }
   }
 
@@ -409,14 +442,17 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
     bias[st] = bp ? bf16_to_f32(bp[static_cast<int64_t>(e) * stream_rows(st) + lrow[st]]) : 0.f;
   }
 #pragma unroll
+  for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = 4 * kq + i;
+    const int m = 16 * mr + 4 * kq + i;
     const int64_t r = row0 + m;
     if (MODE == kModeSwiglu) {
       const int col = col_of(0);
       if (col >= g.ncols) continue;
       float h = 0.f;
-      if (m < valid) h = swiglu(tot[0][i] + bias[0], tot[1][i] + bias[1], g.alpha, g.beta, g.limit);
+      if (m < valid)
+        h = swiglu(tot[mr][0][i] + bias[0], tot[mr][1][i] + bias[1], g.alpha, g.beta, g.limit);
       static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
     } else {
 #pragma unroll
@@ -424,9 +460,9 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
         const int col = col_of(st);
         if (col >= g.ncols) continue;
         if (MODE == kModeFc2) {
-          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[st][i] + bias[st];
+          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[mr][st][i] + bias[st];
         } else {
-          const float h = m < valid ? plain_act(tot[st][i] + bias[st], g.act) : 0.f;
+          const float h = m < valid ? plain_act(tot[mr][st][i] + bias[st], g.act) : 0.f;
           static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
         }
       }
@@ -437,10 +473,10 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
 // Split-K ways from shapes only: enough wave work units to fill the chip a few times
 // over, at most the super-steps of a chunk. Blocks longer than a super-step keep one split
 // (their groups are summed one super-step at a time in the split's own order).
-static int choose_split(const GemmArgs& g, int64_t max_tiles, int bits, int wave_cols) {
+static int choose_split(const GemmArgs& g, int64_t wg_rows, int bits, int wave_cols) {
   const int ssk = bits == 4 ? 128 : 64;
   if (g.bs > ssk) return 1;
-  const int64_t units = max_tiles * ((g.ncols + wave_cols - 1) / wave_cols);
+  const int64_t units = wg_rows * ((g.ncols + wave_cols - 1) / wave_cols);
   const int cap = 256 / ssk;
   int sk = 1;
   while (sk < cap && units * sk < 6144) sk *= 2;
@@ -453,21 +489,25 @@ inline size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk, int nw =
   return static_cast<size_t>(2) * (nw / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
 }
 
-template <int BITS, typename ST, int MODE, int SK, bool PK, int NW>
+template <int BITS, typename ST, int MODE, int SK, bool PK, int NW, int MR>
 static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   constexpr int CPB = NW / SK;
   const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
-  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles)), block(NW * 64);
+  dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles * (g.M / (MR * kM)))),
+      block(NW * 64);
   const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK, NW);
+#define QMOE_DEC(BSV, SKV) \
+  launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, BSV, SKV, PK, NW, MR>, grid, block, lds, s, g)
   switch (g.bs) {
-    case 0: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 0, SK, PK, NW>, grid, block, lds, s, g); break;
-    case 16: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 16, SK, PK, NW>, grid, block, lds, s, g); break;
-    case 32: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 32, SK, PK, NW>, grid, block, lds, s, g); break;
-    case 64: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 64, SK, PK, NW>, grid, block, lds, s, g); break;
-    case 128: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 128, SK, PK, NW>, grid, block, lds, s, g); break;
-    case 256: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 256, 1, PK, NW>, grid, block, lds, s, g); break;
-    default: launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, 512, 1, PK, NW>, grid, block, lds, s, g); break;
+    case 0: QMOE_DEC(0, SK); break;
+    case 16: QMOE_DEC(16, SK); break;
+    case 32: QMOE_DEC(32, SK); break;
+    case 64: QMOE_DEC(64, SK); break;
+    case 128: QMOE_DEC(128, SK); break;
+    case 256: QMOE_DEC(256, 1); break;
+    default: QMOE_DEC(512, 1); break;
   }
+#undef QMOE_DEC
   return hipGetLastError();
 }
 
@@ -475,30 +515,42 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 // weight loads in flight per CU) for 4-bit tiled-layout grids that still give every CU at
 // least two such workgroups, with split-K of at most 2 and the scales of two workgroups
 // within the CU's LDS. (8-bit stacks run slower with eight waves.)
-template <int BITS, int MODE>
-static bool use_eight_waves(const GemmArgs& g, int64_t max_tiles, int sk, bool scale_bf16) {
+template <int BITS, int MODE, int MR>
+static bool use_eight_waves(const GemmArgs& g, int64_t wg_rows, int sk, bool scale_bf16) {
   constexpr int kCUs = 256;
   if (BITS != 4 || !g.packed || sk > 2) return false;
   const int wg_cols = (8 / sk) * (MODE == kModeSwiglu ? 16 : 32);
-  const int64_t wgs = max_tiles * ((g.ncols + wg_cols - 1) / wg_cols);
-  const size_t lds = gemm_bf16_lds(g, scale_bf16, sk, 8) + 3 * kM * 256 * 2;
+  const int64_t wgs = wg_rows * ((g.ncols + wg_cols - 1) / wg_cols);
+  const size_t lds = gemm_bf16_lds(g, scale_bf16, sk, 8) + 3 * MR * kM * 256 * 2;
   return wgs >= 2 * kCUs && 2 * lds <= 160 * 1024;
 }
 
-template <int BITS, typename ST, int MODE, bool PK>
-static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  const int sk = choose_split(g, max_tiles, BITS, MODE == kModeSwiglu ? 16 : 32);
+template <int BITS, typename ST, int MODE, bool PK, int MR>
+static hipError_t launch_bmode_m(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  const int64_t wg_rows = max_tiles * (g.M / (MR * kM));  // workgroup rows of the grid
+  const int sk = choose_split(g, wg_rows, BITS, MODE == kModeSwiglu ? 16 : 32);
   if constexpr (PK && BITS == 4) {
-    if (use_eight_waves<BITS, MODE>(g, max_tiles, sk, sizeof(ST) == 2)) {
-      if (sk == 1) return launch_sk<BITS, ST, MODE, 1, PK, 8>(g, max_tiles, s);
-      return launch_sk<BITS, ST, MODE, 2, PK, 8>(g, max_tiles, s);
+    if (use_eight_waves<BITS, MODE, MR>(g, wg_rows, sk, sizeof(ST) == 2)) {
+      if (sk == 1) return launch_sk<BITS, ST, MODE, 1, PK, 8, MR>(g, max_tiles, s);
+      return launch_sk<BITS, ST, MODE, 2, PK, 8, MR>(g, max_tiles, s);
     }
   }
   switch (sk) {
-    case 1: return launch_sk<BITS, ST, MODE, 1, PK, kDecWaves>(g, max_tiles, s);
-    case 2: return launch_sk<BITS, ST, MODE, 2, PK, kDecWaves>(g, max_tiles, s);
-    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4, PK, kDecWaves>(g, max_tiles, s);
+    case 1: return launch_sk<BITS, ST, MODE, 1, PK, kDecWaves, MR>(g, max_tiles, s);
+    case 2: return launch_sk<BITS, ST, MODE, 2, PK, kDecWaves, MR>(g, max_tiles, s);
+    default: return launch_sk<BITS, ST, MODE, BITS == 4 ? 2 : 4, PK, kDecWaves, MR>(g, max_tiles, s);
   }
+}
+
+// Tiles of 16 rows: one MFMA row block per workgroup. Tiles of 32 rows: two row blocks
+// per workgroup sharing every decoded weight, except for 4-bit fc2 with per-row scales or
+// blocks of 128 and more, which ran faster as two workgroups of 16 rows each (twice the
+// workgroups, with fewer registers and less LDS each).
+template <int BITS, typename ST, int MODE, bool PK>
+static hipError_t launch_bmode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  const bool halves = BITS == 4 && MODE == kModeFc2 && (g.bs == 0 || g.bs >= 128);
+  if (g.M == 2 * kM && !halves) return launch_bmode_m<BITS, ST, MODE, PK, 2>(g, max_tiles, s);
+  return launch_bmode_m<BITS, ST, MODE, PK, 1>(g, max_tiles, s);
 }
 
 template <int BITS, typename ST, bool PK>

@@ -57,15 +57,17 @@ struct GemmTiming {
 void set_gemm_timing(hipEvent_t start, hipEvent_t stop);
 GemmTiming take_gemm_timing();
 
-// Every grouped-GEMM kernel is launched through this: one GemmArgs by value.
-inline hipError_t launch_gemm_kernel(void (*kernel)(GemmArgs), dim3 grid, dim3 block,
-                                     size_t lds, hipStream_t s, GemmArgs g) {
+// Every grouped-GEMM kernel is launched through this: one GemmArgs by value. A launch
+// error is left for the caller's hipGetLastError.
+inline void launch_gemm_kernel(void (*kernel)(GemmArgs), dim3 grid, dim3 block, size_t lds,
+                               hipStream_t s, GemmArgs g) {
   void* args[] = {&g};
   const GemmTiming t = take_gemm_timing();
   if (t.start != nullptr || t.stop != nullptr)
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s,
-                              t.start, t.stop, 0);
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s);
+    (void)hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s,
+                             t.start, t.stop, 0);
+  else
+    (void)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s);
 }
 
 // Tiled layout of one stack: S streams of `rows` rows each, N rows per expert in the
