@@ -53,7 +53,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5", "lin-decode", "lin-prefill"],
+                    help="c1-c5: the MoE layer workloads; lin-*: the single-expert linear "
+                         "layer (qmoe_linear_woq) at two layer shapes")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--bits", type=int, default=4)
     ap.add_argument("--block", type=int, default=32)
@@ -154,6 +157,9 @@ class TimingEvents:
 
 def workload(args):
     from synth import configs
+    if args.workload in configs.LINEAR:
+        cfg = configs.LINEAR[args.workload]
+        return cfg, args.T if args.T is not None else max(cfg.T_points)
     cfg = configs.ALL[args.workload]
     if args.workload == "c5":
         cfg = configs.c5_point(args.bits, args.block)
@@ -206,6 +212,8 @@ def main():
 
     cfg, T = workload(args)
     torch.cuda.set_device(0)
+    if cfg.E == 1 and cfg.k == 1:
+        return main_linear(args, cfg, T)
     print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
     inp = gen.make_inputs(cfg, T)
     d = DeviceInputs(inp)
@@ -366,6 +374,98 @@ def main():
         staged_ms_per_step=round(staged_ms, 5),
         algorithmic=dict(fc1_bytes=alg["fc1_bytes"], fc2_bytes=alg["fc2_bytes"],
                          weight_bytes=alg["weight_bytes"], flops=alg["flops"]),
+    )
+    print(json.dumps(line), flush=True)
+
+
+def main_linear(args, cfg, T):
+    """The single-expert linear layer: one qmoe_linear_woq call per step."""
+    import torch
+
+    import weight_only_quantized_softmax_amd as qm
+    from synth import gen
+    from tests.gpu_helpers import dev
+
+    print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
+    inp = gen.make_linear_inputs(cfg, T)
+    layout = args.layout if cfg.act_dtype == "bf16" else "rows"
+    p = qm.linear_params(T, cfg.H, cfg.I, expert_weight_bits=cfg.bits, block_size=cfg.block_size,
+                         activation=cfg.activation, act_dtype=cfg.act_dtype,
+                         scale_dtype=cfg.scale_dtype, tile_m=args.tile_m, weight_layout=layout)
+    qm.qmoe_validate(p)
+    x = dev(inp.x, cfg.act_dtype)
+    w = dev(inp.w1)
+    if layout == "tiles":
+        w = qm.pack_stack(p, "fc1", w)  # the one-time packing, outside every timed region
+    st = (w, dev(inp.s1, cfg.scale_dtype), dev(inp.b1, cfg.act_dtype) if inp.b1 is not None else None)
+    wbytes = stack_bytes(cfg, cfg.I, cfg.H, cfg.fc1_bias)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / wbytes) + 1)
+    copies = min(copies, 64)
+    stacks = [st] + [tuple(None if t is None else t.clone() for t in st) for _ in range(copies - 1)]
+    y = torch.empty((T, cfg.I), dtype=x.dtype, device="cuda")
+    stream = torch.cuda.Stream()
+    lib = qm._lib.load()
+    sargs = [qm._stack(c, "weight") for c in stacks]
+    sid = stream.cuda_stream
+    xp, yp = x.data_ptr(), y.data_ptr()
+    torch.cuda.synchronize()
+
+    def run(status):
+        if status != 0:
+            qm.check(status)
+
+    tev = TimingEvents(2 * args.steps)
+    print(f"[bench] {copies} weight copies of {wbytes / 1e6:.1f} MB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        run(lib.qmoe_linear_woq(p, xp, sargs[i % copies], yp, sid))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(lib.qmoe_time_next_gemm(tev.ev[2 * i], tev.ev[2 * i + 1]))
+        run(lib.qmoe_linear_woq(p, xp, sargs[i % copies], yp, sid))
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([tev.ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+    tev.close()
+
+    ab = 2 if cfg.act_dtype == "bf16" else 4
+    bytes_ = wbytes + T * cfg.H * ab + T * cfg.I * ab
+    flops = 2 * T * cfg.I * cfg.H
+    if flops / wbytes < 300:
+        gbps = bytes_ / (k_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None)
+    else:
+        tf = flops / (k_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+        chunk = min(T, args.cpu_tokens)
+        done, calls, start = 0, 0, 0
+        c0 = time.perf_counter()
+        while time.perf_counter() - c0 < CPU_SECONDS:
+            oracle.linear(cfg, inp, rows=(start + np.arange(chunk)) % T, nthreads=threads)
+            done += chunk
+            calls += 1
+            start = (start + chunk) % T
+        csec = time.perf_counter() - c0
+        cpu = dict(value=round(done / csec, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"{calls} fp64 oracle evaluations of {chunk} rows of the same T={T} "
+                          f"layer, {done} rows in {csec:.1f} s")
+    line = dict(
+        metric="tokens/s per QLinearWoQ layer + weight-stream HBM GB/s", value=round(T / (ms_per_step * 1e-3), 1),
+        unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16" if cfg.act_dtype == "bf16" else "f32", data="synthetic",
+        config=dict(workload=f"{cfg.name} T={T}", T=T, in_features=cfg.H, out_features=cfg.I,
+                    bits=cfg.bits, block_size=cfg.block_size, activation=cfg.activation,
+                    weight_layout=layout, tile_m=qm.qmoe_tile_m(p), weight_copies=copies),
+        roofline=roof, cpu_baseline=cpu, kernel_ms=dict(linear=round(k_ms, 5)),
+        algorithmic=dict(bytes=bytes_, weight_bytes=wbytes, flops=flops),
     )
     print(json.dumps(line), flush=True)
 

@@ -253,6 +253,24 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                          size_t workspace_bytes, void* stream);
 
 /*
+ * Weight-only-quantized linear layer (ClikaRT "QLinearWoQ" page: y = x @ dequant(weight)^T
+ * + bias, the weight at rest quantized, an optional activation fused as the epilogue):
+ * the grouped GEMM of this library over one expert and no routing.
+ *   p: the parameter block read as one layer -- num_experts 1, k 1; num_tokens = rows of
+ *      x (T), hidden_size = in_features (K), inter_size = out_features (N); activation
+ *      QMOE_ACT_IDENTITY, _RELU or _SILU (swiglu is rejected, QMOE_ERR_INVALID);
+ *      expert_weight_bits, block_size, scale_dtype, act_dtype, tile_m and weight_layout
+ *      as for the expert stacks.
+ *   x [T, K] act_dtype; w.weights uint8 [N, K*bits/8] (QMOE_LAYOUT_ROWS, dequant
+ *   (q - 2^(bits-1)) * scale) or its tiled form (qmoe_pack_stack with which = QMOE_FC1);
+ *   w.scales [N, ceil(K/block_size)] or [N] scale_dtype; w.bias [N] act_dtype or NULL;
+ *   y [T, N] act_dtype, written row for row (no padding rows).
+ * No workspace. Errors as for the other entry points.
+ */
+qmoe_status qmoe_linear_woq(const qmoe_params* p, const void* x, qmoe_stack w, void* y,
+                            void* stream);
+
+/*
  * Measurement hook, not a step of the method. The next grouped-GEMM kernel that the calling
  * thread launches -- the one launch of qmoe_grouped_gemm_fc1_swiglu or
  * qmoe_grouped_gemm_fc2, or the first of qmoe_forward's two -- records its own start and

@@ -94,7 +94,7 @@ def _stack(w, s, b) -> Stack:
 
 def stacks(inp):
     fc1 = _stack(inp.w1, inp.s1, inp.b1)
-    fc2 = _stack(inp.w2, inp.s2, inp.b2)
+    fc2 = _stack(inp.w2, inp.s2, inp.b2) if inp.w2 is not None else Stack()
     fc3 = _stack(inp.w3, inp.s3, inp.b3) if inp.w3 is not None else Stack()
     return fc1, fc2, fc3
 
@@ -146,6 +146,16 @@ def fc1_rows(cfg, inp, row_token, row_expert, nthreads: int = 0) -> np.ndarray:
     lib().oracle_fc1_rows(ctypes.byref(p), ctypes.byref(fc1), ctypes.byref(fc3), _ptr(inp.x),
                           len(rt), _ptr(rt), _ptr(re), _ptr(h), nthreads)
     return h
+
+
+def linear(cfg, inp, rows=None, nthreads: int = 0) -> np.ndarray:
+    """A single-expert weight-only-quantized linear layer (CLIKA "QLinearWoQ" page, class
+    description: y = x @ dequant(W)^T + bias, the activation as its fused epilogue): the fc1
+    row evaluation with every row its own token and expert 0. rows: the x rows to evaluate
+    (default all)."""
+    assert cfg.E == 1 and cfg.k == 1 and cfg.activation != "swiglu"
+    rt = np.arange(inp.x.shape[0]) if rows is None else np.asarray(rows)
+    return fc1_rows(cfg, inp, rt, np.zeros(len(rt), np.int32), nthreads)
 
 
 def fc2_rows(cfg, inp, h_in: np.ndarray, row_index, row_expert, nthreads: int = 0) -> np.ndarray:

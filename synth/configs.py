@@ -102,6 +102,20 @@ C5 = Config(name="c5-sweep", T_points=(1, 256, 4096), H=2048, I=1408, E=64, k=6,
             block_size=32, act_dtype="bf16", scale_dtype="bf16", fc1_bias=True,
             fc2_bias=False, scale_lo=0.002, scale_hi=0.05)
 
+# Single-expert linear layers (QLinearWoQ): one quantized weight [I, H] (out_features I,
+# in_features H), the layer shapes of the MoE workloads above read as dense layers.
+# lin-decode: c2's fused gate/up projection (2880 -> 5760), 4-bit, bs 32, bias, SiLU.
+LIN_DECODE = Config(name="lin-decode-int4", T_points=(1, 64), H=2880, I=5760, E=1, k=1,
+                    normalize=False, fusion=0, alpha=1.0, beta=0.0, limit=INF, bits=4,
+                    block_size=32, act_dtype="bf16", scale_dtype="bf16", fc1_bias=True,
+                    fc2_bias=False, activation="silu")
+# lin-prefill: c3's gate projection (4096 -> 14336), 4-bit per-row scales, no bias.
+LIN_PREFILL = Config(name="lin-prefill-int4", T_points=(4096,), H=4096, I=14336, E=1, k=1,
+                     normalize=False, fusion=0, alpha=1.0, beta=0.0, limit=INF, bits=4,
+                     block_size=0, act_dtype="bf16", scale_dtype="bf16", fc1_bias=False,
+                     fc2_bias=False, activation="identity")
+LINEAR = {"lin-decode": LIN_DECODE, "lin-prefill": LIN_PREFILL}
+
 C5_BITS = (4, 8)
 C5_BLOCKS = (16, 32, 64, 128)
 

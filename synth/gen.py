@@ -117,6 +117,15 @@ def make_inputs(cfg: Config, T: int, seed: int = 0, shared: bool = False) -> Inp
                   b2=b2, w3=w3, s3=s3, b3=b3, shared=sh)
 
 
+def make_linear_inputs(cfg: Config, T: int, seed: int = 0) -> Inputs:
+    """Inputs of a single-expert linear layer (E = 1, k = 1): x [T, H] and the one weight
+    stack [1, I, H/pack] with its scales and optional bias; no logits and no fc2 stack."""
+    assert cfg.E == 1 and cfg.k == 1 and cfg.activation != "swiglu"
+    x = store(rng_for(cfg, "x", T, seed).normal(0.0, cfg.x_sigma, size=(T, cfg.H)), cfg.act_dtype)
+    w1, s1, b1 = gen_weights(cfg, "1", cfg.I, cfg.H, seed)
+    return Inputs(cfg=cfg, T=T, x=x, logits=None, w1=w1, s1=s1, b1=b1, w2=None, s2=None, b2=None)
+
+
 def gen_stage_h(cfg: Config, rows: int, seed: int = 0, sigma: float = 1.0) -> np.ndarray:
     """A synthetic fc2 input [rows, I] in the activation dtype."""
     return store(rng_for(cfg, "h", rows, seed).normal(0.0, sigma, size=(rows, cfg.I)), cfg.act_dtype)

@@ -218,3 +218,23 @@ def test_every_gpu_parity_case_passes_validation(lib):
         if lib.qmoe_validate(params_for(cfg, T, tile_m=m, layout=lay)) != 0:
             bad.append((what, cfg.name, T, m, lay, lib.qmoe_last_error()))
     assert not bad
+
+
+def test_linear_woq_host_checks(lib):
+    """qmoe_linear_woq: one expert, k = 1, no SwiGLU; NULL buffers are unbound; zero rows
+    enqueue nothing (no device is touched on these paths)."""
+    lp = qm.linear_params(8, 256, 128, block_size=32, activation="silu")
+    S = _lib.QmoeStack
+    full = S(weights=1 << 20, scales=1 << 20, bias=None)
+    assert lib.qmoe_linear_woq(lp, None, full, 1 << 20, None) == _lib.QMOE_ERR_UNBOUND
+    assert lib.qmoe_linear_woq(lp, 1 << 20, S(), 1 << 20, None) == _lib.QMOE_ERR_UNBOUND
+    assert lib.qmoe_linear_woq(lp, 1 << 20, full, None, None) == _lib.QMOE_ERR_UNBOUND
+    moe = qm.make_params(8, 256, 128, 4, 2, block_size=32, activation="silu")
+    assert lib.qmoe_linear_woq(moe, 1 << 20, full, 1 << 20, None) == _lib.QMOE_ERR_INVALID
+    sw = qm.make_params(8, 256, 128, 1, 1, block_size=32, activation="swiglu")
+    assert lib.qmoe_linear_woq(sw, 1 << 20, full, 1 << 20, None) == _lib.QMOE_ERR_INVALID
+    empty = qm.linear_params(0, 256, 128, block_size=32)
+    assert lib.qmoe_linear_woq(empty, None, S(), None, None) == _lib.QMOE_OK
+    assert lib.qmoe_tile_m(qm.linear_params(300, 256, 128)) == 128
+    assert lib.qmoe_tile_m(qm.linear_params(37, 256, 128)) == 32
+    assert lib.qmoe_tile_m(qm.linear_params(5, 256, 128)) == 16

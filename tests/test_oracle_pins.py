@@ -237,6 +237,25 @@ def test_single_expert_is_dequant_ffn():
     assert np.allclose(out64, y.numpy(), rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("bits,bs,act,sdt", [(4, 32, "silu", "bf16"), (8, 0, "relu", "f32"),
+                                              (4, 0, "identity", "f32"), (8, 64, "silu", "bf16")])
+def test_linear_is_dense_dequant_matmul(bits, bs, act, sdt):
+    # QLinearWoQ: y = act(x @ dequant(W)^T + b), against torch's linear and activation on
+    # the independently dequantised weight; K = 80 gives a short last block for bs 32 and 64
+    cfg = configs.tiny(E=1, k=1, fusion=0, activation=act, bits=bits, block_size=bs, H=80,
+                       I=24, fc1_bias=True, act_dtype="bf16", scale_dtype=sdt)
+    inp = gen.make_linear_inputs(cfg, 7)
+    got = oracle.linear(cfg, inp)
+    W = torch.from_numpy(bruteforce.dequant_dense(inp.w1, inp.s1, cfg, cfg.I, cfg.H)[0])
+    x = torch.from_numpy(as_f32(inp.x, "bf16").astype(np.float64))
+    b = torch.from_numpy(as_f32(inp.b1[0], "bf16").astype(np.float64))
+    z = torch.nn.functional.linear(x, W, b)
+    ref = {"silu": torch.nn.functional.silu, "relu": torch.relu, "identity": lambda v: v}[act](z)
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # a row subset evaluates the same rows
+    assert np.array_equal(oracle.linear(cfg, inp, rows=[6, 2]), got[[6, 2]])
+
+
 def test_swiglu_clamp_reading():
     # Only the gate is clamped from above; the up value is clamped on both sides.
     cfg = configs.tiny(fusion=2, bits=8, block_size=0, H=16, I=16, E=1, k=1, alpha=1.702,

@@ -21,7 +21,7 @@ __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
            "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
-           "qmoe_time_next_gemm", "forward",
+           "qmoe_time_next_gemm", "qmoe_linear_woq", "linear_params", "linear_woq", "forward",
            "QmoeError", "QmoeParams"]
 
 _DT = {"f32": QMOE_F32, "bf16": QMOE_BF16}
@@ -173,6 +173,35 @@ def pack_stack(p: QmoeParams, which: str, weights: torch.Tensor, stream=None) ->
     packed = torch.empty(n, dtype=torch.uint8, device=weights.device)
     qmoe_pack_stack(p, which, weights, packed, stream)
     return packed
+
+
+def linear_params(num_tokens: int, in_features: int, out_features: int, *,
+                  expert_weight_bits: int = 4, block_size: int = 0, activation: str = "identity",
+                  act_dtype: str = "bf16", scale_dtype: str = "bf16", tile_m: int = 0,
+                  strict_blocks: bool = False, weight_layout: str = "rows") -> QmoeParams:
+    """The parameter block of a QLinearWoQ layer: one expert, k = 1."""
+    return make_params(num_tokens, in_features, out_features, 1, 1,
+                       expert_weight_bits=expert_weight_bits, block_size=block_size,
+                       activation=activation, normalize_routing_weights=False,
+                       act_dtype=act_dtype, scale_dtype=scale_dtype, tile_m=tile_m,
+                       strict_blocks=strict_blocks, weight_layout=weight_layout)
+
+
+def qmoe_linear_woq(p: QmoeParams, x, w: Stack, y, stream=None) -> None:
+    check(load().qmoe_linear_woq(p, _ptr(x, "x"), _stack(w, "weight"), _ptr(y, "y"),
+                                 _stream(stream)))
+
+
+def linear_woq(p: QmoeParams, x: torch.Tensor, w: Stack, stream=None) -> torch.Tensor:
+    """y = act(x @ dequant(W)^T + b) for x [*, in_features] (the QLinearWoQ forward)."""
+    K, N = p.hidden_size, p.inter_size
+    x2 = x.reshape(-1, K)
+    if x2.shape[0] != p.num_tokens:
+        raise QmoeError(QMOE_ERR_SHAPE, f"x holds {x2.shape[0]} rows, params say {p.num_tokens}")
+    _expect(x2, (p.num_tokens, K), _TORCH_DT[p.act_dtype], "x")
+    y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
+    qmoe_linear_woq(p, x2, w, y.view(-1, N), stream)
+    return y
 
 
 def qmoe_time_next_gemm(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:

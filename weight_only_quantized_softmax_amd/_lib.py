@@ -38,8 +38,8 @@ class QmoeStack(ctypes.Structure):
 EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_time_next_gemm",
-           "qmoe_last_error")
+           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
+           "qmoe_time_next_gemm", "qmoe_last_error")
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
     L.qmoe_packed_stack_size.argtypes = [P, ctypes.c_int32]
     L.qmoe_packed_stack_size.restype = sz
     L.qmoe_pack_stack.argtypes, L.qmoe_pack_stack.restype = [P, ctypes.c_int32, vp, vp, vp], st
+    L.qmoe_linear_woq.argtypes = [P, vp, QmoeStack, vp, vp]
+    L.qmoe_linear_woq.restype = st
     L.qmoe_time_next_gemm.argtypes, L.qmoe_time_next_gemm.restype = [vp, vp], st
     L.qmoe_last_error.argtypes, L.qmoe_last_error.restype = [], ctypes.c_char_p
     _lib = L

@@ -297,6 +297,25 @@ qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_a
   return device_status(launch_gemm(p, g, mode, s), "fc1 launch");
 }
 
+// The single-expert linear layer: the fc1-side GEMM over the rows of x in consecutive
+// tiles, plain activation epilogue, output rows stored only for real rows.
+qmoe_status run_linear(const qmoe_params* p, const void* x, qmoe_stack w, void* y, hipStream_t s) {
+  qmoe::GemmArgs g = gemm_args(p);
+  g.a = x;
+  g.linear = 1;
+  g.w = static_cast<const uint8_t*>(w.weights);
+  g.s = w.scales;
+  g.b = w.bias;
+  g.out = y;
+  g.K = static_cast<int>(p->hidden_size);
+  g.a_rows = p->num_tokens;
+  g.N = static_cast<int>(p->inter_size);
+  g.ncols = static_cast<int>(p->inter_size);
+  g.nb = p->block_size ? static_cast<int>((p->hidden_size + p->block_size - 1) / p->block_size) : 0;
+  set_tiles(p, g, static_cast<int>(p->inter_size));
+  return device_status(launch_gemm(p, g, qmoe::kModePlainAct, s), "linear launch");
+}
+
 qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
                     const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s) {
   qmoe::GemmArgs g = gemm_args(p);
@@ -523,6 +542,21 @@ qmoe_status qmoe_pack_stack(const qmoe_params* p, int32_t which, const void* wei
                                                static_cast<uint8_t*>(packed), a,
                                                static_cast<hipStream_t>(stream)),
                        "pack launch");
+}
+
+qmoe_status qmoe_linear_woq(const qmoe_params* p, const void* x, qmoe_stack w, void* y,
+                            void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->num_experts != 1 || p->k != 1)
+    return fail(QMOE_ERR_INVALID, "a linear layer has num_experts 1 and k 1 (got %lld, %lld)",
+                (long long)p->num_experts, (long long)p->k);
+  if (swiglu(p))
+    return fail(QMOE_ERR_INVALID, "a linear layer's activation is identity, relu or silu");
+  if (p->num_tokens == 0) return ok();
+  QMOE_TRY(need(x, "x"));
+  QMOE_TRY(check_stack(w, "weight"));
+  QMOE_TRY(need(y, "y"));
+  return run_linear(p, x, w, y, static_cast<hipStream_t>(stream));
 }
 
 qmoe_status qmoe_time_next_gemm(void* start_event, void* stop_event) {

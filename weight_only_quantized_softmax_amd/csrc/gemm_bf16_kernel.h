@@ -93,9 +93,10 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   // a grouping tile of g.M rows is covered by g.M / TM workgroup rows of TM rows each
   const int nsub = g.M / TM;
   const int tile = blockIdx.y / nsub, sub = blockIdx.y % nsub;
-  if (tile >= *g.num_tiles) return;
-  const int e = g.tile_list[2 * tile];
-  const int valid = min(max(g.tile_list[2 * tile + 1] - sub * TM, 0), TM);
+  if (tile >= gemm_tile_count(g)) return;
+  const int2 tv = gemm_tile(g, tile);
+  const int e = tv.x;
+  const int valid = min(max(tv.y - sub * TM, 0), TM);
   if (MODE == kModeFc2 && valid == 0) return;  // no output rows (fc1 writes zero rows)
   const int64_t row0 = static_cast<int64_t>(tile) * g.M + sub * TM;
 
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
     const int q = (lane % GPR) ^ key(r);
     xk[t] = 8 * q;
     if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
+      const int64_t src = (MODE == kModeFc2) ? row0 + r : gemm_src_row(g, row0 + r);
       xoff[t] = static_cast<uint32_t>((src * K + 8 * q) * 2);
     } else {
       xoff[t] = kOutOfRange;  // padding rows land as zeros
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
       float h = 0.f;
       if (m < valid)
         h = swiglu(tot[mr][0][i] + bias[0], tot[mr][1][i] + bias[1], g.alpha, g.beta, g.limit);
-      static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
+      if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
     } else {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
           if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[mr][st][i] + bias[st];
         } else {
           const float h = m < valid ? plain_act(tot[mr][st][i] + bias[st], g.act) : 0.f;
-          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
+          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
         }
       }
     }

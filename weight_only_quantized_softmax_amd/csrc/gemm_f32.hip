@@ -30,9 +30,10 @@ template <int BITS, typename ST, int MODE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   extern __shared__ float xs[];  // [M][K]
   const int tile = blockIdx.y;
-  if (tile >= *g.num_tiles) return;
-  const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
+  if (tile >= gemm_tile_count(g)) return;
+  const int2 tv = gemm_tile(g, tile);
+  const int e = tv.x;
+  const int valid = tv.y;
   const int M = g.M, K = g.K;
   const int64_t row0 = static_cast<int64_t>(tile) * M;
 
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       if (MODE == kModeFc2) {
         src = row0 + m;
       } else {
-        src = g.sorted_assign[row0 + m] / g.topk;
+        src = gemm_src_row(g, row0 + m);
       }
       v = static_cast<const float*>(g.a)[src * K + kk];
     }
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       if (MODE == kModeFc2) {
         if (m < valid) static_cast<float*>(g.out)[(row0 + m) * g.ncols + col] = v;
       } else {
-        static_cast<float*>(g.out)[(row0 + m) * g.ncols + col] = m < valid ? v : 0.f;
+        if (m < valid || !g.linear)
+          static_cast<float*>(g.out)[(row0 + m) * g.ncols + col] = m < valid ? v : 0.f;
       }
     }
   }

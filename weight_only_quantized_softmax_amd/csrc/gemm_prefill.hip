@@ -69,9 +69,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_kernel(GemmArgs g) {
   __shared__ float scl[PERROW ? 1 : GPS][SROWS];                               // this super-step's scales
 
   const int tile = blockIdx.x;
-  if (tile >= *g.num_tiles) return;
-  const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
+  if (tile >= gemm_tile_count(g)) return;
+  const int2 tv = gemm_tile(g, tile);
+  const int e = tv.x;
+  const int valid = tv.y;
   const int64_t row0 = static_cast<int64_t>(tile) * kTM;
 
   const int tid = threadIdx.x;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_kernel(GemmArgs g) {
     const int f = tid + 256 * i;
     const int m = f / TPR, kk = (f % TPR) * 8;
     if (m < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + m : g.sorted_assign[row0 + m] / g.topk;
+      const int64_t src = (MODE == kModeFc2) ? row0 + m : gemm_src_row(g, row0 + m);
       xoff[i] = static_cast<uint32_t>((src * K + kk) * 2);
     } else {
       xoff[i] = kOutOfRange;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_kernel(GemmArgs g) {
           if (m < valid)
             h = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
                                       : plain_act(z[0], g.act);
-          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
+          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
         }
       }
     }

@@ -80,9 +80,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   __shared__ ST sring[2][SROWS * NBLK];  // scales of this step and the next
 
   int tile, cblk;
-  if (!xcd_item(*g.num_tiles, (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
-  const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
+  if (!xcd_item(gemm_tile_count(g), (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
+  const int2 tv = gemm_tile(g, tile);
+  const int e = tv.x;
+  const int valid = tv.y;
   const int64_t row0 = static_cast<int64_t>(tile) * kBTM;
 
   const int tid = threadIdx.x;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
     const int r = p / GPR, q = granule(t);
     uint32_t off = kOutOfRange;  // padding rows land as zeros
     if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
+      const int64_t src = (MODE == kModeFc2) ? row0 + r : gemm_src_row(g, row0 + r);
       off = static_cast<uint32_t>((src * K + 8 * q) * 2);
     }
     xoff(t) = off;
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
           if (m < valid)
             hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
                                        : plain_act(z[0], g.act);
-          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
         }
       }
     }

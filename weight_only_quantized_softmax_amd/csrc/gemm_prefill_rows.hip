@@ -98,8 +98,9 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   constexpr int wn = WN;
   static_assert(MT == 2 * S::WNC, "each wave sums the rows of two MFMA tiles");
 
-  const int e = g.tile_list[2 * tile];
-  const int valid = g.tile_list[2 * tile + 1];
+  const int2 tv = gemm_tile(g, tile);
+  const int e = tv.x;
+  const int valid = tv.y;
   const int64_t row0 = static_cast<int64_t>(tile) * kRTM;
 
   const int tid = threadIdx.x;
@@ -188,7 +189,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     const int r = p / GPR, q = granule(t);
     uint32_t off = kOutOfRange;  // padding rows land as zeros
     if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : g.sorted_assign[row0 + r] / g.topk;
+      const int64_t src = (MODE == kModeFc2) ? row0 + r : gemm_src_row(g, row0 + r);
       off = static_cast<uint32_t>((src * K + 8 * q) * 2);
     }
     xoff(t) = off;
@@ -369,7 +370,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
           if (m < valid)
             hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
                                        : plain_act(z[0], g.act);
-          static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
         }
       }
     }
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   __shared__ uint32_t xoffs_lds[S::XREG ? 1 : S::NDMA * 256];
 
   int tile, cblk;
-  if (!xcd_item(*g.num_tiles, (g.ncols + S::BCOLS - 1) / S::BCOLS, tile, cblk)) return;
+  if (!xcd_item(gemm_tile_count(g), (g.ncols + S::BCOLS - 1) / S::BCOLS, tile, cblk)) return;
   // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   switch (wave / S::WM) {

@@ -46,7 +46,27 @@ struct GemmArgs {
   int packed;
   int kt;                      // tiles along K (ceil(K / S_K))
   int nbk;                     // 16-row blocks per stream
+  // single-expert linear layer: the rows of a are the output rows, in consecutive tiles
+  // of M rows (no tile list, no gather), and rows past a_rows are never stored
+  int linear;
 };
+
+// Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
+__device__ __forceinline__ int gemm_tile_count(const GemmArgs& g) {
+  return g.linear ? static_cast<int>((g.a_rows + g.M - 1) / g.M) : *g.num_tiles;
+}
+// (expert, valid rows) of tile `tile`
+__device__ __forceinline__ int2 gemm_tile(const GemmArgs& g, int tile) {
+  if (g.linear) {
+    const int64_t left = g.a_rows - static_cast<int64_t>(tile) * g.M;
+    return make_int2(0, static_cast<int>(left < g.M ? left : g.M));
+  }
+  return make_int2(g.tile_list[2 * tile], g.tile_list[2 * tile + 1]);
+}
+// Row of a that feeds padded row `row` of an fc1-side GEMM (fc2 reads row itself).
+__device__ __forceinline__ int64_t gemm_src_row(const GemmArgs& g, int64_t row) {
+  return g.linear ? row : g.sorted_assign[row] / g.topk;
+}
 
 // Measurement hook: HIP events that the calling thread's next grouped-GEMM launch records
 // its own start and end on (hipExtLaunchKernel). take_gemm_timing returns them and clears
