@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "gemm_common.h"
+#include "gemm_gemv_kernel.h"
 #include "launch.h"
 
 namespace qmoe {
@@ -52,9 +53,12 @@ constexpr int kDecWaves = 4;  // waves per workgroup (eight for large tiled-layo
 // PK: the weights come in the tiled layout (qmoe_pack_stack): each lane's 16 bytes of a
 // super-step are one contiguous 1 KB tile of its 16-row slice, already in MFMA order
 // (word j of lane (n, q) holds k = 32j + 8q .. +8 of row n, nibbles in decode order).
-template <int BITS, typename ST, int MODE, int BS, int SK, bool PK, int NW_, int MR>
+template <int BITS, typename ST, int MODE, int BS, int SK, bool PK, int NW_, int MR, int PD>
 __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   constexpr int NW = NW_;
+  // prefetch distance: chunk ci + PD is requested while chunk ci is computed, from a ring
+  // of PD + 1 weight slots and LDS activation stages
+  static_assert(PD >= 2 && PD <= 4, "prefetch distance 2 to 4");
   constexpr int TM = MR * kM;                   // rows of a tile: MR MFMA row blocks of 16
   constexpr bool PERROW = BS == 0;
   constexpr int SSK0 = BITS == 4 ? 128 : 64;
@@ -83,11 +87,16 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   // -(c+z) as a bf16 pair: 136 = 128 + 8 (4-bit), 128 = 0 + 128 (8-bit), both exact
   constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;
 
-  // three activation stages as three arrays, so that the compiler can tell the stage
+  // the activation stages as separate arrays, so that the compiler can tell the stage
   // being read from the stages being filled
   __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs3[PD >= 3 ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs4[PD >= 4 ? STAGE : 8];
+  auto stage = [&](int r) -> uint16_t* {
+    return r == 0 ? xs0 : r == 1 ? xs1 : r == 2 ? xs2 : r == 3 ? xs3 : xs4;
+  };
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // scales
 
   // a grouping tile of g.M rows is covered by g.M / TM workgroup rows of TM rows each
@@ -220,24 +229,25 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  Slot w0, w1, w2;
+  Slot wr[PD + 1];
   xload(0, xs0);
   __builtin_amdgcn_sched_barrier(0);
-  wload(0, w0);
-  if (nchunks > 1) xload(1, xs1);
-  __builtin_amdgcn_sched_barrier(0);
-  wload(min(1, nchunks - 1), w1);
-  // the scales and chunk 0's activations were issued first and loads complete in order:
-  // only chunk 0's weights and chunk 1's loads may still be pending
-  {
-    constexpr int kW2 = 2 * NS * SPW, kW2X = kW2 + NDMA;
-    static_assert(kW2X < 64, "vmcnt holds 6 bits");
-    if (nchunks > 1)
-      __builtin_amdgcn_s_waitcnt((kW2X & 15) | ((kW2X >> 4) << 14) | (7 << 4) | (15 << 8));
-    else
-      __builtin_amdgcn_s_waitcnt((kW2 & 15) | ((kW2 >> 4) << 14) | (7 << 4) | (15 << 8));
+  wload(0, wr[0]);
+#pragma unroll
+  for (int i = 1; i < PD; ++i) {
+    if (i < nchunks) xload(i, stage(i));
+    __builtin_amdgcn_sched_barrier(0);
+    wload(min(i, nchunks - 1), wr[i]);
   }
-  __syncthreads();
+  // the scales and chunk 0's activations were issued first and loads complete in order:
+  // chunk 0 has landed once at most the later loads are pending (the weights of chunks
+  // 0 .. PD-1 and the activations of chunks 1 .. PD-1 that exist)
+  constexpr int kWgt = PD * NS * SPW;  // weight loads issued after an activation load
+  static_assert(kWgt + (PD - 1) * NDMA < 64, "vmcnt holds 6 bits");
+  wait_vm_sel<kWgt, NDMA, PD - 1>(min(PD - 1, nchunks - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   const ST* my_scl[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st)
@@ -364,35 +374,32 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
     }
   };
 
-  // s_waitcnt immediate: vmcnt = the loads issued after chunk ci + 1's activation loads
-  // (chunk ci + 1's weights, chunk ci + 2's activations and weights), expcnt and lgkmcnt
-  // left open
-  constexpr int kAfter = NDMA + 2 * NS * SPW;
-  static_assert(kAfter < 64, "vmcnt holds 6 bits");
-  constexpr int kWaitX = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
-  // chunk ci computes from stage / slot ci % 3 and requests chunk ci + 2 into the third
+  // chunk ci computes from stage / slot ci % (PD + 1) and requests chunk ci + PD into
+  // the slot and stage freed one chunk earlier
   auto chunk = [&](Slot& cur, const uint16_t* xcur, Slot& ahead, uint16_t* xahead, int ci) {
-    if (ci + 2 < nchunks) xload(ci + 2, xahead);
+    if (ci + PD < nchunks) xload(ci + PD, xahead);
     __builtin_amdgcn_sched_barrier(0);
-    wload(min(ci + 2, nchunks - 1), ahead);
+    wload(min(ci + PD, nchunks - 1), ahead);
     compute(cur, xcur, ci);
-    // chunk ci + 1's activations have landed once at most the later loads are pending.
-    // A bare barrier follows: every LDS read of chunk ci has returned (the MFMAs used
-    // it), and a workgroup fence would also wait for chunk ci + 2's loads.
-    if (ci + 2 < nchunks)
-      __builtin_amdgcn_s_waitcnt(kWaitX);
+    // chunk ci + 1's activations have landed once at most the later loads are pending:
+    // the weights of chunks ci + 1 .. ci + PD and the activations of chunks
+    // ci + 2 .. ci + PD that exist. A bare barrier follows: every LDS read of chunk ci has
+    // returned (the MFMAs used it), and a workgroup fence would also wait for the loads
+    // of the chunks ahead.
+    if (ci + 1 < nchunks)
+      wait_vm_sel<kWgt, NDMA, PD - 1>(min(PD - 1, nchunks - ci - 2));
     else
       __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // three chunks per trip so that ring slots and stages are fixed; a chunk past the end
+  // PD + 1 chunks per trip so that ring slots and stages are fixed; a chunk past the end
   // computes nothing and only re-reads the last chunk's weights
-  for (int ci = 0; ci < nchunks; ci += 3) {
-    chunk(w0, xs0, w2, xs2, ci);
-    chunk(w1, xs1, w0, xs0, ci + 1);
-    chunk(w2, xs2, w1, xs1, ci + 2);
+  for (int ci = 0; ci < nchunks; ci += PD + 1) {
+#pragma unroll
+    for (int r = 0; r <= PD; ++r)
+      chunk(wr[r], stage(r), wr[(r + PD) % (PD + 1)], stage((r + PD) % (PD + 1)), ci + r);
   }
 
   if (PERROW) {
@@ -490,7 +497,7 @@ inline size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk, int nw =
   return static_cast<size_t>(2) * (nw / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
 }
 
-template <int BITS, typename ST, int MODE, int SK, bool PK, int NW, int MR>
+template <int BITS, typename ST, int MODE, int SK, bool PK, int NW, int MR, int PD = 2>
 static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   constexpr int CPB = NW / SK;
   const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
@@ -498,7 +505,7 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
       block(NW * 64);
   const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK, NW);
 #define QMOE_DEC(BSV, SKV) \
-  launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, BSV, SKV, PK, NW, MR>, grid, block, lds, s, g)
+  launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, BSV, SKV, PK, NW, MR, PD>, grid, block, lds, s, g)
   switch (g.bs) {
     case 0: QMOE_DEC(0, SK); break;
     case 16: QMOE_DEC(16, SK); break;
@@ -526,6 +533,18 @@ static bool use_eight_waves(const GemmArgs& g, int64_t wg_rows, int sk, bool sca
   return wgs >= 2 * kCUs && 2 * lds <= 160 * 1024;
 }
 
+// Small grids (at most two four-wave workgroups per CU, as at one to a few tokens) run the
+// weight-streaming kernel instead (tiled layout): one column group per workgroup, K split
+// over its waves, no LDS activation stages.
+constexpr int kGemvWaves = 4;
+constexpr int kGemvPD = 2;
+template <int MODE>
+static bool small_grid(const GemmArgs& g, int64_t wg_rows, int sk) {
+  constexpr int kCUs = 256;
+  const int wg_cols = (kDecWaves / sk) * (MODE == kModeSwiglu ? 16 : 32);
+  return wg_rows * ((g.ncols + wg_cols - 1) / wg_cols) <= 2 * kCUs;
+}
+
 template <int BITS, typename ST, int MODE, bool PK, int MR>
 static hipError_t launch_bmode_m(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int64_t wg_rows = max_tiles * (g.M / (MR * kM));  // workgroup rows of the grid
@@ -535,6 +554,10 @@ static hipError_t launch_bmode_m(const GemmArgs& g, int64_t max_tiles, hipStream
       if (sk == 1) return launch_sk<BITS, ST, MODE, 1, PK, 8, MR>(g, max_tiles, s);
       return launch_sk<BITS, ST, MODE, 2, PK, 8, MR>(g, max_tiles, s);
     }
+  }
+  if constexpr (PK && MR == 1) {
+    if (g.M == kM && small_grid<MODE>(g, wg_rows, sk))
+      return launch_gemv<BITS, ST, MODE, kGemvWaves, kGemvPD>(g, max_tiles, s);
   }
   switch (sk) {
     case 1: return launch_sk<BITS, ST, MODE, 1, PK, kDecWaves, MR>(g, max_tiles, s);

@@ -43,6 +43,26 @@ __device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
+// s_waitcnt with vmcnt = N, expcnt and lgkmcnt left open.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// The same with vmcnt = BASE + i * STEP for a wave-uniform i in [0, MAXI], each count a
+// compile-time immediate.
+template <int BASE, int STEP, int MAXI>
+__device__ __forceinline__ void wait_vm_sel(int i) {
+  if constexpr (MAXI == 0) {
+    wait_vm<BASE>();
+  } else {
+    if (i >= MAXI)
+      wait_vm<BASE + MAXI * STEP>();
+    else
+      wait_vm_sel<BASE, STEP, MAXI - 1>(i);
+  }
+}
+
 // (v & mask) | magic in one gfx950 three-input bit operation.
 __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
   return __builtin_amdgcn_bitop3_b32(v, mask, magic, 0xEA);
