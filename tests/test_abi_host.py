@@ -235,6 +235,9 @@ def test_linear_woq_host_checks(lib):
     assert lib.qmoe_linear_woq(sw, 1 << 20, full, 1 << 20, None) == _lib.QMOE_ERR_INVALID
     empty = qm.linear_params(0, 256, 128, block_size=32)
     assert lib.qmoe_linear_woq(empty, None, S(), None, None) == _lib.QMOE_OK
-    assert lib.qmoe_tile_m(qm.linear_params(300, 256, 128)) == 128
+    # one expert: 128-row tiles only where their grid is large (32 tiles x 32 column blocks)
+    assert lib.qmoe_tile_m(qm.linear_params(4096, 4096, 14336)) == 128
+    assert lib.qmoe_tile_m(qm.linear_params(64, 2880, 5760)) == 32
+    assert lib.qmoe_tile_m(qm.linear_params(300, 256, 128)) == 32
     assert lib.qmoe_tile_m(qm.linear_params(37, 256, 128)) == 32
     assert lib.qmoe_tile_m(qm.linear_params(5, 256, 128)) == 16

@@ -29,16 +29,16 @@ def gpu():
     torch.cuda.init()
 
 
-def lin_params(cfg, T, layout="rows"):
+def lin_params(cfg, T, layout="rows", tile_m=0):
     return qm.linear_params(T, cfg.H, cfg.I, expert_weight_bits=cfg.bits,
                             block_size=cfg.block_size, activation=cfg.activation,
                             act_dtype=cfg.act_dtype, scale_dtype=cfg.scale_dtype,
-                            weight_layout=layout)
+                            tile_m=tile_m, weight_layout=layout)
 
 
-def run_linear(cfg, inp, layout):
+def run_linear(cfg, inp, layout, tile_m=0):
     T = inp.x.shape[0]
-    p = lin_params(cfg, T, layout)
+    p = lin_params(cfg, T, layout, tile_m)
     w = dev(inp.w1)
     if layout == "tiles":
         w = qm.pack_stack(p, "fc1", w)
@@ -49,9 +49,9 @@ def run_linear(cfg, inp, layout):
     return host_f64(y, cfg.act_dtype), qm.qmoe_tile_m(p)
 
 
-def check(cfg, T, layout, sample=None):
+def check(cfg, T, layout, sample=None, tile_m=0):
     inp = gen.make_linear_inputs(cfg, T)
-    got, M = run_linear(cfg, inp, layout)
+    got, M = run_linear(cfg, inp, layout, tile_m)
     print("linear", cfg.name, layout, "T", T, "K", cfg.H, "N", cfg.I, "M", M, flush=True)
     assert got.shape == (T, cfg.I)
     rows = np.arange(T)
@@ -86,15 +86,16 @@ SMALL = {
                                    H=384, I=256, fc1_bias=True, act_dtype="bf16",
                                    scale_dtype="bf16"),
 }
-# token counts that select 16-, 32- and 128-row tiles, each with a ragged last tile
-TOKENS = (5, 37, 300)
+# (tokens, tile_m): the library's 16- and 32-row choices and the 128-row kernels asked
+# for explicitly (the library keeps them for large grids), each with a ragged last tile
+TOKENS = ((5, 0), (37, 0), (300, 128))
 
 
 @pytest.mark.parametrize("layout", ["rows", "tiles"])
-@pytest.mark.parametrize("T", TOKENS)
+@pytest.mark.parametrize("T,tile_m", TOKENS)
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_linear_matches_oracle(name, T, layout):
-    M = check(SMALL[name], T, layout)
+def test_linear_matches_oracle(name, T, tile_m, layout):
+    M = check(SMALL[name], T, layout, tile_m=tile_m)
     assert M == {5: 16, 37: 32, 300: 128}[T]
 
 

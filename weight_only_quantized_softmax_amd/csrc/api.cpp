@@ -67,12 +67,16 @@ int64_t n1_rows(const qmoe_params* p) {
 }
 
 // Rows per expert tile, from shapes only: 128-row MFMA tiles when an expert is expected
-// to receive at least 64 rows (prefill); 32-row weight-streaming tiles from 12 expected rows
-// on, so that an expert's 17-32 rows read its weights once, not twice; 16-row tiles below.
+// to receive at least 64 rows (prefill) and the 128-row grid still has some 512 or more
+// workgroups (a single expert, as in the linear layer, gives few tiles); 32-row
+// weight-streaming tiles from 12 expected rows on, so that an expert's 17-32 rows read its
+// weights once, not twice; 16-row tiles below.
 int32_t default_tile_m(const qmoe_params* p) {
   if (p->act_dtype == QMOE_BF16) {
     const int64_t a = p->num_tokens * p->k;
-    if (a >= 64 * p->num_experts) return 128;
+    const int64_t tiles128 = std::max<int64_t>(a / 128, std::min(p->num_experts, a));
+    const int64_t cols128 = std::min(p->hidden_size, p->inter_size) / 128;
+    if (a >= 64 * p->num_experts && tiles128 * cols128 >= 512) return 128;
     return a >= 12 * p->num_experts ? 32 : 16;
   }
   const int64_t kmax = std::max(p->hidden_size, p->inter_size);
