@@ -54,9 +54,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "lin-decode", "lin-prefill"],
-                    help="c1-c5: the MoE layer workloads; lin-*: the single-expert linear "
-                         "layer (qmoe_linear_woq) at two layer shapes")
+                    choices=["c1", "c2", "c3", "c4", "c5", "c2-mx", "c5-mx", "lin-decode",
+                             "lin-prefill"],
+                    help="c1-c5: the MoE layer workloads; c2-mx, c5-mx: the same shapes with "
+                         "MX FP4 weights; lin-*: the single-expert linear layer "
+                         "(qmoe_linear_woq) at two layer shapes")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--bits", type=int, default=4)
     ap.add_argument("--block", type=int, default=32)
@@ -161,6 +163,9 @@ def workload(args):
     if args.workload in configs.LINEAR:
         cfg = configs.LINEAR[args.workload]
         return cfg, args.T if args.T is not None else max(cfg.T_points)
+    if args.workload in configs.MX:
+        cfg = configs.MX[args.workload]
+        return cfg, args.T if args.T is not None else (64 if args.workload == "c2-mx" else 4096)
     cfg = configs.ALL[args.workload]
     if args.workload == "c5":
         cfg = configs.c5_point(args.bits, args.block)
@@ -170,7 +175,7 @@ def workload(args):
 
 def stack_bytes(cfg, N, K, bias):
     w = N * K * cfg.bits // 8
-    sb = 2 if cfg.scale_dtype == "bf16" else 4
+    sb = {"bf16": 2, "f32": 4, "e8m0": 1}[cfg.scale_dtype]
     ab = 2 if cfg.act_dtype == "bf16" else 4
     s = N * (cfg.nblocks(K) if cfg.block_size else 1) * sb
     return w + s + (N * ab if bias else 0)

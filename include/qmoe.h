@@ -52,7 +52,15 @@ typedef enum {
   QMOE_ERR_DEVICE = 6        /* the HIP runtime reported an error */
 } qmoe_status;
 
-typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1 } qmoe_dtype;
+/* QMOE_E8M0: one unsigned byte e per scale, the power of two 2^(e - 127) (scale_dtype only).
+   E8M0 scales select the MX FP4 weight format (ClikaRT "QMoEWoQ" page: the module serves
+   block-quantized checkpoints such as MXFP4 gpt-oss): expert_weight_bits 4 and block_size
+   32, each 4-bit code an E2M1 value (sign, 2-bit exponent with bias 1, 1-bit mantissa:
+   magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with no zero point, dequant(q) = e2m1(q) * 2^(e-127);
+   bf16 activations and the tiled weight layout only (QMOE_ERR_UNSUPPORTED otherwise).
+   Scale bytes 0 and 255 (2^-127 and NaN) and products past the bf16 range are outside
+   the tested range. */
+typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1, QMOE_E8M0 = 2 } qmoe_dtype;
 
 /* Layout of the expert weight stacks (qmoe_params.weight_layout).
    QMOE_LAYOUT_ROWS: the pages' layout, uint8 [E, N, K*bits/8], row-major.
@@ -90,7 +98,7 @@ typedef struct {
      u' = clamp(u, -L, L). swiglu_limit <= 0 or +inf means no clamp. */
   float swiglu_alpha, swiglu_beta, swiglu_limit;
   int32_t act_dtype;    /* qmoe_dtype of x, router logits, biases, shared_output, output */
-  int32_t scale_dtype;  /* qmoe_dtype of the scales */
+  int32_t scale_dtype;  /* qmoe_dtype of the scales (QMOE_E8M0: MX FP4 weights, above) */
   /* Rows per expert tile of the grouping. 0 = the library's choice for these shapes
      (qmoe_tile_m). bf16 activations take 16, 32 or 128; fp32 activations 1 to 16 rows
      that fit the kernel's LDS. Every call of one forward must use the same value. */
@@ -126,7 +134,7 @@ typedef struct {
  *   stream, and for each j < S_K/32 the eight elements k = t*S_K + 32j + 8q + i, i < 8:
  *     4-bit: 32-bit word j (little-endian) holds element i in bits [4p, 4p+4) for
  *            p = (0, 4, 1, 5, 2, 6, 3, 7)[i], i.e. its nibbles hold elements
- *            (0, 2, 4, 6, 1, 3, 5, 7);
+ *            (0, 2, 4, 6, 1, 3, 5, 7); with E8M0 scales (MX FP4) p = i instead;
  *     8-bit: byte 8j + i holds element i.
  *   Elements past K and rows past the stream's end hold code 0 (their products meet
  *   zero activations or are never stored).

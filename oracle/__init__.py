@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qmoe_oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, E8M0 = 0, 1, 2
+_SDT = {"f32": F32, "bf16": BF16, "e8m0": E8M0}
 ACTS = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
 
 
@@ -84,7 +85,7 @@ def params(cfg, T: int) -> Params:
                   block_size=cfg.block_size, fusion=cfg.fusion,
                   activation=ACTS[cfg.activation], normalize=int(cfg.normalize),
                   act_dtype=F32 if cfg.act_dtype == "f32" else BF16,
-                  scale_dtype=F32 if cfg.scale_dtype == "f32" else BF16, pad_=0,
+                  scale_dtype=_SDT[cfg.scale_dtype], pad_=0,
                   alpha=cfg.alpha, beta=cfg.beta, limit=lim)
 
 

@@ -16,6 +16,9 @@
  *    first, equal values in ascending expert index; slots keep that order;
  *  - a 4-bit byte holds element 2j in its low nibble and 2j+1 in its high nibble;
  *  - dequant(q) = (q - 2^(bits-1)) * scale, q the unsigned field;
+ *  - MX FP4 (E8M0 scales; ClikaRT "QMoEWoQ" page: MXFP4 gpt-oss checkpoints, format
+ *    from the OCP Microscaling specification): dequant(q) = e2m1(q) * 2^(e - 127), no
+ *    zero point, one scale byte e per 32 k;
  *  - block_size 0: one scale per output row; otherwise scale index floor(k/bs),
  *    with a shorter last block when bs does not divide K;
  *  - interleaved fusion: row 2i is gate, 2i+1 is up; concatenated: rows [0,I)
@@ -39,6 +42,10 @@
 /* ---- exact widening of stored elements --------------------------------- */
 
 static double widen(const void* base, int32_t dtype, int64_t i) {
+  if (dtype == ORACLE_E8M0) {  // a power of two 2^(e - 127); 255 is not a number
+    const uint8_t e = static_cast<const uint8_t*>(base)[i];
+    return e == 255 ? NAN : std::ldexp(1.0, static_cast<int>(e) - 127);
+  }
   if (dtype == ORACLE_F32) {
     float f;
     std::memcpy(&f, static_cast<const char*>(base) + 4 * i, 4);
@@ -170,8 +177,20 @@ static int32_t qfield(const oracle_params* p, const uint8_t* w, int64_t N, int64
   return (kk % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
 }
 
+/* E2M1: bit 3 the sign, bits 2..1 the exponent (bias 1), bit 0 the mantissa; exponent 0
+   is the subnormal range (0 and 0.5). The eight magnitudes as a table. */
+static double e2m1(int32_t q) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  return (q & 8) ? -mag[q & 7] : mag[q & 7];
+}
+
 double oracle_weight(const oracle_params* p, const oracle_stack* st, int64_t N, int64_t K,
                      int64_t e, int64_t n, int64_t kk) {
+  if (p->scale_dtype == ORACLE_E8M0) {
+    const int64_t nb = (K + p->block_size - 1) / p->block_size;
+    const double s = widen(st->s, ORACLE_E8M0, (e * N + n) * nb + kk / p->block_size);
+    return e2m1(qfield(p, st->w, N, K, e, n, kk)) * s;
+  }
   const int32_t zero = 1 << (p->bits - 1);
   double s;
   if (p->block_size == 0) {

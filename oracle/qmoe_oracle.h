@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E8M0 = 2 /* scales only: 2^(e-127), MX FP4 codes */ };
 enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_IDENTITY = 1, ORACLE_ACT_RELU = 2, ORACLE_ACT_SILU = 3 };
 
 typedef struct {
@@ -43,7 +43,7 @@ typedef struct {
   int32_t activation;    /* ORACLE_ACT_* */
   int32_t normalize;     /* renormalise the k routing weights */
   int32_t act_dtype;     /* ORACLE_F32 / ORACLE_BF16: x, logits, biases, shared, out */
-  int32_t scale_dtype;   /* ORACLE_F32 / ORACLE_BF16 */
+  int32_t scale_dtype;   /* ORACLE_F32 / ORACLE_BF16 / ORACLE_E8M0 (MX FP4 weights) */
   int32_t pad_;
   double alpha, beta, limit; /* limit = +inf: no clamp */
 } oracle_params;

@@ -116,6 +116,13 @@ LIN_PREFILL = Config(name="lin-prefill-int4", T_points=(4096,), H=4096, I=14336,
                      fc2_bias=False, activation="identity")
 LINEAR = {"lin-decode": LIN_DECODE, "lin-prefill": LIN_PREFILL}
 
+# MX FP4 weights (E2M1 codes, one E8M0 scale per 32 k: the gpt-oss checkpoint format the
+# ClikaRT QMoEWoQ page names), on the c2 decode layer and the c5 sweep shape. Scales are
+# the powers of two nearest to U(scale_lo, scale_hi) in log2 (2^-8 .. 2^-6 here).
+C2_MX = C2.with_(name="c2-decode-mxfp4", scale_dtype="e8m0")
+C5_MX = C5.with_(name="c5-sweep-mxfp4", bits=4, block_size=32, scale_dtype="e8m0")
+MX = {"c2-mx": C2_MX, "c5-mx": C5_MX}
+
 C5_BITS = (4, 8)
 C5_BLOCKS = (16, 32, 64, 128)
 

@@ -44,6 +44,11 @@ def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
 
 
 def store(values_f64: np.ndarray, dtype: str) -> np.ndarray:
+    """Values in a storage type: f32, bf16 bits (RNE), or e8m0 (scales only: the byte e of
+    the power of two 2^(e - 127) nearest to the value in log2, e in [1, 254])."""
+    if dtype == "e8m0":
+        e = np.rint(np.log2(np.asarray(values_f64, dtype=np.float64))) + 127
+        return np.clip(e, 1, 254).astype(np.uint8)
     v32 = np.asarray(values_f64, dtype=np.float32)
     if dtype == "f32":
         return v32
@@ -53,7 +58,9 @@ def store(values_f64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def as_f32(a: np.ndarray, dtype: str) -> np.ndarray:
-    """View stored values as float32 (exact for both storage types)."""
+    """View stored values as float32 (exact for every storage type)."""
+    if dtype == "e8m0":
+        return np.ldexp(np.float32(1.0), np.asarray(a, dtype=np.int32) - 127).astype(np.float32)
     return bf16_bits_to_f32(a) if dtype == "bf16" else np.asarray(a, dtype=np.float32)
 
 

@@ -24,6 +24,16 @@ from scipy.special import expit
 from synth.gen import as_f32
 
 
+def e2m1_bits(q: np.ndarray) -> np.ndarray:
+    """E2M1 values from their bit fields (OCP MX FP4): sign bit 3, exponent bits 2..1 with
+    bias 1, mantissa bit 0; exponent 0 is subnormal (0.5 * mantissa)."""
+    sign = np.where((q >> 3) & 1, -1.0, 1.0)
+    ex = (q >> 1) & 3
+    m = (q & 1).astype(np.float64)
+    mag = np.where(ex == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, ex - 1))
+    return sign * mag
+
+
 def dequant_dense(w: np.ndarray, s: np.ndarray, cfg, N: int, K: int) -> np.ndarray:
     E = w.shape[0]
     if cfg.bits == 4:
@@ -32,6 +42,10 @@ def dequant_dense(w: np.ndarray, s: np.ndarray, cfg, N: int, K: int) -> np.ndarr
         q = np.stack([lo, hi], axis=-1).reshape(E, N, K)
     else:
         q = w.astype(np.int64)
+    if cfg.scale_dtype == "e8m0":
+        # MX FP4: no zero point, a power-of-two scale per block of 32
+        scale = np.ldexp(1.0, np.repeat(s.astype(np.int64) - 127, cfg.block_size, axis=2)[:, :, :K])
+        return e2m1_bits(q) * scale
     sf = as_f32(s, cfg.scale_dtype).astype(np.float64)
     if cfg.block_size == 0:
         scale = np.broadcast_to(sf[:, :, None], (E, N, K))

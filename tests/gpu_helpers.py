@@ -31,6 +31,8 @@ def host_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 
 def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str = "rows"):
+    if cfg.scale_dtype == "e8m0":
+        layout = "tiles"  # MX FP4 weights run in the tiled layout only
     return qm.make_params(T, cfg.H, cfg.I, cfg.E, cfg.k, expert_weight_bits=cfg.bits,
                           block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
                           activation=cfg.activation, normalize_routing_weights=cfg.normalize,

@@ -241,3 +241,21 @@ def test_linear_woq_host_checks(lib):
     assert lib.qmoe_tile_m(qm.linear_params(300, 256, 128)) == 32
     assert lib.qmoe_tile_m(qm.linear_params(37, 256, 128)) == 32
     assert lib.qmoe_tile_m(qm.linear_params(5, 256, 128)) == 16
+
+
+def test_mxfp4_params(lib):
+    """E8M0 scales select MX FP4 weights: 4-bit, blocks of 32, bf16 activations, tiled
+    layout; the packing accepts the parameters whatever their layout."""
+    mx = dict(scale_dtype="e8m0", block_size=32, weight_layout="tiles")
+    assert status(good(**mx)) == _lib.QMOE_OK
+    assert status(good(**dict(mx, expert_weight_bits=8))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mx, block_size=16))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mx, block_size=0))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mx, weight_layout="rows"))) == _lib.QMOE_ERR_UNSUPPORTED
+    assert status(good(**dict(mx, act_dtype="f32"))) == _lib.QMOE_ERR_UNSUPPORTED
+    rows = good(**dict(mx, weight_layout="rows"))
+    tiles = good(**mx)
+    assert lib.qmoe_packed_stack_size(rows, _lib.QMOE_FC1) == lib.qmoe_packed_stack_size(tiles, _lib.QMOE_FC1) > 0
+    p = good(**mx)
+    p.scale_dtype = 3
+    assert status(p) == _lib.QMOE_ERR_DTYPE

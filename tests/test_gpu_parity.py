@@ -162,6 +162,11 @@ STAGE_CFGS = {
                                         block_size=512, H=1152, I=544, E=4),
     "f32-interleaved-b8-bias": configs.tiny(fusion=1, bits=8, H=96, I=80, block_size=32,
                                             fc1_bias=True, fc2_bias=True, limit=3.0),
+    # MX FP4 (E2M1 codes, E8M0 scales per 32 k; tiled layout only)
+    "mxfp4-interleaved-bias-clamp": configs.C2_MX.with_(H=512, I=288, E=8),
+    "mxfp4-separate-silu": configs.tiny(activation="silu", fusion=0, act_dtype="bf16",
+                                        scale_dtype="e8m0", bits=4, block_size=32, H=352,
+                                        I=160, fc1_bias=True, scale_lo=0.01, scale_hi=0.1),
 }
 
 
@@ -199,15 +204,24 @@ TILE128_CFGS = {
     "identity-b4-perrow-bias": configs.tiny(activation="identity", fusion=0, act_dtype="bf16",
                                             scale_dtype="bf16", block_size=0, H=256, I=192,
                                             E=4, fc1_bias=True, fc2_bias=True),
+    "mxfp4-concat-raggedK": configs.C5_MX.with_(H=544, I=224, E=8),
 }
 
 # every case in the rows layout at the library's tile height; the bf16 cases at both
 # weight-streaming tile heights (16 rows, and 32 rows of two MFMA row blocks) and in both
 # weight layouts (the tiled one from qmoe_pack_stack); the 128-row cases in both layouts
 _BF16_STAGE = [n for n in sorted(STAGE_CFGS) if STAGE_CFGS[n].act_dtype == "bf16"]
-STAGE_CASES = ([(n, 0, "rows") for n in sorted(STAGE_CFGS)] +
-               [(n, m, lay) for n in _BF16_STAGE for m in (16, 32) for lay in ("rows", "tiles")] +
-               [(n, 128, lay) for n in sorted(TILE128_CFGS) for lay in ("rows", "tiles")])
+
+
+def _layouts(cfg):
+    """MX FP4 weights run in the tiled layout only."""
+    return ("tiles",) if cfg.scale_dtype == "e8m0" else ("rows", "tiles")
+
+
+STAGE_CASES = ([(n, 0, "rows") for n in sorted(STAGE_CFGS) if "rows" in _layouts(STAGE_CFGS[n])] +
+               [(n, m, lay) for n in _BF16_STAGE for m in (16, 32)
+                for lay in _layouts(STAGE_CFGS[n])] +
+               [(n, 128, lay) for n in sorted(TILE128_CFGS) for lay in _layouts(TILE128_CFGS[n])])
 
 
 def stage_cfg(name, tile_m):
@@ -417,6 +431,16 @@ def test_forward_tiled_c4_many_experts_sampled():
 @pytest.mark.parametrize("T", [256, 4096])
 def test_forward_tiled_c5_sweep(T, bs, bits):
     check_forward(configs.c5_point(bits, bs), T, sample=6, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_forward_mxfp4_c2_decode(T):
+    check_forward(configs.C2_MX, T, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [1, 256, 4096])
+def test_forward_mxfp4_c5_sampled(T):
+    check_forward(configs.C5_MX, T, sample=6, layout="tiles")
 
 
 def test_forward_deterministic_and_3d_input():

@@ -53,3 +53,20 @@ def test_pack_matches_reference(bits, which, fusion, act, H, I, E):
     want = tr.pack(w, which, H, I, bits, fusion, swiglu=act == "swiglu")
     assert got.shape == want.shape
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("which,fusion,H,I,E", [("fc1", 1, 2880, 2880, 2), ("fc1", 2, 160, 64, 3),
+                                               ("fc2", 0, 96, 352, 2)])
+def test_pack_mxfp4_keeps_code_order(which, fusion, H, I, E):
+    # MX FP4 (E8M0 scales): element i of a word in nibble i, the order of the scaled FP4
+    # conversions; the params may name either layout (the packing reads only the shapes)
+    p = qm.make_params(4, H, I, E, 1, expert_weight_bits=4, block_size=32, swiglu_fusion=fusion,
+                       act_dtype="bf16", scale_dtype="e8m0", weight_layout="rows")
+    K, N, S, R, _ = tr.stack_geometry(which, H, I, 4, fusion)
+    rng = np.random.default_rng(H + I + E)
+    w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    print("pack mxfp4", which, fusion, H, I, E, flush=True)
+    got = host(qm.pack_stack(p, which, dev(w)))
+    torch.cuda.synchronize()
+    want = tr.pack(w, which, H, I, 4, fusion, natural=True)
+    assert np.array_equal(got, want)

@@ -47,6 +47,10 @@ BRUTE_CASES = {
     "f32-no-renorm-E6k3": configs.tiny(normalize=False, E=6, k=3, logit_sigma=2.0),
     "bf16-fscale-b8-bs64": configs.tiny(act_dtype="bf16", scale_dtype="f32", bits=8,
                                         block_size=64, H=128, I=64),
+    "bf16-mxfp4-interleaved-bias": configs.tiny(act_dtype="bf16", scale_dtype="e8m0", bits=4,
+                                                block_size=32, H=96, I=64, fusion=1,
+                                                fc1_bias=True, fc2_bias=True, limit=7.0,
+                                                scale_lo=0.01, scale_hi=0.2),
 }
 
 
@@ -254,6 +258,27 @@ def test_linear_is_dense_dequant_matmul(bits, bs, act, sdt):
     assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
     # a row subset evaluates the same rows
     assert np.array_equal(oracle.linear(cfg, inp, rows=[6, 2]), got[[6, 2]])
+
+
+def test_mxfp4_weights_are_e2m1_times_power_of_two():
+    # every E2M1 code under three E8M0 scale bytes: the oracle's dequant against the
+    # format's bit fields (bruteforce.e2m1_bits) and torch's own E8M0 conversion; spot
+    # values 0, 0.5, 6 and the negative zero
+    cfg = configs.tiny(E=1, k=1, fusion=0, activation="identity", act_dtype="bf16",
+                       scale_dtype="e8m0", bits=4, block_size=32, H=96, I=16)
+    codes = np.arange(96) % 16
+    w = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    w = np.broadcast_to(w, (1, 16, 48)).copy()
+    ebytes = np.array([127, 120, 131], np.uint8)
+    s = np.broadcast_to(ebytes, (1, 16, 3)).copy()
+    st = oracle.Stack(w=w.ctypes.data, s=s.ctypes.data, b=None)
+    got = np.array([oracle.weight(cfg, st, 16, 96, 0, 5, k) for k in range(96)])
+    scale = torch.from_numpy(ebytes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    want = bruteforce.e2m1_bits(codes) * np.repeat(scale, 32)
+    assert np.array_equal(got, want)
+    assert got[0] == 0.0 and got[1] == 0.5 and got[7] == 6.0 and got[15] == -6.0
+    assert got[8] == 0.0 and math.copysign(1.0, got[8]) == -1.0
+    assert np.all(np.abs(got[:8]) == np.abs(got[8:16]))
 
 
 def test_swiglu_clamp_reading():

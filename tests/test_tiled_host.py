@@ -110,3 +110,18 @@ def test_layout_validation():
     f32 = _params(weight_layout="tiles", act_dtype="f32", scale_dtype="f32",
                   hidden_size=128, inter_size=64)
     assert _lib.load().qmoe_validate(f32) == _lib.QMOE_ERR_UNSUPPORTED
+
+
+def test_natural_order_roundtrip_and_differs():
+    # the MX FP4 tile order (nibble i = element i) unpacks back to the same codes and, for
+    # a word of distinct codes, differs from the decode order
+    rng = np.random.default_rng(5)
+    w = rng.integers(0, 256, size=(2, 64, 80), dtype=np.uint8)  # fc2 of H=64, I=160
+    nat = tr.pack(w, "fc2", 64, 160, 4, 0, natural=True)
+    dec = tr.pack(w, "fc2", 64, 160, 4, 0)
+    assert not np.array_equal(nat, dec)
+    back = tr.unpack(nat, 2, "fc2", 64, 160, 4, 0, natural=True)
+    assert np.array_equal(back, tr.codes_of(w, 160, 4))
+    # lane 0, word 0 of the first tile: row 0's elements 0..7 in nibbles 0..7, i.e. the
+    # row's first four bytes unchanged
+    assert np.array_equal(nat[:4], w[0, 0, :4])

@@ -34,7 +34,8 @@ def codes_of(rows_stack: np.ndarray, K: int, bits: int) -> np.ndarray:
 
 
 def pack(rows_stack: np.ndarray, which: str, H: int, I: int, bits: int, fusion: int,
-         swiglu: bool = True) -> np.ndarray:
+         swiglu: bool = True, natural: bool = False) -> np.ndarray:
+    """natural: 4-bit element i in nibble i (the MX FP4 order) instead of NIBBLE_OF[i]."""
     K, N, S, R, fu = stack_geometry(which, H, I, bits, fusion, swiglu)
     E = rows_stack.shape[0]
     assert rows_stack.shape == (E, N, K * bits // 8)
@@ -62,7 +63,7 @@ def pack(rows_stack: np.ndarray, which: str, H: int, I: int, bits: int, fusion: 
                 if bits == 4:
                     word = np.zeros(el.shape[:-1], np.uint32)
                     for i in range(8):
-                        word |= el[..., i].astype(np.uint32) << np.uint32(4 * NIBBLE_OF[i])
+                        word |= el[..., i].astype(np.uint32) << np.uint32(4 * (i if natural else NIBBLE_OF[i]))
                     # the word's little-endian bytes
                     out[:, :, :, :, l, 4 * j:4 * j + 4] = np.stack(
                         [(word >> np.uint32(8 * c)) & np.uint32(0xFF) for c in range(4)],
@@ -73,7 +74,7 @@ def pack(rows_stack: np.ndarray, which: str, H: int, I: int, bits: int, fusion: 
 
 
 def unpack(packed: np.ndarray, E: int, which: str, H: int, I: int, bits: int, fusion: int,
-           swiglu: bool = True) -> np.ndarray:
+           swiglu: bool = True, natural: bool = False) -> np.ndarray:
     """Codes [E, N, K] of the rows-layout stack, read back tile by tile, lane by lane."""
     K, N, S, R, fu = stack_geometry(which, H, I, bits, fusion, swiglu)
     ssk = 128 if bits == 4 else 64
@@ -86,7 +87,7 @@ def unpack(packed: np.ndarray, E: int, which: str, H: int, I: int, bits: int, fu
             for i in range(8):
                 k = np.arange(KT) * ssk + 32 * j + 8 * q + i
                 if bits == 4:
-                    p = NIBBLE_OF[i]
+                    p = i if natural else NIBBLE_OF[i]
                     byte = t[:, :, :, :, l, 4 * j + p // 2]
                     v = (byte >> 4) if (p % 2) else (byte & 0x0F)
                 else:

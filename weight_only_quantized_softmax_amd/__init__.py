@@ -13,7 +13,7 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (ACT, QMOE_BF16, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SHAPE,
+from ._lib import (ACT, QMOE_BF16, QMOE_E8M0, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SHAPE,
                    QMOE_ERR_UNBOUND, QMOE_F32, QMOE_FC1, QMOE_FC2, QMOE_FC3, QMOE_LAYOUT_ROWS,
                    QMOE_LAYOUT_TILES, QmoeError, QmoeParams, QmoeStack, check, load)
 
@@ -24,7 +24,7 @@ __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe
            "qmoe_time_next_gemm", "qmoe_linear_woq", "linear_params", "linear_woq", "forward",
            "QmoeError", "QmoeParams"]
 
-_DT = {"f32": QMOE_F32, "bf16": QMOE_BF16}
+_DT = {"f32": QMOE_F32, "bf16": QMOE_BF16, "e8m0": QMOE_E8M0}
 _LAYOUT = {"rows": QMOE_LAYOUT_ROWS, "tiles": QMOE_LAYOUT_TILES}
 _WHICH = {"fc1": QMOE_FC1, "fc2": QMOE_FC2, "fc3": QMOE_FC3}
 _TORCH_DT = {QMOE_F32: torch.float32, QMOE_BF16: torch.bfloat16}

@@ -12,7 +12,7 @@ QMOE_ERR_UNSUPPORTED, QMOE_ERR_UNBOUND, QMOE_ERR_DEVICE = 4, 5, 6
 STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "UNBOUND",
                 6: "DEVICE"}
 
-QMOE_F32, QMOE_BF16 = 0, 1
+QMOE_F32, QMOE_BF16, QMOE_E8M0 = 0, 1, 2
 QMOE_LAYOUT_ROWS, QMOE_LAYOUT_TILES = 0, 1
 QMOE_FC1, QMOE_FC2, QMOE_FC3 = 1, 2, 3
 ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}

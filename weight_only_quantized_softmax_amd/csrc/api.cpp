@@ -112,8 +112,16 @@ qmoe_status validate(const qmoe_params* p) {
     return fail(QMOE_ERR_INVALID, "swiglu_fusion must be 0 unless the activation is swiglu");
   if (p->act_dtype != QMOE_F32 && p->act_dtype != QMOE_BF16)
     return fail(QMOE_ERR_DTYPE, "act_dtype %d unknown", p->act_dtype);
-  if (p->scale_dtype != QMOE_F32 && p->scale_dtype != QMOE_BF16)
+  if (p->scale_dtype != QMOE_F32 && p->scale_dtype != QMOE_BF16 && p->scale_dtype != QMOE_E8M0)
     return fail(QMOE_ERR_DTYPE, "scale_dtype %d unknown", p->scale_dtype);
+  if (p->scale_dtype == QMOE_E8M0) {
+    // MX FP4: E2M1 codes, one E8M0 scale per 32 k
+    if (p->expert_weight_bits != 4 || p->block_size != 32)
+      return fail(QMOE_ERR_INVALID, "E8M0 scales (MX FP4) need expert_weight_bits 4 and block_size 32");
+    if (p->act_dtype != QMOE_BF16 || p->weight_layout != QMOE_LAYOUT_TILES)
+      return fail(QMOE_ERR_UNSUPPORTED,
+                  "MX FP4 weights run with bf16 activations in the tiled layout (qmoe_pack_stack)");
+  }
   if (p->weight_layout != QMOE_LAYOUT_ROWS && p->weight_layout != QMOE_LAYOUT_TILES)
     return fail(QMOE_ERR_INVALID, "weight_layout %d unknown", p->weight_layout);
   if (p->weight_layout == QMOE_LAYOUT_TILES && p->act_dtype != QMOE_BF16)
@@ -142,7 +150,7 @@ qmoe_status validate(const qmoe_params* p) {
       return fail(QMOE_ERR_UNSUPPORTED, "bf16 path: a tensor or one expert's stack reaches 2 GiB");
     if (p->block_size) {
       const int64_t nb = (kmax + p->block_size - 1) / p->block_size;
-      const int64_t sbytes = p->scale_dtype == QMOE_BF16 ? 2 : 4;
+      const int64_t sbytes = p->scale_dtype == QMOE_BF16 ? 2 : (p->scale_dtype == QMOE_E8M0 ? 1 : 4);
       if (2 * 64 * nb * sbytes > 64 * 1024)
         return fail(QMOE_ERR_UNSUPPORTED, "bf16 path: %lld scales per row do not fit in LDS",
                     (long long)nb);
@@ -154,6 +162,17 @@ qmoe_status validate(const qmoe_params* p) {
                   (long long)kmax);
   }
   return ok();
+}
+
+// The packing ignores weight_layout; MX FP4 parameters are checked as they will be used
+// (tiled layout).
+qmoe_status validate_for_pack(const qmoe_params* p) {
+  if (p && p->scale_dtype == QMOE_E8M0) {
+    qmoe_params q = *p;
+    q.weight_layout = QMOE_LAYOUT_TILES;
+    return validate(&q);
+  }
+  return validate(p);
 }
 
 int64_t max_tiles_of(const qmoe_params* p) {
@@ -232,6 +251,7 @@ bool pack_args(const qmoe_params* p, int32_t which, qmoe::PackArgs& a) {
     return false;
   }
   const int ssk = p->expert_weight_bits == 4 ? 128 : 64;
+  a.natural = p->scale_dtype == QMOE_E8M0;
   a.NB = (a.rows + 15) / 16;
   a.KT = (a.K + ssk - 1) / ssk;
   return true;
@@ -255,6 +275,7 @@ qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   g.inter = static_cast<int>(p->inter_size);
   g.M = tile_m_of(p);
   g.packed = p->weight_layout == QMOE_LAYOUT_TILES;
+  g.mx = p->scale_dtype == QMOE_E8M0;
   return g;
 }
 
@@ -520,7 +541,7 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
 }
 
 size_t qmoe_packed_stack_size(const qmoe_params* p, int32_t which) {
-  if (validate(p) != QMOE_OK) return 0;
+  if (validate_for_pack(p) != QMOE_OK) return 0;
   qmoe::PackArgs a{};
   if (!pack_args(p, which, a)) return 0;
   return packed_bytes(a);
@@ -528,7 +549,7 @@ size_t qmoe_packed_stack_size(const qmoe_params* p, int32_t which) {
 
 qmoe_status qmoe_pack_stack(const qmoe_params* p, int32_t which, const void* weights,
                             void* packed, void* stream) {
-  QMOE_TRY(validate(p));
+  QMOE_TRY(validate_for_pack(p));
   qmoe::PackArgs a{};
   if (!pack_args(p, which, a))
     return fail(QMOE_ERR_INVALID, "stack %d does not exist for these parameters", which);

@@ -21,6 +21,8 @@
 // group ends. Per-row scales multiply the finished sum.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "gemm_gemv_kernel.h"
@@ -61,6 +63,10 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
   static_assert(PD >= 2 && PD <= 4, "prefetch distance 2 to 4");
   constexpr int TM = MR * kM;                   // rows of a tile: MR MFMA row blocks of 16
   constexpr bool PERROW = BS == 0;
+  // MX FP4 (E8M0 scale bytes): each code is scaled as it is converted, so the MFMAs
+  // accumulate the whole K with no correction term and no per-block scaling
+  constexpr bool MX = std::is_same<ST, uint8_t>::value;
+  static_assert(!MX || (BITS == 4 && BS == 32 && PK), "MX FP4: 4-bit, blocks of 32, tiled layout");
   constexpr int SSK0 = BITS == 4 ? 128 : 64;
   // KORD: MFMA j of a super-step takes the 32 consecutive k [32j, 32j + 32) (tiled layout,
   // or 4-bit rows with blocks shorter than a super-step, by a cross-lane transpose)
@@ -308,6 +314,18 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
           if (BITS == 4 && !PK) xr = order_for_nibbles(xr);
           xa[mr] = __builtin_bit_cast(bf16x8, xr);
         }
+        if constexpr (MX) {
+          // this k-slice is one block: its scale byte, 32-k block (k0 >> 5) + 4u + j
+          const int blk = (k0 >> 5) + u * (SSK >> 5) + j;
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const bf16x8 bm = decode_mx(wv[st][j], scale_value<ST>(my_scl[st][blk]));
+#pragma unroll
+            for (int mr = 0; mr < MR; ++mr)
+              acc[mr][st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mr], bm, acc[mr][st][0], 0, 0, 0);
+          }
+          continue;
+        }
         bf16x8 bw[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -402,6 +420,14 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
       chunk(wr[r], stage(r), wr[(r + PD) % (PD + 1)], stage((r + PD) % (PD + 1)), ci + r);
   }
 
+  if (MX) {
+#pragma unroll
+    for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[mr][st][i] = acc[mr][st][0][i];
+  }
   if (PERROW) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -491,10 +517,10 @@ static int choose_split(const GemmArgs& g, int64_t wg_rows, int bits, int wave_c
   return sk;
 }
 
-// Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows.
-inline size_t gemm_bf16_lds(const GemmArgs& g, bool scale_bf16, int sk, int nw = kDecWaves) {
+// Dynamic LDS of the bf16 kernel: the scales of the workgroup's rows (scale_bytes each).
+inline size_t gemm_bf16_lds(const GemmArgs& g, int scale_bytes, int sk, int nw = kDecWaves) {
   if (g.bs == 0) return 0;
-  return static_cast<size_t>(2) * (nw / sk) * 16 * g.nb * (scale_bf16 ? 2 : 4);
+  return static_cast<size_t>(2) * (nw / sk) * 16 * g.nb * scale_bytes;
 }
 
 template <int BITS, typename ST, int MODE, int SK, bool PK, int NW, int MR, int PD = 2>
@@ -503,9 +529,12 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
   const int wg_cols = CPB * (MODE == kModeSwiglu ? 16 : 32);
   dim3 grid((g.ncols + wg_cols - 1) / wg_cols, static_cast<unsigned>(max_tiles * (g.M / (MR * kM)))),
       block(NW * 64);
-  const size_t lds = gemm_bf16_lds(g, sizeof(ST) == 2, SK, NW);
+  const size_t lds = gemm_bf16_lds(g, sizeof(ST), SK, NW);
 #define QMOE_DEC(BSV, SKV) \
   launch_gemm_kernel(gemm_bf16_tile_kernel<BITS, ST, MODE, BSV, SKV, PK, NW, MR, PD>, grid, block, lds, s, g)
+  if constexpr (std::is_same<ST, uint8_t>::value) {  // MX FP4: blocks of 32 only
+    QMOE_DEC(32, SK);
+  } else {
   switch (g.bs) {
     case 0: QMOE_DEC(0, SK); break;
     case 16: QMOE_DEC(16, SK); break;
@@ -514,6 +543,7 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
     case 128: QMOE_DEC(128, SK); break;
     case 256: QMOE_DEC(256, 1); break;
     default: QMOE_DEC(512, 1); break;
+  }
   }
 #undef QMOE_DEC
   return hipGetLastError();
@@ -524,12 +554,12 @@ static hipError_t launch_sk(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 // least two such workgroups, with split-K of at most 2 and the scales of two workgroups
 // within the CU's LDS. (8-bit stacks run slower with eight waves.)
 template <int BITS, int MODE, int MR>
-static bool use_eight_waves(const GemmArgs& g, int64_t wg_rows, int sk, bool scale_bf16) {
+static bool use_eight_waves(const GemmArgs& g, int64_t wg_rows, int sk, int scale_bytes) {
   constexpr int kCUs = 256;
   if (BITS != 4 || !g.packed || sk > 2) return false;
   const int wg_cols = (8 / sk) * (MODE == kModeSwiglu ? 16 : 32);
   const int64_t wgs = wg_rows * ((g.ncols + wg_cols - 1) / wg_cols);
-  const size_t lds = gemm_bf16_lds(g, scale_bf16, sk, 8) + 3 * MR * kM * 256 * 2;
+  const size_t lds = gemm_bf16_lds(g, scale_bytes, sk, 8) + 3 * MR * kM * 256 * 2;
   return wgs >= 2 * kCUs && 2 * lds <= 160 * 1024;
 }
 
@@ -550,7 +580,7 @@ static hipError_t launch_bmode_m(const GemmArgs& g, int64_t max_tiles, hipStream
   const int64_t wg_rows = max_tiles * (g.M / (MR * kM));  // workgroup rows of the grid
   const int sk = choose_split(g, wg_rows, BITS, MODE == kModeSwiglu ? 16 : 32);
   if constexpr (PK && BITS == 4) {
-    if (use_eight_waves<BITS, MODE, MR>(g, wg_rows, sk, sizeof(ST) == 2)) {
+    if (use_eight_waves<BITS, MODE, MR>(g, wg_rows, sk, sizeof(ST))) {
       if (sk == 1) return launch_sk<BITS, ST, MODE, 1, PK, 8, MR>(g, max_tiles, s);
       return launch_sk<BITS, ST, MODE, 2, PK, 8, MR>(g, max_tiles, s);
     }
@@ -589,6 +619,9 @@ template <bool PK>
 static hipError_t launch_gemm_bf16_layout(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                           int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
+  if constexpr (PK) {
+    if (g.mx) return launch_mode<4, uint8_t, PK>(g, mode, max_tiles, s);
+  }
   if (bits == 4)
     return scale_bf16 ? launch_mode<4, uint16_t, PK>(g, mode, max_tiles, s)
                       : launch_mode<4, float, PK>(g, mode, max_tiles, s);

@@ -111,6 +111,26 @@ template <>
 __device__ __forceinline__ float scale_value<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
 template <>
 __device__ __forceinline__ float scale_value<float>(float v) { return v; }
+// E8M0 (MX) scale byte e: 2^(e - 127) as the float whose exponent field is e (the MX
+// conversions read only the exponent of their scale operand)
+template <>
+__device__ __forceinline__ float scale_value<uint8_t>(uint8_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 23);
+}
+
+// Eight E2M1 (MX FP4) codes of a word, natural order (code i in bits [4i, 4i+4)), times a
+// power-of-two scale, to eight bf16: gfx950's scaled conversion takes one byte (two
+// codes, the low nibble first) per instruction; the products are exact in bf16.
+__device__ __forceinline__ bf16x8 decode_mx(uint32_t w, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  const u32x4 r = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 // 4x4 transpose of 32-bit words across the four 16-lane rows of a wave: afterwards word j
 // of row r holds what word r of row j held. gfx950 permlane32_swap exchanges the upper half

@@ -17,6 +17,8 @@
 // group's fp32 sum, and each group's sum is scaled once (per-row scales once at the end).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -26,6 +28,8 @@ namespace qmoe {
 template <int BITS, typename ST, int MODE, int BS, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
   constexpr bool PERROW = BS == 0;
+  constexpr bool MX = std::is_same<ST, uint8_t>::value;  // MX FP4: scaled as converted
+  static_assert(!MX || (BITS == 4 && BS == 32), "MX FP4: 4-bit, blocks of 32");
   constexpr int SSK = BITS == 4 ? 128 : 64;  // K per weight tile
   constexpr int MPS = SSK / 32;              // MFMAs per tile
   constexpr bool XPOSE = BS > 0 && BS < SSK; // several scale groups inside one tile
@@ -165,6 +169,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
       const int kj = ksu + 32 * j;
       if (kj >= K) break;
       const bf16x8 xa = __builtin_bit_cast(bf16x8, sl.x[j]);
+      if constexpr (MX) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const bf16x8 bm = decode_mx(sl.w[st][j], scale_value<ST>(my_scl[st][kj >> 5]));
+          acc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bm, acc[st][0], 0, 0, 0);
+        }
+        continue;
+      }
       bf16x8 bw[NS];
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -222,6 +234,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
     }
   }
 
+  if (MX) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[st][i] = acc[st][0][i];
+  }
   if (PERROW) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -286,8 +304,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
 }
 
 // Dynamic LDS: the group's scales (32 rows), then the partial sums of NW - 1 K ranges.
-inline size_t gemm_gemv_lds(const GemmArgs& g, bool scale_bf16, int nw) {
-  const size_t scales = g.bs == 0 ? 0 : (32 * static_cast<size_t>(g.nb) * (scale_bf16 ? 2 : 4) + 15) / 16 * 16;
+inline size_t gemm_gemv_lds(const GemmArgs& g, int scale_bytes, int nw) {
+  const size_t scales = g.bs == 0 ? 0 : (32 * static_cast<size_t>(g.nb) * scale_bytes + 15) / 16 * 16;
   return scales + static_cast<size_t>(nw - 1) * 2 * 4 * 64 * 4;
 }
 
@@ -295,9 +313,12 @@ template <int BITS, typename ST, int MODE, int NW, int PD>
 static hipError_t launch_gemv(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   constexpr int CW = MODE == kModeSwiglu ? 16 : 32;
   dim3 grid((g.ncols + CW - 1) / CW, static_cast<unsigned>(max_tiles)), block(NW * 64);
-  const size_t lds = gemm_gemv_lds(g, sizeof(ST) == 2, NW);
+  const size_t lds = gemm_gemv_lds(g, sizeof(ST), NW);
 #define QMOE_GEMV(BSV) \
   launch_gemm_kernel(gemm_bf16_gemv_kernel<BITS, ST, MODE, BSV, NW, PD>, grid, block, lds, s, g)
+  if constexpr (std::is_same<ST, uint8_t>::value) {  // MX FP4: blocks of 32 only
+    QMOE_GEMV(32);
+  } else {
   switch (g.bs) {
     case 0: QMOE_GEMV(0); break;
     case 16: QMOE_GEMV(16); break;
@@ -306,6 +327,7 @@ static hipError_t launch_gemv(const GemmArgs& g, int64_t max_tiles, hipStream_t 
     case 128: QMOE_GEMV(128); break;
     case 256: QMOE_GEMV(256); break;
     default: QMOE_GEMV(512); break;
+  }
   }
 #undef QMOE_GEMV
   return hipGetLastError();

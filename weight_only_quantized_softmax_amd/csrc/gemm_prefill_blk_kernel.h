@@ -25,6 +25,8 @@
 //     joins each slice's accumulator when the group ends.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -68,6 +70,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   constexpr bool PF = SINGLE || BS == SSK;
   constexpr uint32_t kNegCorr = BITS == 4 ? 0xC308C308u : 0xC300C300u;  // -(c+z) bf16 pair
   static_assert(PK || BITS == 4 || BS >= 64, "8-bit rows-layout blocks shorter than 64 take the other kernel");
+  // MX FP4 (E8M0 scale bytes): codes scaled as they are converted, products accumulated
+  // straight into the totals
+  constexpr bool MX = std::is_same<ST, uint8_t>::value;
+  static_assert(!MX || (BITS == 4 && BS == 32 && PK), "MX FP4: 4-bit, blocks of 32, tiled layout");
 
   __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
@@ -281,7 +287,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
         for (int mt = 0; mt < 4; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
       }
       const int kj = s * SSK + 32 * j;
-      if constexpr (SINGLE) {
+      if constexpr (MX) {
+        // k-slice j is block j of the step
+        bf16x8 bm[kBNB];
+#pragma unroll
+        for (int b = 0; b < kBNB; ++b)
+          bm[b] = decode_mx(w[b][j], scale_value<ST>(sc[(wn * 64 + b * 16 + n) * NBLK + j]));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8 xb = __builtin_bit_cast(bf16x8, xa[mt]);
+#pragma unroll
+          for (int b = 0; b < kBNB; ++b)
+            tot[mt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, bm[b], tot[mt][b], 0, 0, 0);
+        }
+      } else if constexpr (SINGLE) {
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
           const bool mine = (G == 1) || (lgrp2 == gg);
@@ -429,6 +448,9 @@ static hipError_t launch_blk_bs(const GemmArgs& g, int64_t max_tiles, hipStream_
 
 template <int BITS, typename ST, int MODE, bool PK>
 static hipError_t launch_blk_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  if constexpr (std::is_same<ST, uint8_t>::value) {  // MX FP4: blocks of 32 only
+    return launch_blk_bs<BITS, ST, MODE, 32, PK>(g, max_tiles, s);
+  } else {
   // 8-bit rows-layout blocks shorter than 64 are not served here (prefill_blk_supports)
   constexpr bool kShort = PK || BITS == 4;
   switch (g.bs) {
@@ -440,6 +462,7 @@ static hipError_t launch_blk_mode(const GemmArgs& g, int64_t max_tiles, hipStrea
     default: return launch_blk_bs<BITS, ST, MODE, 512, PK>(g, max_tiles, s);
   }
   return hipErrorInvalidValue;
+  }
 }
 
 template <int BITS, typename ST, bool PK>
@@ -453,6 +476,9 @@ template <bool PK>
 static hipError_t launch_blk_layout(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                     int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
+  if constexpr (PK) {
+    if (g.mx) return launch_blk_t<4, uint8_t, PK>(g, mode, max_tiles, s);
+  }
   if (bits == 4)
     return scale_bf16 ? launch_blk_t<4, uint16_t, PK>(g, mode, max_tiles, s)
                       : launch_blk_t<4, float, PK>(g, mode, max_tiles, s);

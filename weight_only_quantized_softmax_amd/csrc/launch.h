@@ -49,6 +49,9 @@ struct GemmArgs {
   // single-expert linear layer: the rows of a are the output rows, in consecutive tiles
   // of M rows (no tile list, no gather), and rows past a_rows are never stored
   int linear;
+  // MX FP4 weights: E2M1 codes with one E8M0 scale byte per 32 k (tiled layout, natural
+  // nibble order); the kernels take them with ST = uint8_t
+  int mx;
 };
 
 // Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
@@ -94,6 +97,7 @@ inline void launch_gemm_kernel(void (*kernel)(GemmArgs), dim3 grid, dim3 block, 
 // rows-layout source.
 struct PackArgs {
   int E, S, rows, N, K, bits, fusion, NB, KT;
+  int natural;  // 4-bit codes keep their order (MX FP4) instead of the decode order
 };
 hipError_t launch_pack_stack(const uint8_t* src, uint8_t* dst, const PackArgs& a, hipStream_t s);
 

@@ -47,10 +47,10 @@ __global__ __launch_bounds__(256) void pack_stack_kernel(const uint8_t* __restri
     for (int j = 0; j < ssk / 32; ++j) {
       const int64_t k0 = static_cast<int64_t>(t) * ssk + 32 * j + 8 * q;
       if (a.bits == 4) {
-        // element i goes to nibble (0, 4, 1, 5, 2, 6, 3, 7)[i] of word j
+        // element i goes to nibble (0, 4, 1, 5, 2, 6, 3, 7)[i] of word j (MX FP4: nibble i)
         uint32_t w = 0u;
         for (int i = 0; i < 8; ++i) {
-          const int p = (i >> 1) + ((i & 1) << 2);
+          const int p = a.natural ? i : (i >> 1) + ((i & 1) << 2);
           w |= code_at(row, k0 + i, a.K, 4) << (4 * p);
         }
         out[j] = w;
