@@ -224,7 +224,7 @@ def main():
     inp = gen.make_inputs(cfg, T)
     d = DeviceInputs(inp)
     layout = args.layout if cfg.act_dtype == "bf16" else "rows"  # tiles serve bf16 activations
-    p = params_for(cfg, T, tile_m=args.tile_m, layout=layout)
+    p = params_for(cfg, T, tile_m=args.tile_m, layout=layout, ebias=d.ebias)
     qm.qmoe_validate(p)
 
     # stage buffers (the same kernels qmoe_forward launches, called one by one)

@@ -107,6 +107,20 @@ typedef struct {
   /* qmoe_layout of every weight stack handed to the GEMM and forward entry points.
      QMOE_LAYOUT_TILES requires act_dtype QMOE_BF16. */
   int32_t weight_layout;
+  /* Routing variants (CLIKA "MoE" page: routing kwargs n_group, topk_group,
+     routed_scaling_factor; ClikaRT "QMoEWoQ" page: the aux-free selection bias
+     e_score_correction_bias [E]). All off when zero / NULL.
+     n_group > 1: experts form n_group groups of E / n_group consecutive indices (E a
+       multiple, n_group <= 16); a group scores the largest selection key of its experts;
+       the topk_group best groups are kept (ties to the lower group) and the k experts are
+       chosen among theirs (k <= topk_group * E / n_group).
+     routed_scaling_factor: multiplies the k routing weights after any renormalisation
+       (0 means 1).
+     e_score_correction_bias: device [E] in act_dtype, or NULL; the selection key of expert
+       e is the fp32 sum logit + bias[e]; the weights use the logits alone. */
+  int32_t n_group, topk_group;
+  float routed_scaling_factor;
+  const void* e_score_correction_bias;
 } qmoe_params;
 
 /* One quantized expert stack (graiphic QMoE fcN_experts_weights / fcN_scales / fcN_experts_bias).

@@ -39,7 +39,9 @@ class Params(ctypes.Structure):
                 ("activation", ctypes.c_int32), ("normalize", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("scale_dtype", ctypes.c_int32),
                 ("pad_", ctypes.c_int32), ("alpha", ctypes.c_double),
-                ("beta", ctypes.c_double), ("limit", ctypes.c_double)]
+                ("beta", ctypes.c_double), ("limit", ctypes.c_double),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("routed_scale", ctypes.c_double), ("score_bias", ctypes.c_void_p)]
 
 
 class Stack(ctypes.Structure):
@@ -79,14 +81,18 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data
 
 
-def params(cfg, T: int) -> Params:
+def params(cfg, T: int, score_bias: Optional[np.ndarray] = None) -> Params:
+    """The oracle's parameter block; score_bias: the selection bias [E] in the activation
+    dtype (the caller keeps the array alive during the call)."""
     lim = cfg.limit if (cfg.limit is not None and cfg.limit > 0) else math.inf
     return Params(T=T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k, bits=cfg.bits,
                   block_size=cfg.block_size, fusion=cfg.fusion,
                   activation=ACTS[cfg.activation], normalize=int(cfg.normalize),
                   act_dtype=F32 if cfg.act_dtype == "f32" else BF16,
                   scale_dtype=_SDT[cfg.scale_dtype], pad_=0,
-                  alpha=cfg.alpha, beta=cfg.beta, limit=lim)
+                  alpha=cfg.alpha, beta=cfg.beta, limit=lim, n_group=cfg.n_group,
+                  topk_group=cfg.topk_group, routed_scale=cfg.routed_scale,
+                  score_bias=_ptr(score_bias))
 
 
 def _stack(w, s, b) -> Stack:
@@ -100,9 +106,9 @@ def stacks(inp):
     return fc1, fc2, fc3
 
 
-def route(cfg, logits: np.ndarray):
+def route(cfg, logits: np.ndarray, score_bias: Optional[np.ndarray] = None):
     T = logits.shape[0]
-    p = params(cfg, T)
+    p = params(cfg, T, score_bias)
     ids = np.zeros((T, cfg.k), np.int32)
     w = np.zeros((T, cfg.k), np.float64)
     lib().oracle_route(ctypes.byref(p), _ptr(logits), _ptr(ids), _ptr(w))
@@ -186,7 +192,7 @@ def combine(cfg, y: np.ndarray, assign_pos: np.ndarray, w: np.ndarray, shared=No
 def forward(cfg, inp, sel=None, nthreads: int = 0):
     """Oracle forward for all tokens (sel=None) or the listed token indices."""
     T = inp.x.shape[0]
-    p = params(cfg, T)
+    p = params(cfg, T, inp.ebias)
     fc1, fc2, fc3 = stacks(inp)
     if sel is not None:
         sel = np.ascontiguousarray(sel, dtype=np.int64)

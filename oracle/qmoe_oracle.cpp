@@ -99,16 +99,43 @@ static void store_out(const oracle_params* p, void* dst, int64_t i, double v) {
 static void route_token(const oracle_params* p, const void* logits, int64_t t, int32_t* ids,
                         double* w) {
   const int64_t E = p->E;
-  std::vector<double> l(E);
+  std::vector<double> l(E), key(E);
   for (int64_t e = 0; e < E; ++e) l[e] = widen(logits, p->act_dtype, t * E + e);
+  // Selection keys: the logits, or with a selection bias their fp32 sum with it (the sum
+  // of two stored values, rounded once to float, as the reading of the bias states).
+  for (int64_t e = 0; e < E; ++e) {
+    if (p->score_bias) {
+      const float b = static_cast<float>(widen(p->score_bias, p->act_dtype, e));
+      key[e] = static_cast<double>(static_cast<float>(l[e]) + b);
+    } else {
+      key[e] = l[e];
+    }
+  }
+  // Grouped top-k: groups of E / n_group consecutive experts scored by their largest key;
+  // the topk_group best (ties to the lower group) stay selectable.
+  std::vector<char> allowed(E, 1);
+  if (p->n_group > 1) {
+    const int64_t G = p->n_group, gsize = E / G;
+    std::vector<double> gs(G);
+    for (int64_t g = 0; g < G; ++g)
+      gs[g] = *std::max_element(key.begin() + g * gsize, key.begin() + (g + 1) * gsize);
+    std::vector<int32_t> gorder(G);
+    std::iota(gorder.begin(), gorder.end(), 0);
+    std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) { return gs[a] > gs[b]; });
+    std::vector<char> kept(G, 0);
+    for (int64_t r = 0; r < p->topk_group; ++r) kept[gorder[r]] = 1;
+    for (int64_t e = 0; e < E; ++e) allowed[e] = kept[e / gsize];
+  }
 
-  // Selection: larger logit first; a stable sort keeps equal logits in index order.
-  std::vector<int32_t> order(E);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return l[a] > l[b]; });
+  // Selection: larger key first; a stable sort keeps equal keys in index order.
+  std::vector<int32_t> order;
+  for (int64_t e = 0; e < E; ++e)
+    if (allowed[e]) order.push_back(static_cast<int32_t>(e));
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return key[a] > key[b]; });
 
-  // Softmax over all E (shifted by the maximum for range only; the value is unchanged).
-  double m = l[order[0]];
+  // Softmax over all E logits (shifted by the maximum for range only; the value is
+  // unchanged).
+  const double m = *std::max_element(l.begin(), l.end());
   double denom = 0.0;
   for (int64_t e = 0; e < E; ++e) denom += std::exp(l[e] - m);
 
@@ -120,6 +147,8 @@ static void route_token(const oracle_params* p, const void* logits, int64_t t, i
   }
   if (p->normalize)
     for (int64_t j = 0; j < p->k; ++j) w[j] /= sum;
+  const double scale = p->routed_scale != 0.0 ? p->routed_scale : 1.0;
+  for (int64_t j = 0; j < p->k; ++j) w[j] *= scale;
 }
 
 void oracle_route(const oracle_params* p, const void* logits, int32_t* ids, double* w) {

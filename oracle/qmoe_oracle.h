@@ -46,6 +46,11 @@ typedef struct {
   int32_t scale_dtype;   /* ORACLE_F32 / ORACLE_BF16 / ORACLE_E8M0 (MX FP4 weights) */
   int32_t pad_;
   double alpha, beta, limit; /* limit = +inf: no clamp */
+  /* routing variants: grouped top-k (n_group > 1), weight scaling (0 means 1), and the
+     selection bias [E] in the activation dtype (NULL: none) */
+  int32_t n_group, topk_group;
+  double routed_scale;
+  const void* score_bias;
 } oracle_params;
 
 typedef struct {

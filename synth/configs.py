@@ -48,6 +48,13 @@ class Config:
     scale_hi: float = 0.02
     bias_sigma: float = 0.02
     seed_base: int = 20261203
+    # routing variants (CLIKA "MoE" page routing kwargs; ClikaRT "QMoEWoQ" page selection
+    # bias): grouped top-k, weight scaling, and a selection bias [E] ~ N(0, ebias_sigma)
+    n_group: int = 0
+    topk_group: int = 0
+    routed_scale: float = 1.0
+    score_bias: bool = False
+    ebias_sigma: float = 0.5
 
     def with_(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -122,6 +129,12 @@ LINEAR = {"lin-decode": LIN_DECODE, "lin-prefill": LIN_PREFILL}
 C2_MX = C2.with_(name="c2-decode-mxfp4", scale_dtype="e8m0")
 C5_MX = C5.with_(name="c5-sweep-mxfp4", bits=4, block_size=32, scale_dtype="e8m0")
 MX = {"c2-mx": C2_MX, "c5-mx": C5_MX}
+
+# Routing variants on the c5 shape (64 experts in 8 groups of 8, 4 groups kept, k = 6, a
+# selection bias and a weight scale of 2.5) and on c2 (a selection bias only).
+C5_ROUTED = C5.with_(name="c5-grouped-biased", n_group=8, topk_group=4, routed_scale=2.5,
+                     score_bias=True)
+C2_BIASED = C2.with_(name="c2-biased", score_bias=True)
 
 C5_BITS = (4, 8)
 C5_BLOCKS = (16, 32, 64, 128)

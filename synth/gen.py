@@ -24,7 +24,7 @@ from .configs import Config
 
 TENSOR_IDS = {"x": 1, "logits": 2, "w1": 3, "s1": 4, "b1": 5, "w3": 6, "s3": 7,
               "b3": 8, "w2": 9, "s2": 10, "b2": 11, "shared": 12, "h": 13, "y": 14,
-              "topk_w": 15, "topk_ids": 16}
+              "topk_w": 15, "topk_ids": 16, "ebias": 17}
 
 
 def rng_for(cfg: Config, tensor: str, T: Optional[int] = None, seed: int = 0) -> np.random.Generator:
@@ -85,6 +85,7 @@ class Inputs:
     s3: Optional[np.ndarray] = None
     b3: Optional[np.ndarray] = None
     shared: Optional[np.ndarray] = None
+    ebias: Optional[np.ndarray] = None  # selection bias [E], activation dtype
 
 
 def gen_weights(cfg: Config, which: str, N: int, K: int, seed: int = 0):
@@ -113,6 +114,14 @@ def gen_activations(cfg: Config, T: int, seed: int = 0, shared: bool = False):
     return x, logits, sh
 
 
+def gen_score_bias(cfg: Config, seed: int = 0) -> Optional[np.ndarray]:
+    """The selection bias [E] of a config that has one (activation dtype), else None."""
+    if not cfg.score_bias:
+        return None
+    return store(rng_for(cfg, "ebias", seed=seed).normal(0.0, cfg.ebias_sigma, size=cfg.E),
+                 cfg.act_dtype)
+
+
 def make_inputs(cfg: Config, T: int, seed: int = 0, shared: bool = False) -> Inputs:
     x, logits, sh = gen_activations(cfg, T, seed, shared)
     w1, s1, b1 = gen_weights(cfg, "1", cfg.n1, cfg.H, seed)
@@ -121,7 +130,7 @@ def make_inputs(cfg: Config, T: int, seed: int = 0, shared: bool = False) -> Inp
     if cfg.has_fc3:
         w3, s3, b3 = gen_weights(cfg, "3", cfg.I, cfg.H, seed)
     return Inputs(cfg=cfg, T=T, x=x, logits=logits, w1=w1, s1=s1, b1=b1, w2=w2, s2=s2,
-                  b2=b2, w3=w3, s3=s3, b3=b3, shared=sh)
+                  b2=b2, w3=w3, s3=s3, b3=b3, shared=sh, ebias=gen_score_bias(cfg, seed))
 
 
 def make_linear_inputs(cfg: Config, T: int, seed: int = 0) -> Inputs:

@@ -54,28 +54,45 @@ def dequant_dense(w: np.ndarray, s: np.ndarray, cfg, N: int, K: int) -> np.ndarr
     return (q - (1 << (cfg.bits - 1))).astype(np.float64) * scale
 
 
-def select(cfg, logits_row: np.ndarray):
+def _best_subset(values: np.ndarray, candidates, size: int):
+    """The size-subset of candidates with the largest sum of values; ties: the
+    lexicographically smallest (itertools yields them in that order)."""
     best, best_sum = None, None
-    for subset in itertools.combinations(range(cfg.E), cfg.k):
-        s = float(sum(logits_row[list(subset)]))
+    for subset in itertools.combinations(candidates, size):
+        s = float(sum(values[list(subset)]))
         if best_sum is None or s > best_sum:
             best, best_sum = subset, s
     return list(best)
 
 
-def gates(cfg, logits: np.ndarray) -> np.ndarray:
-    """Dense [T, E] routing weights (zero for unselected experts)."""
+def select(cfg, keys_row: np.ndarray):
+    """Experts of one token by subset enumeration. Grouped top-k: the topk_group groups
+    whose largest keys have the largest sum, then the k experts of those groups whose keys
+    have the largest sum."""
+    cand = list(range(cfg.E))
+    if cfg.n_group > 1:
+        gsize = cfg.E // cfg.n_group
+        gmax = keys_row.reshape(cfg.n_group, gsize).max(axis=1)
+        groups = _best_subset(gmax, range(cfg.n_group), cfg.topk_group)
+        cand = [e for g in sorted(groups) for e in range(g * gsize, (g + 1) * gsize)]
+    return _best_subset(keys_row, cand, cfg.k)
+
+
+def gates(cfg, logits: np.ndarray, ebias=None) -> np.ndarray:
+    """Dense [T, E] routing weights (zero for unselected experts). ebias: the selection
+    bias, added to the float32 logits in float32 for the choice only."""
     T = logits.shape[0]
     G = np.zeros((T, cfg.E))
     for t in range(T):
         row = logits[t]
-        chosen = select(cfg, row)
+        keys = row if ebias is None else (row.astype(np.float32) + ebias.astype(np.float32)).astype(np.float64)
+        chosen = select(cfg, keys)
         p = np.exp(row - row.max())
         p = p / p.sum()
         wsel = p[chosen]
         if cfg.normalize:
             wsel = wsel / wsel.sum()
-        G[t, chosen] = wsel
+        G[t, chosen] = wsel * cfg.routed_scale
     return G
 
 
@@ -116,7 +133,8 @@ def forward(cfg, inp) -> np.ndarray:
     else:
         raise ValueError(cfg.activation)
     y = np.einsum("eti,ehi->eth", h, W2) + (0.0 if inp.b2 is None else bias(inp.b2)[:, None, :])
-    G = gates(cfg, lg)
+    eb = None if inp.ebias is None else as_f32(inp.ebias, cfg.act_dtype)
+    G = gates(cfg, lg, eb)
     out = np.einsum("te,eth->th", G, y)
     if inp.shared is not None:
         out = out + as_f32(inp.shared, cfg.act_dtype).astype(np.float64)

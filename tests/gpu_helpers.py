@@ -30,7 +30,9 @@ def host_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
     return as_f32(host(t), dtype).astype(np.float64)
 
 
-def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str = "rows"):
+def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str = "rows",
+               ebias=None):
+    """ebias: the device selection bias [E] (required when the config has one)."""
     if cfg.scale_dtype == "e8m0":
         layout = "tiles"  # MX FP4 weights run in the tiled layout only
     return qm.make_params(T, cfg.H, cfg.I, cfg.E, cfg.k, expert_weight_bits=cfg.bits,
@@ -38,7 +40,9 @@ def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str =
                           activation=cfg.activation, normalize_routing_weights=cfg.normalize,
                           swiglu_alpha=cfg.alpha, swiglu_beta=cfg.beta, swiglu_limit=cfg.limit,
                           act_dtype=cfg.act_dtype, scale_dtype=cfg.scale_dtype, tile_m=tile_m,
-                          strict_blocks=strict, weight_layout=layout)
+                          strict_blocks=strict, weight_layout=layout, n_group=cfg.n_group,
+                          topk_group=cfg.topk_group, routed_scaling_factor=cfg.routed_scale,
+                          e_score_correction_bias=ebias)
 
 
 class DeviceInputs:
@@ -55,6 +59,7 @@ class DeviceInputs:
         if inp.w3 is not None:
             self.fc3 = (dev(inp.w3), dev(inp.s3, s), dev(inp.b3, a) if inp.b3 is not None else None)
         self.shared = dev(inp.shared, a) if inp.shared is not None else None
+        self.ebias = dev(inp.ebias, a) if inp.ebias is not None else None
 
     def tiled(self, p):
         """A copy whose weight stacks are in the tiled layout (qmoe_pack_stack), scales and

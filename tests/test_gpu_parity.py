@@ -41,8 +41,9 @@ def say(*a):
 
 # --------------------------------------------------------------------------- route
 
-def run_route(cfg, logits_np, T):
-    p = params_for(cfg, T)
+def run_route(cfg, logits_np, T, ebias_np=None):
+    eb = dev(ebias_np, cfg.act_dtype) if ebias_np is not None else None
+    p = params_for(cfg, T, ebias=eb)
     lg = dev(logits_np, cfg.act_dtype)
     ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
@@ -57,6 +58,15 @@ ROUTE_CASES = {
     "E512-k8": (configs.tiny(E=512, k=8, act_dtype="bf16", logit_sigma=0.5), 300),
     "E130-k32": (configs.tiny(E=130, k=32, act_dtype="f32", normalize=False), 100),
     "E1-k1": (configs.tiny(E=1, k=1, act_dtype="bf16"), 7),
+    # routing variants: selection bias, grouped top-k, weight scaling
+    "c5-grouped-biased-T256": (configs.C5_ROUTED, 256),
+    "c2-biased-T64": (configs.C2_BIASED, 64),
+    "E256-g8-k8-biased-bf16": (configs.tiny(E=256, k=8, n_group=8, topk_group=4, score_bias=True,
+                                            routed_scale=2.5, act_dtype="bf16"), 200),
+    "E32-g4-top1-f32-norenorm": (configs.tiny(E=32, k=4, n_group=4, topk_group=1,
+                                              normalize=False, act_dtype="f32"), 100),
+    "E96-g16-biased-f32": (configs.tiny(E=96, k=6, n_group=16, topk_group=3, score_bias=True,
+                                        act_dtype="f32", routed_scale=0.5), 64),
 }
 
 
@@ -65,8 +75,9 @@ def test_route_matches_oracle(name):
     cfg, T = ROUTE_CASES[name]
     say("route", name, cfg.E, cfg.k, T)
     _, logits, _ = gen.gen_activations(cfg, T)
-    ids, w = run_route(cfg, logits, T)
-    rids, rw = oracle.route(cfg, logits)
+    eb = gen.gen_score_bias(cfg)
+    ids, w = run_route(cfg, logits, T, eb)
+    rids, rw = oracle.route(cfg, logits, eb)
     assert np.array_equal(ids, rids)
     assert np.max(np.abs(w - rw)) < 2e-6
 
@@ -350,8 +361,10 @@ def test_combine_rounds_to_nearest_even():
 
 def forward_gpu(cfg, inp, d=None, reshape3d=False, layout="rows"):
     T = inp.x.shape[0]
-    p = params_for(cfg, T, layout=layout)
-    d = d or _device(inp, p)
+    base = d if d is not None else DeviceInputs(inp)
+    p = params_for(cfg, T, layout=layout, ebias=base.ebias)
+    if d is None:
+        d = base.tiled(p) if p.weight_layout == qm.QMOE_LAYOUT_TILES else base
     x = d.x.view(1, T, cfg.H) if reshape3d else d.x
     sh = d.shared.view(1, T, cfg.H) if (reshape3d and d.shared is not None) else d.shared
     out = qm.forward(p, x, d.logits, d.fc1, d.fc2, d.fc3, sh)
@@ -365,8 +378,8 @@ def check_forward(cfg, T, sample=None, shared=False, seed=0, layout="rows"):
     out, d = forward_gpu(cfg, inp, layout=layout)
     got = host_f64(out, cfg.act_dtype)
     # routing and grouping of every token, bit for bit
-    ids_g, _ = run_route(cfg, inp.logits, T)
-    ids_o, w_o = oracle.route(cfg, inp.logits)
+    ids_g, _ = run_route(cfg, inp.logits, T, inp.ebias)
+    ids_o, w_o = oracle.route(cfg, inp.logits, inp.ebias)
     assert np.array_equal(ids_g, ids_o)
     M, perm_g = run_permute(cfg, ids_o, T)
     perm_o = oracle.permute(cfg, ids_o, M)
@@ -431,6 +444,18 @@ def test_forward_tiled_c4_many_experts_sampled():
 @pytest.mark.parametrize("T", [256, 4096])
 def test_forward_tiled_c5_sweep(T, bs, bits):
     check_forward(configs.c5_point(bits, bs), T, sample=6, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [8, 64])
+def test_forward_routing_variants_c2_biased(T):
+    # a selection bias on c2 (T = 8 takes the one-kernel routing and grouping)
+    check_forward(configs.C2_BIASED, T, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [16, 256])
+def test_forward_routing_variants_c5_grouped(T):
+    # grouped top-k, selection bias and weight scaling on the c5 shape
+    check_forward(configs.C5_ROUTED, T, sample=6, layout="tiles")
 
 
 @pytest.mark.parametrize("T", [1, 8, 64])

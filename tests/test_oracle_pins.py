@@ -47,6 +47,11 @@ BRUTE_CASES = {
     "f32-no-renorm-E6k3": configs.tiny(normalize=False, E=6, k=3, logit_sigma=2.0),
     "bf16-fscale-b8-bs64": configs.tiny(act_dtype="bf16", scale_dtype="f32", bits=8,
                                         block_size=64, H=128, I=64),
+    "bf16-grouped-biased-scaled": configs.tiny(act_dtype="bf16", scale_dtype="bf16", E=16, k=3,
+                                               n_group=4, topk_group=2, score_bias=True,
+                                               routed_scale=2.5, fusion=1, fc1_bias=True),
+    "f32-grouped-norenorm": configs.tiny(E=12, k=2, n_group=3, topk_group=1, normalize=False,
+                                         logit_sigma=2.0),
     "bf16-mxfp4-interleaved-bias": configs.tiny(act_dtype="bf16", scale_dtype="e8m0", bits=4,
                                                 block_size=32, H=96, I=64, fusion=1,
                                                 fc1_bias=True, fc2_bias=True, limit=7.0,
@@ -93,6 +98,30 @@ def test_route_matches_subset_bruteforce_with_many_ties():
         kth = lf[t, ids[t, -1]]
         ties += int(np.sum(lf[t] == kth) > np.sum(lf[t, ids[t]] == kth))
     assert ties > 30  # the boundary tie rule was exercised
+
+
+@pytest.mark.parametrize("n_group,topk_group,k,bias", [(4, 2, 3, True), (8, 3, 5, False),
+                                                       (2, 1, 4, True)])
+def test_grouped_biased_route_matches_subset_bruteforce_with_ties(n_group, topk_group, k, bias):
+    # logits and biases on a coarse grid, so that selection keys, group scores and their
+    # fp32 sums tie often; the brute force enumerates group sets and expert subsets
+    E = 16
+    cfg = configs.tiny(E=E, k=k, n_group=n_group, topk_group=topk_group, score_bias=bias,
+                       routed_scale=1.5, act_dtype="f32")
+    rng = np.random.default_rng(n_group * 10 + k)
+    lg = (rng.integers(-3, 4, size=(40, E)) * 0.25).astype(np.float32)
+    eb = (rng.integers(-2, 3, size=E) * 0.25).astype(np.float32) if bias else None
+    ids, w = oracle.route(cfg, lg, eb)
+    G = bruteforce.gates(cfg, lg.astype(np.float64), eb)
+    for t in range(40):
+        assert sorted(ids[t].tolist()) == sorted(np.nonzero(G[t])[0].tolist()), t
+        assert np.allclose(w[t], G[t, ids[t]], rtol=1e-13)
+    # the slots hold the chosen experts by descending key, equal keys in index order
+    keys = lg if eb is None else lg + eb
+    for t in range(40):
+        kk = keys[t, ids[t]]
+        assert all(kk[j] > kk[j + 1] or (kk[j] == kk[j + 1] and ids[t, j] < ids[t, j + 1])
+                   for j in range(k - 1))
 
 
 def test_route_uniform_logits_pick_lowest_indices():

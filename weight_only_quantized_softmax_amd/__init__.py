@@ -38,7 +38,13 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                 swiglu_alpha: float = 1.0, swiglu_beta: float = 0.0,
                 swiglu_limit: float = math.inf, act_dtype: str = "bf16",
                 scale_dtype: str = "bf16", tile_m: int = 0,
-                strict_blocks: bool = False, weight_layout: str = "rows") -> QmoeParams:
+                strict_blocks: bool = False, weight_layout: str = "rows", n_group: int = 0,
+                topk_group: int = 0, routed_scaling_factor: float = 1.0,
+                e_score_correction_bias: Optional[torch.Tensor] = None) -> QmoeParams:
+    """The parameter block. e_score_correction_bias: a device tensor [E] in the activation
+    dtype (the block keeps its address, so the tensor must outlive the calls)."""
+    bias = None if e_score_correction_bias is None else _ptr(e_score_correction_bias,
+                                                            "e_score_correction_bias")
     return QmoeParams(num_tokens=num_tokens, hidden_size=hidden_size, inter_size=inter_size,
                       num_experts=num_experts, k=k, expert_weight_bits=expert_weight_bits,
                       block_size=block_size, swiglu_fusion=swiglu_fusion,
@@ -48,7 +54,9 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                       swiglu_limit=swiglu_limit, act_dtype=_DT[act_dtype],
                       scale_dtype=_DT[scale_dtype], tile_m=tile_m,
                       strict_blocks=int(bool(strict_blocks)),
-                      weight_layout=_LAYOUT[weight_layout])
+                      weight_layout=_LAYOUT[weight_layout], n_group=n_group,
+                      topk_group=topk_group, routed_scaling_factor=routed_scaling_factor,
+                      e_score_correction_bias=bias)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str):

@@ -27,7 +27,10 @@ class QmoeParams(ctypes.Structure):
                 ("swiglu_alpha", ctypes.c_float), ("swiglu_beta", ctypes.c_float),
                 ("swiglu_limit", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("scale_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("strict_blocks", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
+                ("strict_blocks", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float),
+                ("e_score_correction_bias", ctypes.c_void_p)]
 
 
 class QmoeStack(ctypes.Structure):

@@ -98,6 +98,22 @@ qmoe_status validate(const qmoe_params* p) {
   if (p->k < 1 || p->k > p->num_experts)
     return fail(QMOE_ERR_INVALID, "k %lld outside [1, num_experts]", (long long)p->k);
   if (p->k > kMaxTopK) return fail(QMOE_ERR_UNSUPPORTED, "k %lld > %lld", (long long)p->k, (long long)kMaxTopK);
+  if (p->n_group > 1) {
+    if (p->n_group > qmoe::kMaxGroups)
+      return fail(QMOE_ERR_UNSUPPORTED, "n_group %d > %d", p->n_group, qmoe::kMaxGroups);
+    if (p->num_experts % p->n_group)
+      return fail(QMOE_ERR_INVALID, "num_experts %lld is not a multiple of n_group %d",
+                  (long long)p->num_experts, p->n_group);
+    if (p->topk_group < 1 || p->topk_group > p->n_group)
+      return fail(QMOE_ERR_INVALID, "topk_group %d outside [1, n_group]", p->topk_group);
+    if (p->k > p->topk_group * (p->num_experts / p->n_group))
+      return fail(QMOE_ERR_INVALID, "k %lld exceeds the experts of topk_group groups",
+                  (long long)p->k);
+  } else if (p->n_group < 0 || p->topk_group < 0) {
+    return fail(QMOE_ERR_INVALID, "n_group and topk_group must not be negative");
+  }
+  if (!std::isfinite(p->routed_scaling_factor))
+    return fail(QMOE_ERR_INVALID, "routed_scaling_factor must be finite");
   if (p->expert_weight_bits != 4 && p->expert_weight_bits != 8)
     return fail(QMOE_ERR_INVALID, "expert_weight_bits %d is not 4 or 8", p->expert_weight_bits);
   if (p->block_size != 0 && (!is_pow2(p->block_size) || p->block_size < 16))
@@ -173,6 +189,15 @@ qmoe_status validate_for_pack(const qmoe_params* p) {
     return validate(&q);
   }
   return validate(p);
+}
+
+qmoe::RouteOpts route_opts(const qmoe_params* p) {
+  qmoe::RouteOpts o{};
+  o.bias = p->e_score_correction_bias;
+  o.n_group = p->n_group > 1 ? p->n_group : 1;
+  o.topk_group = p->n_group > 1 ? p->topk_group : 1;
+  o.scale = p->routed_scaling_factor != 0.f ? p->routed_scaling_factor : 1.f;
+  return o;
 }
 
 int64_t max_tiles_of(const qmoe_params* p) {
@@ -412,7 +437,7 @@ qmoe_status qmoe_route(const qmoe_params* p, const void* router_logits, int32_t*
   return device_status(
       qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
                          static_cast<int>(p->num_experts), static_cast<int>(p->k),
-                         p->normalize_routing_weights, topk_ids, topk_w,
+                         p->normalize_routing_weights, route_opts(p), topk_ids, topk_w,
                          static_cast<hipStream_t>(stream)),
       "route launch");
 }
@@ -515,14 +540,14 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
         qmoe::launch_route_permute(router_logits, p->act_dtype == QMOE_BF16,
                                    static_cast<int>(p->num_tokens), static_cast<int>(p->num_experts),
                                    static_cast<int>(p->k), p->normalize_routing_weights,
-                                   tile_m_of(p), w.topk_ids, w.topk_w, w.counts, w.offsets,
+                                   route_opts(p), tile_m_of(p), w.topk_ids, w.topk_w, w.counts, w.offsets,
                                    w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles, s),
         "route+permute launch"));
   } else {
     QMOE_TRY(device_status(
         qmoe::launch_route(router_logits, p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
                            static_cast<int>(p->num_experts), static_cast<int>(p->k),
-                           p->normalize_routing_weights, w.topk_ids, w.topk_w, s),
+                           p->normalize_routing_weights, route_opts(p), w.topk_ids, w.topk_w, s),
         "route launch"));
     QMOE_TRY(device_status(
         qmoe::launch_permute(w.topk_ids, A, static_cast<int>(p->num_experts), tile_m_of(p), w.counts,

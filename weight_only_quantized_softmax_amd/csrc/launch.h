@@ -101,15 +101,24 @@ struct PackArgs {
 };
 hipError_t launch_pack_stack(const uint8_t* src, uint8_t* dst, const PackArgs& a, hipStream_t s);
 
+// Routing variants: selection bias, grouped top-k, weight scaling (route.h).
+constexpr int kMaxGroups = 16;
+struct RouteOpts {
+  const void* bias;     // [E] in the logits' dtype, or nullptr
+  int n_group;          // <= 1: no grouping
+  int topk_group;
+  float scale;          // multiplies the k weights
+};
+
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
-                        int32_t* ids, float* w, hipStream_t s);
+                        const RouteOpts& o, int32_t* ids, float* w, hipStream_t s);
 
 // One launch for routing and grouping: batches of at most this many tokens (and at most
 // kPermFusedMax assignments).
 constexpr int64_t kRoutePermuteMaxT = 16;
 bool route_permute_fits(int64_t T, int64_t A);
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
-                                int M, int32_t* ids, float* w, int32_t* counts,
+                                const RouteOpts& o, int M, int32_t* ids, float* w, int32_t* counts,
                                 int32_t* padded_offsets, int32_t* sorted_assign,
                                 int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles,
                                 hipStream_t s);

@@ -142,8 +142,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(
 // batch is small enough that one block routes it quickly.
 template <typename TA, int V>
 __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
-    const TA* __restrict__ logits, int T, int E, int k, int normalize, int ebits, int M,
-    int32_t* ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    const TA* __restrict__ logits, int T, int E, int k, int normalize, RouteOpts o, int ebits,
+    int M, int32_t* ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ padded_offsets, int32_t* __restrict__ sorted_assign,
     int32_t* __restrict__ assign_pos, int32_t* __restrict__ tile_list,
     int32_t* __restrict__ num_tiles) {
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
   int* scan_tmp = run + E;        // [kPermWaves + 1]
   int* wc = scan_tmp + kPermWaves + 1;  // [kPermWaves][E]
   const int wave = threadIdx.x / kWave;
-  for (int t = wave; t < T; t += kPermWaves) route_token<TA, V>(logits, t, E, k, normalize, ids, topk_w);
+  for (int t = wave; t < T; t += kPermWaves) route_token<TA, V>(logits, t, E, k, normalize, o, ids, topk_w);
   for (int i = threadIdx.x; i < E; i += kPermThreads) cnt[i] = 0;
   __syncthreads();  // the ids written by each wave's lane 0 are visible to the whole block
   const int64_t A = static_cast<int64_t>(T) * k;
@@ -235,22 +235,24 @@ size_t permute_scratch_bytes(int64_t A, int E) {
 bool route_permute_fits(int64_t T, int64_t A) { return A <= kPermFusedMax && T <= kRoutePermuteMaxT; }
 
 template <typename TA, int V>
-static void launch_rp(const TA* logits, int T, int E, int k, int normalize, int M, int32_t* ids,
+static void launch_rp(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
+                      int M, int32_t* ids,
                       float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                       int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
   const size_t lds = (2 * E + kPermWaves + 1 + kPermWaves * E) * sizeof(int);
-  route_permute_kernel<TA, V><<<1, kPermThreads, lds, s>>>(logits, T, E, k, normalize, bits_for(E), M,
+  route_permute_kernel<TA, V><<<1, kPermThreads, lds, s>>>(logits, T, E, k, normalize, o, bits_for(E), M,
                                                           ids, w, counts, padded_offsets,
                                                           sorted_assign, assign_pos, tile_list,
                                                           num_tiles);
 }
 
 template <typename TA>
-static void launch_rp_t(const TA* logits, int T, int E, int k, int normalize, int M, int32_t* ids,
+static void launch_rp_t(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
+                        int M, int32_t* ids,
                         float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
   const int V = (E + 63) / 64;
-#define QMOE_RP(VV) launch_rp<TA, VV>(logits, T, E, k, normalize, M, ids, w, counts, padded_offsets, \
+#define QMOE_RP(VV) launch_rp<TA, VV>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets, \
                                       sorted_assign, assign_pos, tile_list, num_tiles, s)
   if (V <= 1) QMOE_RP(1);
   else if (V <= 2) QMOE_RP(2);
@@ -261,15 +263,15 @@ static void launch_rp_t(const TA* logits, int T, int E, int k, int normalize, in
 }
 
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
-                                int M, int32_t* ids, float* w, int32_t* counts,
+                                const RouteOpts& o, int M, int32_t* ids, float* w, int32_t* counts,
                                 int32_t* padded_offsets, int32_t* sorted_assign,
                                 int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles,
                                 hipStream_t s) {
   if (bf16)
-    launch_rp_t(static_cast<const uint16_t*>(logits), T, E, k, normalize, M, ids, w, counts,
+    launch_rp_t(static_cast<const uint16_t*>(logits), T, E, k, normalize, o, M, ids, w, counts,
                 padded_offsets, sorted_assign, assign_pos, tile_list, num_tiles, s);
   else
-    launch_rp_t(static_cast<const float*>(logits), T, E, k, normalize, M, ids, w, counts,
+    launch_rp_t(static_cast<const float*>(logits), T, E, k, normalize, o, M, ids, w, counts,
                 padded_offsets, sorted_assign, assign_pos, tile_list, num_tiles, s);
   return hipGetLastError();
 }
