@@ -310,6 +310,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
 #pragma unroll
           for (int b = 0; b < kBNB; ++b)
             sv[b] = scale_value<ST>(sc[(wn * 64 + b * 16 + n) * NBLK + bl]);
+          // software-pipelined by one product: the scaling FMAs of a product follow the
+          // next product's MFMA, so they never wait on the MFMA just issued
+          floatx4 aprev = zero4;
+          int pprev = -1;
+          auto scale_into = [&](int pidx, const floatx4& a) {
+            const int pm = pidx / kBNB, pb = pidx % kBNB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[pm][pb][i] += sv[pb] * a[i];
+            pin(tot[pm][pb]);
+          };
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             const bf16x8 xb = __builtin_bit_cast(bf16x8, xa[mt]);
@@ -318,11 +328,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
             for (int b = 0; b < kBNB; ++b) {
               const bf16x8 bw = decode(w[b], j);
               const floatx4 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mine ? bw : zero8, c, 0, 0, 0);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) tot[mt][b][i] += sv[b] * a[i];
-              pin(tot[mt][b]);
+              if (pprev >= 0) scale_into(pprev, aprev);
+              aprev = a;
+              pprev = mt * kBNB + b;
             }
           }
+          scale_into(pprev, aprev);
         }
       } else {
         // a group opens where a block starts and closes where the next one starts or K
