@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--block", type=int, default=32)
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--int8", action="store_true",
+                    help="the int8 activation tier: x and h rounded to per-block int8")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens per oracle call")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     ap.add_argument("--tile-m", type=int, default=0,
@@ -219,7 +221,11 @@ def main():
     cfg, T = workload(args)
     torch.cuda.set_device(0)
     if cfg.E == 1 and cfg.k == 1:
+        if args.int8:
+            sys.exit("--int8 applies to the MoE forward")
         return main_linear(args, cfg, T)
+    if args.int8:
+        cfg = cfg.with_(int8=True, name=f"{cfg.name}-a8")
     print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
     inp = gen.make_inputs(cfg, T)
     d = DeviceInputs(inp)
@@ -242,6 +248,7 @@ def main():
     nt = torch.empty(1, **i32)
     scratch = torch.empty(max(qm.qmoe_permute_scratch_size(p), 256), dtype=torch.uint8, device="cuda")
     h = torch.empty((rows, cfg.I), dtype=adt, device="cuda")
+    xq = torch.empty((T, cfg.H), dtype=adt, device="cuda") if cfg.int8 else None
     y = torch.empty((rows, cfg.H), dtype=torch.float32, device="cuda")
     out = torch.empty((T, cfg.H), dtype=adt, device="cuda")
     stream = torch.cuda.current_stream()
@@ -287,10 +294,16 @@ def main():
         s1, s2, s3 = st_args[i % copies]
         run(lib.qmoe_route(*route))
         run(lib.qmoe_permute(*perm))
+        x = d.x
+        if cfg.int8:
+            run(lib.qmoe_quantize_act(p, ptr(d.x), T, cfg.H, ptr(xq), sid))
+            x = xq
         if timed:
             run(lib.qmoe_time_next_gemm(evp[i][0], evp[i][1]))
-        run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(d.x), ptr(sa), ptr(tl), ptr(nt), s1, s3,
+        run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(x), ptr(sa), ptr(tl), ptr(nt), s1, s3,
                                              ptr(h), sid))
+        if cfg.int8:
+            run(lib.qmoe_quantize_act(p, ptr(h), rows, cfg.I, ptr(h), sid))
         if timed:
             run(lib.qmoe_time_next_gemm(evp[i][2], evp[i][3]))
         run(lib.qmoe_grouped_gemm_fc2(p, ptr(h), ptr(tl), ptr(nt), s2, ptr(y), sid))
@@ -372,7 +385,8 @@ def main():
         config=dict(workload=f"{cfg.name} T={T}", T=T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k,
                     bits=cfg.bits, block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
                     weight_layout=layout, tile_m=qm.qmoe_tile_m(p), weight_copies=copies,
-                    touched_experts=alg["touched"]),
+                    touched_experts=alg["touched"],
+                    activations="int8 blocks" if cfg.int8 else cfg.act_dtype),
         roofline=roof,
         cpu_baseline=cpu,
         weight_stream_GBps=round(stream_gbps, 1),

@@ -121,7 +121,15 @@ typedef struct {
   int32_t n_group, topk_group;
   float routed_scaling_factor;
   const void* e_score_correction_bias;
+  /* qmoe_compute_mode: QMOE_COMPUTE_FLOAT (0) keeps the activations as they are;
+     QMOE_COMPUTE_INT8 (the int8 block tier of the ClikaRT "QMoEWoQ" page) rounds the
+     input of each GEMM to per-block int8 first (qmoe_quantize_act): qmoe_forward does so
+     for x and h; callers of the GEMM entry points quantize their inputs themselves.
+     Needs block_size > 0. */
+  int32_t compute_mode;
 } qmoe_params;
+
+typedef enum { QMOE_COMPUTE_FLOAT = 0, QMOE_COMPUTE_INT8 = 1 } qmoe_compute_mode;
 
 /* One quantized expert stack (graiphic QMoE fcN_experts_weights / fcN_scales / fcN_experts_bias).
    weights: uint8 [E, N, K*bits/8] (QMOE_LAYOUT_ROWS) or the tiled form from qmoe_pack_stack
@@ -273,6 +281,20 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                          qmoe_stack fc1, qmoe_stack fc2, qmoe_stack fc3,
                          const void* shared_output, void* output, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * The int8 activation tier's rounding (ClikaRT "QMoEWoQ" page: the activation is rounded
+ * to per-block int8 before the dot where a block weight runs on the int8 tier).
+ *   in, out: [rows, cols] act_dtype, row-major (out may equal in). Each run of
+ *   p->block_size elements of a row (a shorter last one when block_size does not divide
+ *   cols) gets the power-of-two scale 2^e, e the smallest integer with
+ *   max|x| <= 127 * 2^e, and codes q = rint(x / 2^e) (ties to even, |q| <= 127); out holds
+ *   q * 2^e, exact in the activation dtype. Needs block_size > 0.
+ * qmoe_forward with compute_mode QMOE_COMPUTE_INT8 applies it to x (cols = hidden_size)
+ * and to h (cols = inter_size); the GEMM entry points take their inputs as given.
+ */
+qmoe_status qmoe_quantize_act(const qmoe_params* p, const void* in, int64_t rows, int64_t cols,
+                              void* out, void* stream);
 
 /*
  * Weight-only-quantized linear layer (ClikaRT "QLinearWoQ" page: y = x @ dequant(weight)^T

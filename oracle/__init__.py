@@ -41,7 +41,8 @@ class Params(ctypes.Structure):
                 ("pad_", ctypes.c_int32), ("alpha", ctypes.c_double),
                 ("beta", ctypes.c_double), ("limit", ctypes.c_double),
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
-                ("routed_scale", ctypes.c_double), ("score_bias", ctypes.c_void_p)]
+                ("routed_scale", ctypes.c_double), ("score_bias", ctypes.c_void_p),
+                ("int8_act", ctypes.c_int32), ("pad2_", ctypes.c_int32)]
 
 
 class Stack(ctypes.Structure):
@@ -70,6 +71,7 @@ def lib():
         L.oracle_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [P, S, S, S, vp, vp, vp, i64, vp, vp, vp, i32]
         L.oracle_round_bf16.argtypes = [vp, i64, vp]
+        L.oracle_int8_round.argtypes = [P, vp, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -92,7 +94,7 @@ def params(cfg, T: int, score_bias: Optional[np.ndarray] = None) -> Params:
                   scale_dtype=_SDT[cfg.scale_dtype], pad_=0,
                   alpha=cfg.alpha, beta=cfg.beta, limit=lim, n_group=cfg.n_group,
                   topk_group=cfg.topk_group, routed_scale=cfg.routed_scale,
-                  score_bias=_ptr(score_bias))
+                  score_bias=_ptr(score_bias), int8_act=int(cfg.int8))
 
 
 def _stack(w, s, b) -> Stack:
@@ -205,6 +207,17 @@ def forward(cfg, inp, sel=None, nthreads: int = 0):
                          _ptr(inp.x), _ptr(inp.logits), _ptr(inp.shared), n, _ptr(sel),
                          _ptr(out64), _ptr(outr), nthreads)
     return out64, outr
+
+
+def int8_round(cfg, a: np.ndarray) -> np.ndarray:
+    """The int8 activation tier's per-block rounding of the rows of a ([rows, cols], stored
+    in the activation dtype); the result has a's dtype and shape."""
+    a = np.ascontiguousarray(a)
+    rows, cols = a.shape
+    out = np.zeros_like(a)
+    p = params(cfg, rows)
+    lib().oracle_int8_round(ctypes.byref(p), _ptr(a), rows, cols, _ptr(out))
+    return out
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:

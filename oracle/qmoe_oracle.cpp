@@ -25,7 +25,13 @@
  *    gate, [I,2I) up; separate stacks: fc1 gate, fc3 up; biases follow rows;
  *  - SwiGLU: g' = min(g, L), u' = clamp(u, -L, L), h = g' * sigmoid(alpha g') * (u' + beta);
  *  - biases are added before the activation (fc1/fc3) and before the routing
- *    weight (fc2); shared_output is added after the weighted sum.
+ *    weight (fc2); shared_output is added after the weighted sum;
+ *  - the int8 block tier (ClikaRT "QMoEWoQ" page, class description) rounds each
+ *    block_size run of an activation row to int8 codes under one power-of-two scale 2^e,
+ *    e the smallest integer with max|x| <= 127 * 2^e, code = x / 2^e rounded to nearest,
+ *    ties to even; the GEMM then takes code * 2^e. It applies to the row x enters fc1
+ *    with and to h, after h has been rounded to the activation dtype (the dtype h is held
+ *    in between the two GEMMs), so both sides decide the codes from the same values.
  */
 #include "qmoe_oracle.h"
 
@@ -91,6 +97,48 @@ static void store_out(const oracle_params* p, void* dst, int64_t i, double v) {
   } else {
     uint16_t h = round_to_bf16(v);
     std::memcpy(static_cast<char*>(dst) + 2 * i, &h, 2);
+  }
+}
+
+/* ---- the int8 activation tier -------------------------------------------- */
+
+/* The smallest integer e with a <= 127 * 2^e (a >= 0; 0 for an all-zero block). The search
+   starts at e0 = ilogb(a) - 6, below the answer since 127 * 2^(e0 - 1) < 2^ilogb(a) <= a. */
+static int int8_block_exponent(double a) {
+  if (!(a > 0.0)) return 0;
+  int e = std::ilogb(a) - 6;
+  while (a > 127.0 * std::ldexp(1.0, e)) ++e;
+  return e;
+}
+
+/* Round one activation row, block by block (a shorter last block when block_size does not
+   divide len). */
+static void int8_round_row(const oracle_params* p, double* v, int64_t len) {
+  const int64_t bs = p->block_size;
+  for (int64_t b0 = 0; b0 < len; b0 += bs) {
+    const int64_t b1 = std::min(b0 + bs, len);
+    double a = 0.0;
+    for (int64_t i = b0; i < b1; ++i) a = std::max(a, std::fabs(v[i]));
+    const int e = int8_block_exponent(a);
+    for (int64_t i = b0; i < b1; ++i)
+      v[i] = std::ldexp(std::nearbyint(std::ldexp(v[i], -e)), e);
+  }
+}
+
+/* v rounded to the activation dtype and widened back. */
+static double to_act_dtype(const oracle_params* p, double v) {
+  if (p->act_dtype == ORACLE_F32) return static_cast<double>(static_cast<float>(v));
+  const uint16_t h = round_to_bf16(v);
+  return widen(&h, ORACLE_BF16, 0);
+}
+
+void oracle_int8_round(const oracle_params* p, const void* in, int64_t rows, int64_t cols,
+                       void* out) {
+  std::vector<double> v(cols);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t i = 0; i < cols; ++i) v[i] = widen(in, p->act_dtype, r * cols + i);
+    int8_round_row(p, v.data(), cols);
+    for (int64_t i = 0; i < cols; ++i) store_out(p, out, r * cols + i, v[i]);  // exact
   }
 }
 
@@ -358,8 +406,13 @@ void oracle_forward(const oracle_params* p, const oracle_stack* fc1, const oracl
     std::vector<double> w(k), xr(H), h(I), y(H), acc(H, 0.0);
     route_token(p, logits, t, ids.data(), w.data());
     widen_row(x, p->act_dtype, t, H, xr.data());
+    if (p->int8_act) int8_round_row(p, xr.data(), H);
     for (int64_t j = 0; j < k; ++j) {
       expert_fc1(p, fc1, fc3, ids[j], xr.data(), h.data());
+      if (p->int8_act) {
+        for (int64_t i = 0; i < I; ++i) h[i] = to_act_dtype(p, h[i]);
+        int8_round_row(p, h.data(), I);
+      }
       expert_fc2(p, fc2, ids[j], h.data(), y.data());
       for (int64_t m = 0; m < H; ++m) acc[m] += w[j] * y[m];
     }

@@ -21,6 +21,8 @@
  *   fc2      y = h . dequant(W2)^T + b2
  *   combine  out[t] = sum_j w_j * y(t, j) (+ shared_output[t]), rounded once to
  *            the activation dtype (ClikaRT "QMoEWoQ" page, forward)
+ *   int8     (optional) x and h rounded to per-block int8 before fc1 and fc2
+ *            (ClikaRT "QMoEWoQ" page, class description: the int8 block tier)
  *
  * Parity status of each function is stated in its comment in qmoe_oracle.cpp.
  */
@@ -51,6 +53,9 @@ typedef struct {
   int32_t n_group, topk_group;
   double routed_scale;
   const void* score_bias;
+  /* 1: the int8 activation tier, x and h rounded to per-block int8 before each GEMM */
+  int32_t int8_act;
+  int32_t pad2_;
 } oracle_params;
 
 typedef struct {
@@ -92,6 +97,11 @@ void oracle_forward(const oracle_params* p, const oracle_stack* fc1, const oracl
                     const oracle_stack* fc3, const void* x, const void* logits, const void* shared,
                     int64_t n_sel, const int64_t* sel, double* out64, void* out_rounded,
                     int nthreads);
+
+/* The int8 tier's rounding of rows [rows, cols] in the activation dtype: out (same dtype)
+   holds code * 2^e per block of block_size (block_size > 0). */
+void oracle_int8_round(const oracle_params* p, const void* in, int64_t rows, int64_t cols,
+                       void* out);
 
 /* Round fp64 values to bfloat16 bit patterns, nearest-even. */
 void oracle_round_bf16(const double* v, int64_t n, uint16_t* out);

@@ -55,6 +55,8 @@ class Config:
     routed_scale: float = 1.0
     score_bias: bool = False
     ebias_sigma: float = 0.5
+    # the int8 activation tier (ClikaRT "QMoEWoQ" page, class description)
+    int8: bool = False
 
     def with_(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -135,6 +137,11 @@ MX = {"c2-mx": C2_MX, "c5-mx": C5_MX}
 C5_ROUTED = C5.with_(name="c5-grouped-biased", n_group=8, topk_group=4, routed_scale=2.5,
                      score_bias=True)
 C2_BIASED = C2.with_(name="c2-biased", score_bias=True)
+# the int8 activation tier on the decode, prefill and many-expert shapes
+C2_INT8 = C2.with_(name="c2-decode-int4-a8", int8=True)
+C4_INT8 = C4.with_(name="c4-many-expert-int8-a8", int8=True)
+C5_INT8 = C5.with_(name="c5-sweep-a8", int8=True)
+C2_MX_INT8 = C2_MX.with_(name="c2-decode-mxfp4-a8", int8=True)
 
 C5_BITS = (4, 8)
 C5_BLOCKS = (16, 32, 64, 128)

@@ -7,7 +7,8 @@ It is built differently from the oracle on purpose:
   smallest index set), which equals "top-k, ties to the lower index";
 * every expert's FFN is evaluated for every token and mixed through a dense
   [T, E] gate matrix; no grouping or permutation is involved;
-* the sigmoid comes from scipy.
+* the sigmoid comes from scipy;
+* the int8 activation tier's scale is found by trying every power of two in turn.
 
 Sources for what is computed: CLIKA "MoE" page (router picks top-k experts,
 gated FFN, outputs combined under the router weights); CLIKA "QLinearWoQ" page
@@ -96,6 +97,34 @@ def gates(cfg, logits: np.ndarray, ebias=None) -> np.ndarray:
     return G
 
 
+def int8_round(v: np.ndarray, bs: int) -> np.ndarray:
+    """The int8 activation tier on the last axis by search: for each run of bs elements,
+    try every scale 2^e from e = -300 up and keep the first with max|x| <= 127 * 2^e, then
+    numpy's half-to-even rounding of x / 2^e."""
+    v = np.asarray(v, np.float64)
+    out = np.empty_like(v)
+    flat, res = v.reshape(-1, v.shape[-1]), out.reshape(-1, v.shape[-1])
+    for r in range(flat.shape[0]):
+        for b0 in range(0, flat.shape[1], bs):
+            blk = flat[r, b0:b0 + bs]
+            a = np.max(np.abs(blk))
+            e = 0
+            if a > 0:
+                e = next(c for c in range(-300, 300) if a <= 127.0 * 2.0 ** c)
+            res[r, b0:b0 + bs] = np.round(blk / 2.0 ** e) * 2.0 ** e
+    return out
+
+
+def round_act(v: np.ndarray, act_dtype: str) -> np.ndarray:
+    """Single rounding of doubles to the activation dtype: float32 by numpy's cast; bf16 by
+    rounding the significand to 8 bits, half to even (normal values)."""
+    if act_dtype == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    _, ex = np.frexp(v)
+    q = np.ldexp(1.0, ex - 8)
+    return np.round(v / q) * q
+
+
 def _act_pair(cfg, g, u):
     L = cfg.limit
     g = np.minimum(g, L)
@@ -113,6 +142,8 @@ def forward(cfg, inp) -> np.ndarray:
     def bias(b):
         return 0.0 if b is None else as_f32(b, cfg.act_dtype).astype(np.float64)
 
+    if cfg.int8:
+        x = int8_round(x, cfg.block_size)
     z1 = np.einsum("th,enh->etn", x, W1) + (0.0 if inp.b1 is None else bias(inp.b1)[:, None, :])
     if cfg.activation == "swiglu":
         if cfg.fusion == 1:
@@ -132,6 +163,8 @@ def forward(cfg, inp) -> np.ndarray:
         h = z1 * expit(z1)
     else:
         raise ValueError(cfg.activation)
+    if cfg.int8:
+        h = int8_round(round_act(h, cfg.act_dtype), cfg.block_size)
     y = np.einsum("eti,ehi->eth", h, W2) + (0.0 if inp.b2 is None else bias(inp.b2)[:, None, :])
     eb = None if inp.ebias is None else as_f32(inp.ebias, cfg.act_dtype)
     G = gates(cfg, lg, eb)

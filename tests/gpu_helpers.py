@@ -42,7 +42,8 @@ def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str =
                           act_dtype=cfg.act_dtype, scale_dtype=cfg.scale_dtype, tile_m=tile_m,
                           strict_blocks=strict, weight_layout=layout, n_group=cfg.n_group,
                           topk_group=cfg.topk_group, routed_scaling_factor=cfg.routed_scale,
-                          e_score_correction_bias=ebias)
+                          e_score_correction_bias=ebias,
+                          compute_mode="int8" if cfg.int8 else "float")
 
 
 class DeviceInputs:

@@ -259,3 +259,22 @@ def test_mxfp4_params(lib):
     p = good(**mx)
     p.scale_dtype = 3
     assert status(p) == _lib.QMOE_ERR_DTYPE
+
+
+def test_int8_tier_params(lib):
+    """compute_mode int8 needs per-block scales; unknown modes are rejected; the workspace
+    grows by the rounded copy of x; qmoe_quantize_act checks its shape and needs
+    block_size > 0 (no device is touched on these paths)."""
+    assert status(good(compute_mode="int8")) == _lib.QMOE_OK
+    assert status(good(compute_mode="int8", block_size=0)) == _lib.QMOE_ERR_INVALID
+    p = good()
+    p.compute_mode = 2
+    assert status(p) == _lib.QMOE_ERR_INVALID
+    f, q = good(), good(compute_mode="int8")
+    xbytes = q.num_tokens * q.hidden_size * 2
+    assert lib.qmoe_workspace_size(q) >= lib.qmoe_workspace_size(f) + xbytes
+    assert lib.qmoe_quantize_act(good(), 1 << 20, 0, 64, 1 << 20, None) == _lib.QMOE_OK
+    assert lib.qmoe_quantize_act(good(), 1 << 20, 4, 0, 1 << 20, None) == _lib.QMOE_ERR_SHAPE
+    assert lib.qmoe_quantize_act(good(), None, 4, 64, 1 << 20, None) == _lib.QMOE_ERR_UNBOUND
+    assert lib.qmoe_quantize_act(good(block_size=0), 1 << 20, 4, 64, 1 << 20,
+                                 None) == _lib.QMOE_ERR_INVALID

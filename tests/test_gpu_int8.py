@@ -1,0 +1,91 @@
+"""The int8 activation tier on the GPU (ClikaRT "QMoEWoQ" page, class description: the
+activation is rounded to per-block int8 before the dot).
+
+* the rounding itself (qmoe_quantize_act) bit for bit against the oracle's, both dtypes,
+  ragged last blocks, in place and out of place;
+* the forward with compute_mode int8 against the oracle's int8 forward on the decode,
+  prefill, many-expert and MX FP4 shapes, at the bf16 tolerance.
+
+fp32 activations are checked through the rounding alone: the codes of h are decided from h,
+and an fp32 h that differs from the oracle's fp64 h in its last bit (summation order) can
+move one code by a step, which is worth more than the fp32 tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_softmax_amd as qm
+from synth import configs
+from synth.gen import store
+from tests.gpu_helpers import dev, host, params_for
+from tests.test_gpu_parity import check_forward, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(rng, rows, cols, bs):
+    nb = -(-cols // bs)
+    mag = 2.0 ** rng.integers(-12, 12, (rows, nb))
+    v = rng.normal(0, 1, (rows, cols)) * np.repeat(mag, bs, axis=1)[:, :cols]
+    if rows > 0:
+        v[0, :min(cols, bs)] = 0.0
+    if rows > 1:
+        w = min(cols, bs)
+        v[1, 0] = 127.0 * 2.0 ** -3
+        v[1, 1:w] = (rng.integers(-126, 126, w - 1) + 0.5) * 2.0 ** -3
+    if rows > 2:
+        v[2, 0] = 127.5 * 2.0 ** -3
+    return v
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,bs", [(1, 2880, 32), (64, 2880, 128), (300, 2048, 16),
+                                          (7, 80, 32), (5, 200, 64), (3, 81, 16),
+                                          (0, 64, 32)])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_quantize_act_bit_exact(act, rows, cols, bs, inplace):
+    say("quantize", act, rows, cols, bs, "inplace" if inplace else "")
+    rng = np.random.default_rng(rows * 7 + cols + bs)
+    # the rounding reads block_size and the activation dtype of the parameter block; its
+    # other shapes only need to be valid ones
+    cfg = configs.tiny(act_dtype=act, block_size=bs)
+    v = store(_rows(rng, rows, cols, bs), act)
+    p = params_for(cfg, max(rows, 1))
+    x = dev(v, act)
+    out = x if inplace else torch.empty_like(x)
+    qm.qmoe_quantize_act(p, x, out)
+    torch.cuda.synchronize()
+    want = oracle.int8_round(cfg, v) if rows else v
+    assert np.array_equal(host(out), want)
+
+
+def test_quantize_act_rejects_per_row_scales():
+    cfg = configs.tiny(act_dtype="bf16", block_size=0, H=64)
+    p = params_for(cfg, 4)
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(qm.QmoeError):
+        qm.qmoe_quantize_act(p, x, x)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("layout", ["rows", "tiles"])
+def test_forward_int8_c2_decode(T, layout):
+    check_forward(configs.C2_INT8, T, shared=(T == 8), layout=layout)
+
+
+def test_forward_int8_c4_many_experts_ragged_blocks():
+    check_forward(configs.C4_INT8, 512, sample=16, layout="tiles")
+
+
+@pytest.mark.parametrize("bits,bs", [(4, 32), (8, 128), (4, 16)])
+@pytest.mark.parametrize("T", [256, 4096])
+def test_forward_int8_c5(T, bits, bs):
+    check_forward(configs.c5_point(bits, bs).with_(int8=True), T, sample=6, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_forward_int8_mxfp4_c2(T):
+    check_forward(configs.C2_MX_INT8, T, layout="tiles")

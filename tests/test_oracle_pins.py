@@ -56,6 +56,14 @@ BRUTE_CASES = {
                                                 block_size=32, H=96, I=64, fusion=1,
                                                 fc1_bias=True, fc2_bias=True, limit=7.0,
                                                 scale_lo=0.01, scale_hi=0.2),
+    "bf16-int8-interleaved-bs32-bias": configs.tiny(
+        act_dtype="bf16", scale_dtype="bf16", fusion=1, bits=4, block_size=32, fc1_bias=True,
+        fc2_bias=True, limit=7.0, int8=True),
+    "f32-int8-ragged-bs32-K80": configs.tiny(H=80, I=48, block_size=32, limit=2.0,
+                                             scale_lo=0.05, scale_hi=0.1, int8=True),
+    "bf16-int8-mxfp4-separate": configs.tiny(act_dtype="bf16", scale_dtype="e8m0", bits=4,
+                                             block_size=32, H=96, I=64, fusion=0,
+                                             scale_lo=0.01, scale_hi=0.2, int8=True),
 }
 
 
@@ -438,6 +446,85 @@ def test_stage_functions_compose_to_forward():
     ref = _fwd(cfg, inp)
     # only the f32 storage of h, y and w separates the two
     assert np.max(np.abs(out64 - ref)) < 1e-5 * rms(ref)
+
+
+# --------------------------------------------------------------------------- int8 tier
+
+def _int8_rows(rng, rows, cols, bs):
+    """Rows whose blocks span many magnitudes, with exact ties and block maxima that sit
+    on the 127 * 2^e boundaries."""
+    nb = -(-cols // bs)
+    mag = 2.0 ** rng.integers(-20, 20, (rows, nb))
+    v = rng.normal(0, 1, (rows, cols)) * np.repeat(mag, bs, axis=1)[:, :cols]
+    v[0, :min(cols, bs)] = 0.0                 # an all-zero block
+    # row 1: exact ties (n + 1/2) * 2^-3 under a block maximum of 127 * 2^-3
+    if rows > 1:
+        v[1, 0] = 127.0 * 2.0 ** -3          # the largest that keeps e = -3
+        v[1, 1:min(cols, bs)] = (rng.integers(-126, 126, min(cols, bs) - 1) + 0.5) * 2.0 ** -3
+    if rows > 2:
+        v[2, 0] = 127.5 * 2.0 ** -3          # just too large: e = -2
+    return v
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("bs,cols", [(32, 96), (32, 80), (16, 16), (64, 200), (128, 130)])
+def test_int8_round_matches_scale_search(act, bs, cols):
+    rng = np.random.default_rng(bs * 1000 + cols)
+    cfg = configs.tiny(act_dtype=act, block_size=bs, H=cols)
+    v = store(_int8_rows(rng, 9, cols, bs), act)
+    got = as_f32(oracle.int8_round(cfg, v), act).astype(np.float64)
+    want = bruteforce.int8_round(as_f32(v, act).astype(np.float64), bs)
+    assert np.array_equal(got, want)
+
+
+def test_int8_round_properties():
+    rng = np.random.default_rng(3)
+    bs, cols = 32, 100
+    cfg = configs.tiny(act_dtype="f32", block_size=bs, H=cols)
+    v = store(_int8_rows(rng, 40, cols, bs), "f32")
+    out = oracle.int8_round(cfg, v)
+    # idempotent: a rounded row is its own rounding
+    assert np.array_equal(oracle.int8_round(cfg, out), out)
+    x = v.astype(np.float64)
+    q = out.astype(np.float64)
+    for r in range(x.shape[0]):
+        for b0 in range(0, cols, bs):
+            blk, qb = x[r, b0:b0 + bs], q[r, b0:b0 + bs]
+            a = np.max(np.abs(blk))
+            if a == 0:
+                assert not qb.any()
+                continue
+            # the scale: the power of two that makes the largest code land in [64, 127]
+            e = math.frexp(np.max(np.abs(qb)))[1] - 7
+            codes = qb / 2.0 ** e
+            assert np.array_equal(codes, np.round(codes))
+            assert 64 <= np.max(np.abs(codes)) <= 127
+            # the error of each element is at most half a code step
+            assert np.max(np.abs(qb - blk)) <= 2.0 ** (e - 1)
+
+
+def test_int8_round_by_hand():
+    # one block of three: max 1.0 -> e = -6 (127/64 >= 1 > 127/128): codes 64, -32 and
+    # 0.3 * 64 = 19.2 -> 19; a second block of two: max 3.0 -> e = -5 (127/32 >= 3 > 127/64),
+    # codes 2.5 * 32 = 80 and 3 * 32 = 96 exactly
+    cfg = configs.tiny(act_dtype="f32", block_size=3, H=5)
+    v = np.array([[1.0, -0.5, 0.3, 2.5, -3.0]], np.float32)
+    got = oracle.int8_round(cfg, v)[0].astype(np.float64)
+    assert got.tolist() == [1.0, -0.5, 19 / 64, 2.5, -3.0]
+    # a tie: 2.5 * 2^-6 is half way between codes 2 and 3 under max 1.0; ties to even -> 2
+    v = np.array([[1.0, 2.5 / 64, 3.5 / 64]], np.float32)
+    got = oracle.int8_round(configs.tiny(act_dtype="f32", block_size=3, H=3), v)[0]
+    assert got.astype(np.float64).tolist() == [1.0, 2 / 64, 4 / 64]
+
+
+def test_int8_forward_differs_from_float_forward():
+    # the tier changes the result (it is not silently off), by about the size int8 codes allow
+    cfg = configs.tiny(act_dtype="f32", block_size=16, fusion=2)
+    inp = gen.make_inputs(cfg, 5)
+    f, _ = oracle.forward(cfg, inp)
+    q, _ = oracle.forward(cfg.with_(int8=True), inp)
+    d = rms(q - f) / rms(f)
+    assert 1e-4 < d < 5e-2
 
 
 # --------------------------------------------------------------------------- rounding

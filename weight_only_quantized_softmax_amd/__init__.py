@@ -21,12 +21,13 @@ __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
            "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
-           "qmoe_time_next_gemm", "qmoe_linear_woq", "linear_params", "linear_woq", "forward",
+           "qmoe_time_next_gemm", "qmoe_linear_woq", "qmoe_quantize_act", "linear_params", "linear_woq", "forward",
            "QmoeError", "QmoeParams"]
 
 _DT = {"f32": QMOE_F32, "bf16": QMOE_BF16, "e8m0": QMOE_E8M0}
 _LAYOUT = {"rows": QMOE_LAYOUT_ROWS, "tiles": QMOE_LAYOUT_TILES}
 _WHICH = {"fc1": QMOE_FC1, "fc2": QMOE_FC2, "fc3": QMOE_FC3}
+_COMPUTE = {"float": 0, "int8": 1}
 _TORCH_DT = {QMOE_F32: torch.float32, QMOE_BF16: torch.bfloat16}
 
 Stack = Optional[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]]
@@ -40,7 +41,8 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                 scale_dtype: str = "bf16", tile_m: int = 0,
                 strict_blocks: bool = False, weight_layout: str = "rows", n_group: int = 0,
                 topk_group: int = 0, routed_scaling_factor: float = 1.0,
-                e_score_correction_bias: Optional[torch.Tensor] = None) -> QmoeParams:
+                e_score_correction_bias: Optional[torch.Tensor] = None,
+                compute_mode: str = "float") -> QmoeParams:
     """The parameter block. e_score_correction_bias: a device tensor [E] in the activation
     dtype (the block keeps its address, so the tensor must outlive the calls)."""
     bias = None if e_score_correction_bias is None else _ptr(e_score_correction_bias,
@@ -56,7 +58,7 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                       strict_blocks=int(bool(strict_blocks)),
                       weight_layout=_LAYOUT[weight_layout], n_group=n_group,
                       topk_group=topk_group, routed_scaling_factor=routed_scaling_factor,
-                      e_score_correction_bias=bias)
+                      e_score_correction_bias=bias, compute_mode=_COMPUTE[compute_mode])
 
 
 def _ptr(t: Optional[torch.Tensor], name: str):
@@ -210,6 +212,14 @@ def linear_woq(p: QmoeParams, x: torch.Tensor, w: Stack, stream=None) -> torch.T
     y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
     qmoe_linear_woq(p, x2, w, y.view(-1, N), stream)
     return y
+
+
+def qmoe_quantize_act(p: QmoeParams, x: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """The int8 activation tier's per-block rounding of the rows of x into out ([rows, cols])."""
+    if x.dim() != 2 or tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype:
+        raise QmoeError(QMOE_ERR_SHAPE, "qmoe_quantize_act: x and out must be [rows, cols] alike")
+    rows, cols = x.shape
+    check(load().qmoe_quantize_act(p, _ptr(x, "in"), rows, cols, _ptr(out, "out"), _stream(stream)))
 
 
 def qmoe_time_next_gemm(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:

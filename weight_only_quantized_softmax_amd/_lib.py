@@ -30,7 +30,8 @@ class QmoeParams(ctypes.Structure):
                 ("strict_blocks", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float),
-                ("e_score_correction_bias", ctypes.c_void_p)]
+                ("e_score_correction_bias", ctypes.c_void_p),
+                ("compute_mode", ctypes.c_int32)]
 
 
 class QmoeStack(ctypes.Structure):
@@ -42,7 +43,7 @@ EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
            "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
-           "qmoe_time_next_gemm", "qmoe_last_error")
+           "qmoe_quantize_act", "qmoe_time_next_gemm", "qmoe_last_error")
 
 _lib = None
 
@@ -80,6 +81,8 @@ def load() -> ctypes.CDLL:
     L.qmoe_pack_stack.argtypes, L.qmoe_pack_stack.restype = [P, ctypes.c_int32, vp, vp, vp], st
     L.qmoe_linear_woq.argtypes = [P, vp, QmoeStack, vp, vp]
     L.qmoe_linear_woq.restype = st
+    L.qmoe_quantize_act.argtypes = [P, vp, i64, i64, vp, vp]
+    L.qmoe_quantize_act.restype = st
     L.qmoe_time_next_gemm.argtypes, L.qmoe_time_next_gemm.restype = [vp, vp], st
     L.qmoe_last_error.argtypes, L.qmoe_last_error.restype = [], ctypes.c_char_p
     _lib = L

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_bf16_tiled.hip", "gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_prefill_blk_tiled.hip", "gemm_f32.hip", "combine.hip", "pack.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_bf16_tiled.hip", "gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_prefill_blk_tiled.hip", "gemm_f32.hip", "combine.hip", "pack.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -114,6 +114,10 @@ qmoe_status validate(const qmoe_params* p) {
   }
   if (!std::isfinite(p->routed_scaling_factor))
     return fail(QMOE_ERR_INVALID, "routed_scaling_factor must be finite");
+  if (p->compute_mode != QMOE_COMPUTE_FLOAT && p->compute_mode != QMOE_COMPUTE_INT8)
+    return fail(QMOE_ERR_INVALID, "compute_mode %d unknown", p->compute_mode);
+  if (p->compute_mode == QMOE_COMPUTE_INT8 && p->block_size == 0)
+    return fail(QMOE_ERR_INVALID, "the int8 activation tier needs block_size > 0");
   if (p->expert_weight_bits != 4 && p->expert_weight_bits != 8)
     return fail(QMOE_ERR_INVALID, "expert_weight_bits %d is not 4 or 8", p->expert_weight_bits);
   if (p->block_size != 0 && (!is_pow2(p->block_size) || p->block_size < 16))
@@ -222,6 +226,7 @@ struct Workspace {
   void* perm_scratch;
   void* h;
   float* y;
+  void* xq;  // the int8-tier copy of x (compute_mode QMOE_COMPUTE_INT8)
   size_t bytes;
 };
 
@@ -247,6 +252,7 @@ Workspace carve(const qmoe_params* p, char* base) {
   w.perm_scratch = take(qmoe::permute_scratch_bytes(A, static_cast<int>(p->num_experts)));
   w.h = take(rows * p->inter_size * act);
   w.y = reinterpret_cast<float*>(take(rows * p->hidden_size * 4));
+  if (p->compute_mode == QMOE_COMPUTE_INT8) w.xq = take(p->num_tokens * p->hidden_size * act);
   w.bytes = off;
   return w;
 }
@@ -555,7 +561,23 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                              w.perm_scratch, s),
         "permute launch"));
   }
-  QMOE_TRY(run_fc1(p, input, w.sorted_assign, w.tiles, w.num_tiles, fc1, fc3, w.h, s));
+  const bool int8 = p->compute_mode == QMOE_COMPUTE_INT8;
+  const bool abf = p->act_dtype == QMOE_BF16;
+  const void* x = input;
+  if (int8) {
+    QMOE_TRY(device_status(qmoe::launch_quantize_blocks(input, w.xq, abf, p->num_tokens,
+                                                        static_cast<int>(p->hidden_size),
+                                                        p->block_size, nullptr, 0, s),
+                           "quantize x launch"));
+    x = w.xq;
+  }
+  QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, fc1, fc3, w.h, s));
+  if (int8)
+    QMOE_TRY(device_status(qmoe::launch_quantize_blocks(w.h, w.h, abf, max_rows_of(p),
+                                                        static_cast<int>(p->inter_size),
+                                                        p->block_size, w.num_tiles,
+                                                        static_cast<int>(tile_m_of(p)), s),
+                           "quantize h launch"));
   QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s));
   QMOE_TRY(device_status(
       qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output,
@@ -607,6 +629,22 @@ qmoe_status qmoe_linear_woq(const qmoe_params* p, const void* x, qmoe_stack w, v
   QMOE_TRY(check_stack(w, "weight"));
   QMOE_TRY(need(y, "y"));
   return run_linear(p, x, w, y, static_cast<hipStream_t>(stream));
+}
+
+qmoe_status qmoe_quantize_act(const qmoe_params* p, const void* in, int64_t rows, int64_t cols,
+                              void* out, void* stream) {
+  QMOE_TRY(validate(p));
+  if (p->block_size == 0)
+    return fail(QMOE_ERR_INVALID, "the int8 activation tier needs block_size > 0");
+  if (rows < 0 || cols < 1 || cols >= (int64_t(1) << 31))
+    return fail(QMOE_ERR_SHAPE, "rows %lld, cols %lld", (long long)rows, (long long)cols);
+  if (rows == 0) return ok();
+  QMOE_TRY(need(in, "in"));
+  QMOE_TRY(need(out, "out"));
+  return device_status(qmoe::launch_quantize_blocks(in, out, p->act_dtype == QMOE_BF16, rows,
+                                                    static_cast<int>(cols), p->block_size, nullptr, 0,
+                                                    static_cast<hipStream_t>(stream)),
+                       "quantize launch");
 }
 
 qmoe_status qmoe_time_next_gemm(void* start_event, void* stop_event) {

@@ -158,6 +158,12 @@ hipError_t launch_gemm_bf16_prefill_blk_tiled(const GemmArgs& g, int mode, int b
 hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                            int64_t max_tiles, hipStream_t s);
 
+// int8 activation tier: rows x K elements rounded to per-block int8 codes times a power of
+// two (quant.hip); in may equal out.
+// num_tiles (device, may be null): only the first *num_tiles * tile_m rows are rounded.
+hipError_t launch_quantize_blocks(const void* in, void* out, bool bf16, int64_t rows, int K,
+                                  int bs, const int32_t* num_tiles, int tile_m, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
                           const void* shared, void* out, bool bf16, int T, int H, int k,
                           hipStream_t s);
