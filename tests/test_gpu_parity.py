@@ -495,3 +495,21 @@ def test_forward_zero_tokens():
     w = torch.empty(16, dtype=torch.uint8, device="cuda")
     out = qm.forward(p, x, lg, (w, w, None), (w, w, None))
     assert out.shape == (0, cfg.H)
+
+
+@pytest.mark.parametrize("E,k,T,variant", [
+    (8, 2, 64, None), (64, 4, 17, None), (64, 6, 64, "bias"), (200, 8, 40, None),
+    (256, 4, 64, "groups"), (512, 4, 16, None), (512, 8, 17, None), (384, 2, 16, "bias")])
+def test_forward_fused_routing_sizes(E, k, T, variant):
+    # qmoe_forward routes and groups in one kernel up to 64 tokens (16 above 256 experts,
+    # one token a wave): both sides of those edges, routing variants included
+    kw = dict(E=E, k=k, T=T, variant=variant)
+    say("fused routing", kw)
+    extra = {}
+    if variant == "bias":
+        extra = dict(score_bias=True)
+    elif variant == "groups":
+        extra = dict(n_group=8, topk_group=3, score_bias=True, routed_scale=2.0)
+    cfg = configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64, bits=4,
+                       block_size=32, logit_sigma=2.0, fusion=1, **extra)
+    check_forward(cfg, T)

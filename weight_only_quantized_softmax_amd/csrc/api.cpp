@@ -541,7 +541,7 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
     return fail(QMOE_ERR_INVALID, "workspace %zu bytes < %zu", workspace_bytes, w.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t A = p->num_tokens * p->k;
-  if (qmoe::route_permute_fits(p->num_tokens, A)) {
+  if (qmoe::route_permute_fits(p->num_tokens, A, p->num_experts, p->k)) {
     QMOE_TRY(device_status(
         qmoe::launch_route_permute(router_logits, p->act_dtype == QMOE_BF16,
                                    static_cast<int>(p->num_tokens), static_cast<int>(p->num_experts),

@@ -113,10 +113,10 @@ struct RouteOpts {
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
                         const RouteOpts& o, int32_t* ids, float* w, hipStream_t s);
 
-// One launch for routing and grouping: batches of at most this many tokens (and at most
-// kPermFusedMax assignments).
-constexpr int64_t kRoutePermuteMaxT = 16;
-bool route_permute_fits(int64_t T, int64_t A);
+// One launch for routing and grouping: batches that one 1024-lane block routes in one pass
+// (64 tokens when a token takes a 16-lane row, 16 when it takes a wave) and of at most
+// kPermFusedMax assignments.
+bool route_permute_fits(int64_t T, int64_t A, int64_t E, int64_t k);
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
                                 const RouteOpts& o, int M, int32_t* ids, float* w, int32_t* counts,
                                 int32_t* padded_offsets, int32_t* sorted_assign,

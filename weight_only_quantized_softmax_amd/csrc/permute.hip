@@ -136,11 +136,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(
   block_rank_scatter(ids, 0, A, E, ebits, run, wc, sorted_assign, assign_pos);
 }
 
-// Routing and grouping of a small batch in one block: the block's waves route the tokens
-// in turn (route.h), the routed ids reach every wave through the barrier, and the block
-// then groups them as permute_fused_kernel does. One launch in place of two where the
-// batch is small enough that one block routes it quickly.
-template <typename TA, int V>
+// Routing and grouping of a small batch in one block: each 16-lane row (or each wave, for
+// more than 256 experts or k > 16) of the block routes one token (route.h), the routed ids
+// reach every wave through the barrier, and the block then groups them as
+// permute_fused_kernel does. One launch in place of two where the batch fits one pass.
+template <typename TA, int G, int V>
 __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
     const TA* __restrict__ logits, int T, int E, int k, int normalize, RouteOpts o, int ebits,
     int M, int32_t* ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
   int* run = cnt + E;             // [E]
   int* scan_tmp = run + E;        // [kPermWaves + 1]
   int* wc = scan_tmp + kPermWaves + 1;  // [kPermWaves][E]
-  const int wave = threadIdx.x / kWave;
-  for (int t = wave; t < T; t += kPermWaves) route_token<TA, V>(logits, t, E, k, normalize, o, ids, topk_w);
+  const int t = threadIdx.x / G;  // one token per group of G lanes
+  if (t < T) route_token<TA, G, V>(logits, t, E, k, normalize, o, ids, topk_w);
   for (int i = threadIdx.x; i < E; i += kPermThreads) cnt[i] = 0;
   __syncthreads();  // the ids written by each wave's lane 0 are visible to the whole block
   const int64_t A = static_cast<int64_t>(T) * k;
@@ -232,18 +232,37 @@ size_t permute_scratch_bytes(int64_t A, int E) {
   return static_cast<size_t>(nblk) * E * sizeof(int32_t);
 }
 
-bool route_permute_fits(int64_t T, int64_t A) { return A <= kPermFusedMax && T <= kRoutePermuteMaxT; }
+bool route_permute_fits(int64_t T, int64_t A, int64_t E, int64_t k) {
+  const int G = route_by_rows(static_cast<int>(E), static_cast<int>(k)) ? 16 : kWave;
+  return A <= kPermFusedMax && T <= kPermThreads / G;
+}
 
-template <typename TA, int V>
+template <typename TA, int G, int V>
 static void launch_rp(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
                       int M, int32_t* ids,
                       float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                       int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
   const size_t lds = (2 * E + kPermWaves + 1 + kPermWaves * E) * sizeof(int);
-  route_permute_kernel<TA, V><<<1, kPermThreads, lds, s>>>(logits, T, E, k, normalize, o, bits_for(E), M,
-                                                          ids, w, counts, padded_offsets,
-                                                          sorted_assign, assign_pos, tile_list,
-                                                          num_tiles);
+  route_permute_kernel<TA, G, V><<<1, kPermThreads, lds, s>>>(
+      logits, T, E, k, normalize, o, bits_for(E), M, ids, w, counts, padded_offsets,
+      sorted_assign, assign_pos, tile_list, num_tiles);
+}
+
+template <typename TA, int G>
+static void launch_rp_g(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
+                        int M, int32_t* ids,
+                        float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
+                        int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
+  const int V = (E + G - 1) / G;
+#define QMOE_RP(VV) launch_rp<TA, G, VV>(logits, T, E, k, normalize, o, M, ids, w, counts, \
+                                         padded_offsets, sorted_assign, assign_pos, tile_list, \
+                                         num_tiles, s)
+  if (V <= 1) QMOE_RP(1);
+  else if (V <= 2) QMOE_RP(2);
+  else if (V <= 4) QMOE_RP(4);
+  else if (V <= 8) QMOE_RP(8);
+  else QMOE_RP(16);
+#undef QMOE_RP
 }
 
 template <typename TA>
@@ -251,15 +270,12 @@ static void launch_rp_t(const TA* logits, int T, int E, int k, int normalize, co
                         int M, int32_t* ids,
                         float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
-  const int V = (E + 63) / 64;
-#define QMOE_RP(VV) launch_rp<TA, VV>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets, \
-                                      sorted_assign, assign_pos, tile_list, num_tiles, s)
-  if (V <= 1) QMOE_RP(1);
-  else if (V <= 2) QMOE_RP(2);
-  else if (V <= 4) QMOE_RP(4);
-  else if (V <= 8) QMOE_RP(8);
-  else QMOE_RP(16);
-#undef QMOE_RP
+  if (route_by_rows(E, k))
+    launch_rp_g<TA, 16>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets,
+                        sorted_assign, assign_pos, tile_list, num_tiles, s);
+  else
+    launch_rp_g<TA, kWave>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets,
+                           sorted_assign, assign_pos, tile_list, num_tiles, s);
 }
 
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,

@@ -5,11 +5,14 @@
 // combine under the router weights (routing_mode "softmax_topk", renormalize);
 // graiphic "QMoE" page: attributes k and normalize_routing_weights.
 //
-// Lane l holds the logits of experts [l*V, l*V+V), so a lower lane always holds lower
-// expert indices. Selection works on an order-preserving integer image of the logit
-// (after folding -0 into +0), reduced across the wave with DPP/swizzle max steps; among
-// lanes holding the maximum, the lowest lane wins (ballot + count-trailing-zeros), and
-// inside a lane the lowest slot, which gives "equal logits: lower index first".
+// A token is routed by a group of G lanes: a whole wave (G = 64), or one 16-lane DPP row
+// (G = 16, four tokens a wave, where E <= 256 and k <= 16). Lane l of the group holds the
+// logits of experts [l*V, l*V+V), so a lower lane always holds lower expert indices.
+// Selection works on an order-preserving integer image of the logit (after folding -0
+// into +0), reduced across the group with DPP max steps (and a swizzle and readlanes for
+// the whole wave); among lanes holding the maximum, the lowest lane wins (ballot +
+// count-trailing-zeros), and inside a lane the lowest slot, which gives "equal logits:
+// lower index first".
 #pragma once
 
 #include "common.h"
@@ -28,8 +31,62 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float(b);
 }
 
-// Routes token t (the whole wave calls this with the same t): writes its k expert ids and
-// weights to topk_ids[t*k ..] and topk_w[t*k ..] from lane 0.
+// Reductions over the G lanes routing one token; every lane of the group gets the result.
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(G == 16 || G == 64, "a token is routed by a DPP row or a wave");
+  if constexpr (G == 64) {
+    return wave_max_u32(v);
+  } else {
+    v = max(v, dpp<QMOE_DPP_QUAD_1032>(v));
+    v = max(v, dpp<QMOE_DPP_QUAD_2301>(v));
+    v = max(v, dpp<QMOE_DPP_ROW_HALF_MIRROR>(v));
+    return max(v, dpp<QMOE_DPP_ROW_MIRROR>(v));
+  }
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum_f32(float f) {
+  if constexpr (G == 64) return wave_sum_f32(f);
+  else return row16_sum_f32(f);
+}
+
+// The value of x in lane src (an absolute lane of the caller's group).
+template <int G>
+__device__ __forceinline__ uint32_t group_read(uint32_t x, int src) {
+  if constexpr (G == 64) return __builtin_amdgcn_readlane(x, src);
+  else return static_cast<uint32_t>(__shfl(static_cast<int>(x), src));
+}
+
+// The logits of one token as its group holds them.
+template <int V>
+struct TokenLogits {
+  float val[V];      // the logits (-inf past E)
+  uint32_t key[V];   // selection keys: order_key(logit + bias), 0 past E
+  uint32_t lkmax;    // the lane's largest order_key of the logits alone
+};
+
+// Loads token t's logits (and the selection bias) into the group's registers.
+template <typename TA, int G, int V>
+__device__ __forceinline__ void load_token(const TA* logits, int t, int E, const RouteOpts& o,
+                                           TokenLogits<V>& r) {
+  const int gl = lane_id() & (G - 1);
+  const TA* row = logits + static_cast<int64_t>(t) * E;
+  const TA* bias = static_cast<const TA*>(o.bias);
+  r.lkmax = 0u;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = gl * V + v;
+    r.val[v] = e < E ? load_elem(row, e) : -INFINITY;
+    r.lkmax = max(r.lkmax, e < E ? order_key(r.val[v]) : 0u);  // 0 is below every finite key
+    const float sel = (bias != nullptr && e < E) ? r.val[v] + load_elem(bias, e) : r.val[v];
+    r.key[v] = e < E ? order_key(sel) : 0u;
+  }
+}
+
+// Routes token t from its loaded logits (all G lanes of the group call this with the same
+// t): lanes j < k of the group write its j-th expert id and weight to topk_ids[t*k + j] and
+// topk_w[t*k + j].
 // Routing variants (RouteOpts; CLIKA "MoE" page routing kwargs n_group, topk_group,
 // routed_scaling_factor; ClikaRT "QMoEWoQ" page, the aux-free selection bias
 // e_score_correction_bias [E]): the bias is added to the logits in fp32 for the selection
@@ -38,31 +95,23 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // groups (ties to the lower group) are kept and the k experts are chosen among theirs;
 // the weights are the softmax over all E logits at the chosen experts, renormalised if
 // asked, then multiplied by the scaling factor.
-template <typename TA, int V>
-__device__ __forceinline__ void route_token(const TA* logits, int t, int E, int k, int normalize,
-                                            const RouteOpts& o, int32_t* topk_ids, float* topk_w) {
+template <int G, int V>
+__device__ __forceinline__ void route_loaded(TokenLogits<V>& r, int t, int E, int k,
+                                             int normalize, const RouteOpts& o,
+                                             int32_t* topk_ids, float* topk_w) {
   const int lane = lane_id();
-  float val[V];
-  uint32_t key[V];  // selection key per slot
-  uint32_t lkmax = 0u;
-  const TA* row = logits + static_cast<int64_t>(t) * E;
-  const TA* bias = static_cast<const TA*>(o.bias);
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = lane * V + v;
-    val[v] = e < E ? load_elem(row, e) : -INFINITY;
-    lkmax = max(lkmax, e < E ? order_key(val[v]) : 0u);  // 0 is below every finite key
-    const float sel = (bias != nullptr && e < E) ? val[v] + load_elem(bias, e) : val[v];
-    key[v] = e < E ? order_key(sel) : 0u;
-  }
+  const int gl = lane & (G - 1);
+  const int gbase = lane - gl;
+  float* val = r.val;
+  uint32_t* key = r.key;
 
   // Softmax over all E: the maximum and the normaliser come first.
-  const float m = key_value(wave_max_u32(lkmax));
+  const float m = key_value(group_max_u32<G>(r.lkmax));
   float part = 0.f;
 #pragma unroll
   for (int v = 0; v < V; ++v)
-    if (lane * V + v < E) part += expf(val[v] - m);
-  const float denom = wave_sum_f32(part);
+    if (gl * V + v < E) part += expf(val[v] - m);
+  const float denom = group_sum_f32<G>(part);
 
   if (o.n_group > 1) {
     // group scores (the same in every lane), then the kept groups
@@ -74,13 +123,13 @@ __device__ __forceinline__ void route_token(const TA* logits, int t, int E, int 
       uint32_t local = 0u;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const int e = lane * V + v;
+        const int e = gl * V + v;
         if (e < E && e / gsize == gi) local = max(local, key[v]);
       }
-      gsc[gi] = wave_max_u32(local);
+      gsc[gi] = group_max_u32<G>(local);
     }
     uint32_t keep = 0u;
-    for (int r = 0; r < o.topk_group; ++r) {
+    for (int rr = 0; rr < o.topk_group; ++rr) {
       int bg = -1;
       uint32_t bs = 0u;
 #pragma unroll
@@ -92,14 +141,15 @@ __device__ __forceinline__ void route_token(const TA* logits, int t, int E, int 
     }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int e = lane * V + v;
+      const int e = gl * V + v;
       if (e < E && !((keep >> (e / gsize)) & 1u)) key[v] = 0u;
     }
   }
 
-  int32_t* ids_out = topk_ids + static_cast<int64_t>(t) * k;
-  float* w_out = topk_w + static_cast<int64_t>(t) * k;
-  float sum = 0.f;
+  // slot j's id and weight stay in lane j of the group (k <= G), so nothing is read back
+  float sum = 0.f, my_w = 0.f;
+  int my_id = 0;
+  const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
   for (int j = 0; j < k; ++j) {
     uint32_t best = key[0];
     int bslot = 0;
@@ -110,12 +160,12 @@ __device__ __forceinline__ void route_token(const TA* logits, int t, int E, int 
 #pragma unroll
     for (int v = 1; v < V; ++v)
       if (v == bslot) bval = val[v];
-    const uint32_t wmax = wave_max_u32(best);
-    const uint64_t holders = ballot(best == wmax);
-    const int src = __builtin_ctzll(holders);
-    const int idx = __builtin_amdgcn_readlane(lane * V + bslot, src);
+    const uint32_t gmax = group_max_u32<G>(best);
+    const uint64_t holders = (ballot(best == gmax) >> gbase) & gmask;
+    const int src = gbase + __builtin_ctzll(holders);
+    const int idx = static_cast<int>(group_read<G>(static_cast<uint32_t>(gl * V + bslot), src));
     // the chosen expert's own logit (the weight ignores the selection bias)
-    const float lv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(bval), src));
+    const float lv = __uint_as_float(group_read<G>(__float_as_uint(bval), src));
     if (lane == src) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
@@ -123,18 +173,30 @@ __device__ __forceinline__ void route_token(const TA* logits, int t, int E, int 
     }
     const float w = expf(lv - m) / denom;
     sum += w;
-    if (lane == 0) {
-      ids_out[j] = idx;
-      w_out[j] = w;
+    if (gl == j) {
+      my_w = w;
+      my_id = idx;
     }
   }
-  if (lane == 0) {
-    for (int j = 0; j < k; ++j) {
-      float w = normalize ? w_out[j] / sum : w_out[j];
-      if (o.scale != 1.0f) w *= o.scale;
-      w_out[j] = w;
-    }
+  if (gl < k) {
+    float w = normalize ? my_w / sum : my_w;
+    if (o.scale != 1.0f) w *= o.scale;
+    topk_ids[static_cast<int64_t>(t) * k + gl] = my_id;
+    topk_w[static_cast<int64_t>(t) * k + gl] = w;
   }
 }
+
+// Loads and routes token t.
+template <typename TA, int G, int V>
+__device__ __forceinline__ void route_token(const TA* logits, int t, int E, int k, int normalize,
+                                            const RouteOpts& o, int32_t* topk_ids, float* topk_w) {
+  TokenLogits<V> r;
+  load_token<TA, G, V>(logits, t, E, o, r);
+  route_loaded<G, V>(r, t, E, k, normalize, o, topk_ids, topk_w);
+}
+
+// A token takes one 16-lane row where its experts fit 16 slots a lane and its k slots fit
+// the row's lanes; else a whole wave.
+inline bool route_by_rows(int E, int k) { return E <= 256 && k <= 16; }
 
 }  // namespace qmoe
