@@ -546,7 +546,7 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
         qmoe::launch_route_permute(router_logits, p->act_dtype == QMOE_BF16,
                                    static_cast<int>(p->num_tokens), static_cast<int>(p->num_experts),
                                    static_cast<int>(p->k), p->normalize_routing_weights,
-                                   route_opts(p), tile_m_of(p), w.topk_ids, w.topk_w, w.counts, w.offsets,
+                                   route_opts(p), tile_m_of(p), w.topk_w, w.counts, w.offsets,
                                    w.sorted_assign, w.assign_pos, w.tiles, w.num_tiles, s),
         "route+permute launch"));
   } else {

@@ -115,10 +115,11 @@ hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int 
 
 // One launch for routing and grouping: batches that one 1024-lane block routes in one pass
 // (64 tokens when a token takes a 16-lane row, 16 when it takes a wave) and of at most
-// kPermFusedMax assignments.
+// kPermFusedMax assignments. The expert ids stay inside the kernel; the weights and the
+// grouping are written as by launch_route and launch_permute.
 bool route_permute_fits(int64_t T, int64_t A, int64_t E, int64_t k);
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
-                                const RouteOpts& o, int M, int32_t* ids, float* w, int32_t* counts,
+                                const RouteOpts& o, int M, float* w, int32_t* counts,
                                 int32_t* padded_offsets, int32_t* sorted_assign,
                                 int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles,
                                 hipStream_t s);

@@ -137,13 +137,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(
 }
 
 // Routing and grouping of a small batch in one block: each 16-lane row (or each wave, for
-// more than 256 experts or k > 16) of the block routes one token (route.h), the routed ids
-// reach every wave through the barrier, and the block then groups them as
-// permute_fused_kernel does. One launch in place of two where the batch fits one pass.
+// more than 256 experts or k > 16) of the block routes one token (route.h) into LDS, the
+// routed ids reach every wave through the barrier, and the block then groups them as
+// permute_fused_kernel does (the ids never go to memory: nothing after the grouping reads
+// them). One launch in place of two where the batch fits one pass.
 template <typename TA, int G, int V>
 __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
     const TA* __restrict__ logits, int T, int E, int k, int normalize, RouteOpts o, int ebits,
-    int M, int32_t* ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int M, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ padded_offsets, int32_t* __restrict__ sorted_assign,
     int32_t* __restrict__ assign_pos, int32_t* __restrict__ tile_list,
     int32_t* __restrict__ num_tiles) {
@@ -152,10 +153,11 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
   int* run = cnt + E;             // [E]
   int* scan_tmp = run + E;        // [kPermWaves + 1]
   int* wc = scan_tmp + kPermWaves + 1;  // [kPermWaves][E]
+  int* ids = wc + kPermWaves * E;       // [T * k]
   const int t = threadIdx.x / G;  // one token per group of G lanes
   if (t < T) route_token<TA, G, V>(logits, t, E, k, normalize, o, ids, topk_w);
   for (int i = threadIdx.x; i < E; i += kPermThreads) cnt[i] = 0;
-  __syncthreads();  // the ids written by each wave's lane 0 are visible to the whole block
+  __syncthreads();  // the ids each group wrote are visible to the whole block
   const int64_t A = static_cast<int64_t>(T) * k;
   block_histogram(ids, 0, A, cnt);
   __syncthreads();
@@ -239,22 +241,23 @@ bool route_permute_fits(int64_t T, int64_t A, int64_t E, int64_t k) {
 
 template <typename TA, int G, int V>
 static void launch_rp(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
-                      int M, int32_t* ids,
+                      int M,
                       float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                       int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
-  const size_t lds = (2 * E + kPermWaves + 1 + kPermWaves * E) * sizeof(int);
+  const size_t lds =
+      (2 * E + kPermWaves + 1 + kPermWaves * E + static_cast<size_t>(T) * k) * sizeof(int);
   route_permute_kernel<TA, G, V><<<1, kPermThreads, lds, s>>>(
-      logits, T, E, k, normalize, o, bits_for(E), M, ids, w, counts, padded_offsets,
+      logits, T, E, k, normalize, o, bits_for(E), M, w, counts, padded_offsets,
       sorted_assign, assign_pos, tile_list, num_tiles);
 }
 
 template <typename TA, int G>
 static void launch_rp_g(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
-                        int M, int32_t* ids,
+                        int M,
                         float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
   const int V = (E + G - 1) / G;
-#define QMOE_RP(VV) launch_rp<TA, G, VV>(logits, T, E, k, normalize, o, M, ids, w, counts, \
+#define QMOE_RP(VV) launch_rp<TA, G, VV>(logits, T, E, k, normalize, o, M, w, counts, \
                                          padded_offsets, sorted_assign, assign_pos, tile_list, \
                                          num_tiles, s)
   if (V <= 1) QMOE_RP(1);
@@ -267,27 +270,27 @@ static void launch_rp_g(const TA* logits, int T, int E, int k, int normalize, co
 
 template <typename TA>
 static void launch_rp_t(const TA* logits, int T, int E, int k, int normalize, const RouteOpts& o,
-                        int M, int32_t* ids,
+                        int M,
                         float* w, int32_t* counts, int32_t* padded_offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles, hipStream_t s) {
   if (route_by_rows(E, k))
-    launch_rp_g<TA, 16>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets,
+    launch_rp_g<TA, 16>(logits, T, E, k, normalize, o, M, w, counts, padded_offsets,
                         sorted_assign, assign_pos, tile_list, num_tiles, s);
   else
-    launch_rp_g<TA, kWave>(logits, T, E, k, normalize, o, M, ids, w, counts, padded_offsets,
+    launch_rp_g<TA, kWave>(logits, T, E, k, normalize, o, M, w, counts, padded_offsets,
                            sorted_assign, assign_pos, tile_list, num_tiles, s);
 }
 
 hipError_t launch_route_permute(const void* logits, bool bf16, int T, int E, int k, int normalize,
-                                const RouteOpts& o, int M, int32_t* ids, float* w, int32_t* counts,
+                                const RouteOpts& o, int M, float* w, int32_t* counts,
                                 int32_t* padded_offsets, int32_t* sorted_assign,
                                 int32_t* assign_pos, int32_t* tile_list, int32_t* num_tiles,
                                 hipStream_t s) {
   if (bf16)
-    launch_rp_t(static_cast<const uint16_t*>(logits), T, E, k, normalize, o, M, ids, w, counts,
+    launch_rp_t(static_cast<const uint16_t*>(logits), T, E, k, normalize, o, M, w, counts,
                 padded_offsets, sorted_assign, assign_pos, tile_list, num_tiles, s);
   else
-    launch_rp_t(static_cast<const float*>(logits), T, E, k, normalize, o, M, ids, w, counts,
+    launch_rp_t(static_cast<const float*>(logits), T, E, k, normalize, o, M, w, counts,
                 padded_offsets, sorted_assign, assign_pos, tile_list, num_tiles, s);
   return hipGetLastError();
 }
