@@ -203,8 +203,8 @@ def algorithmic(cfg, T, counts):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the forward runs on a single MI355X; "
-              "multi-GPU sharding is described in DESIGN.md and not launched here.",
+        print("bench.py measures one GPU: the forward runs on a single MI355X, and no "
+              "multi-GPU (sharded) run is launched by this script.",
               file=sys.stderr)
         sys.exit(2)
 

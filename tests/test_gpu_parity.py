@@ -31,7 +31,7 @@ NTHREADS = min(16, os.cpu_count() or 1)
 def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    qm._lib.load()  # the HIP library must be present on a GPU machine
+    qm._lib.load()  # the HIP library must be present wherever a GPU is
     torch.cuda.init()
 
 
