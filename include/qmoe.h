@@ -124,8 +124,8 @@ typedef struct {
   /* qmoe_compute_mode: QMOE_COMPUTE_FLOAT (0) keeps the activations as they are;
      QMOE_COMPUTE_INT8 (the int8 block tier of the ClikaRT "QMoEWoQ" page) rounds the
      input of each GEMM to per-block int8 first (qmoe_quantize_act): qmoe_forward does so
-     for x and h; callers of the GEMM entry points quantize their inputs themselves.
-     Needs block_size > 0. */
+     for x and h; the GEMM entry points and qmoe_linear_woq take their inputs as given
+     (their callers apply qmoe_quantize_act first). Needs block_size > 0. */
   int32_t compute_mode;
 } qmoe_params;
 
@@ -291,7 +291,8 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
  *   max|x| <= 127 * 2^e, and codes q = rint(x / 2^e) (ties to even, |q| <= 127); out holds
  *   q * 2^e, exact in the activation dtype. Needs block_size > 0.
  * qmoe_forward with compute_mode QMOE_COMPUTE_INT8 applies it to x (cols = hidden_size)
- * and to h (cols = inter_size); the GEMM entry points take their inputs as given.
+ * and to h (cols = inter_size); the GEMM entry points and qmoe_linear_woq take their
+ * inputs as given.
  */
 qmoe_status qmoe_quantize_act(const qmoe_params* p, const void* in, int64_t rows, int64_t cols,
                               void* out, void* stream);
