@@ -89,3 +89,23 @@ def test_forward_int8_c5(T, bits, bs):
 @pytest.mark.parametrize("T", [1, 64])
 def test_forward_int8_mxfp4_c2(T):
     check_forward(configs.C2_MX_INT8, T, layout="tiles")
+
+
+@pytest.mark.parametrize("T", [16, 256])
+def test_forward_int8_with_routing_variants(T):
+    # grouped top-k, selection bias and weight scaling together with the int8 tier
+    check_forward(configs.C5_ROUTED.with_(int8=True), T, sample=6, layout="tiles")
+
+
+@pytest.mark.parametrize("bits,bs", [(4, 32), (8, 64)])
+def test_forward_int8_rows_layout_prefill(bits, bs):
+    # the weights as given (rows layout) through the 128-row kernels
+    check_forward(configs.c5_point(bits, bs).with_(int8=True), 4096, sample=6, layout="rows")
+
+
+def test_forward_int8_unfused_gate_up():
+    # separate gate (fc1) and up (fc3) stacks, per-block scales of 64, 32-row tiles
+    cfg = configs.tiny(E=8, k=2, act_dtype="bf16", scale_dtype="bf16", H=256, I=128,
+                       fusion=0, bits=4, block_size=64, fc1_bias=True, fc2_bias=True,
+                       limit=7.0, int8=True)
+    check_forward(cfg, 300, layout="tiles")
