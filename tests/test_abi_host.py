@@ -213,6 +213,16 @@ def test_every_gpu_parity_case_passes_validation(lib):
     for b, bs in itertools.product(configs.C5_BITS, configs.C5_BLOCKS):
         cases += [(configs.c5_point(b, bs), T, 0, lay, "c5") for T in configs.C5.T_points
                   for lay in ("rows", "tiles")]
+    # the variants: MX FP4, routing options, the int8 tier
+    for c in (configs.C2_MX, configs.C5_MX, configs.C2_BIASED, configs.C5_ROUTED,
+              configs.C2_INT8, configs.C4_INT8, configs.C5_INT8, configs.C2_MX_INT8,
+              configs.C5_ROUTED.with_(int8=True)):
+        cases += [(c, T, 0, "tiles", "variant") for T in c.T_points]
+    cases += [(configs.c5_point(b, bs).with_(int8=True), 4096, 0, "rows", "int8 rows")
+              for b, bs in ((4, 32), (8, 64))]
+    for E, k, T, _ in t.FUSED_ROUTING_CASES:
+        cases.append((configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64,
+                                   bits=4, block_size=32, fusion=1), T, 0, "rows", "fused"))
     bad = []
     for cfg, T, m, lay, what in cases:
         if lib.qmoe_validate(params_for(cfg, T, tile_m=m, layout=lay)) != 0:

@@ -497,9 +497,12 @@ def test_forward_zero_tokens():
     assert out.shape == (0, cfg.H)
 
 
-@pytest.mark.parametrize("E,k,T,variant", [
+FUSED_ROUTING_CASES = [
     (8, 2, 64, None), (64, 4, 17, None), (64, 6, 64, "bias"), (200, 8, 40, None),
-    (256, 4, 64, "groups"), (512, 4, 16, None), (512, 8, 17, None), (384, 2, 16, "bias")])
+    (256, 4, 64, "groups"), (512, 4, 16, None), (512, 8, 17, None), (384, 2, 16, "bias")]
+
+
+@pytest.mark.parametrize("E,k,T,variant", FUSED_ROUTING_CASES)
 def test_forward_fused_routing_sizes(E, k, T, variant):
     # qmoe_forward routes and groups in one kernel up to 64 tokens (16 above 256 experts,
     # one token a wave): both sides of those edges, routing variants included
