@@ -359,15 +359,26 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
           // each stream's accumulator takes the correction -(c+z) * sum x and the products;
           // a group starts from zero
 #pragma unroll
-          for (int mr = 0; mr < MR; ++mr)
+          for (int mr = 0; mr < MR; ++mr) {
+            if (first) {
+              // a group's start: the correction depends on the activations alone, so one
+              // MFMA serves every stream as the addend of its products
+              const floatx4 cor =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mr], mine ? negc : zero, zero4, 0, 0, 0);
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-              const floatx4 from = first ? zero4 : acc[mr][st][gg];
-              acc[mr][st][gg] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mr], mine ? negc : zero, from, 0, 0, 0);
-              acc[mr][st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  xa[mr], mine ? bw[st] : zero, acc[mr][st][gg], 0, 0, 0);
+              for (int st = 0; st < NS; ++st)
+                acc[mr][st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    xa[mr], mine ? bw[st] : zero, cor, 0, 0, 0);
+            } else {
+#pragma unroll
+              for (int st = 0; st < NS; ++st) {
+                acc[mr][st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    xa[mr], mine ? negc : zero, acc[mr][st][gg], 0, 0, 0);
+                acc[mr][st][gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    xa[mr], mine ? bw[st] : zero, acc[mr][st][gg], 0, 0, 0);
+              }
             }
+          }
           if (last) {
             // the group's block: the two blocks of 16 inside one 4-bit MFMA are gl0 and
             // gl0 + 1, the blocks of an 8-bit super-step gl0 + gg; otherwise the MFMA or
