@@ -111,7 +111,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
   };
   auto stream_rows = [&](int st) { return (kTwo && g.fusion == 0) ? g.inter : g.N; };
   auto stream_w = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.w3 : g.w; };
-  auto stream_s = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s; };
   auto stream_b = [&](int st) { return (st == 1 && kTwo && g.fusion == 0) ? g.b3 : g.b; };
   // column of slice b, row n of wave column wnn (clamped into the stack where it is read)
   auto slice_col = [&](int wnn, int b, int nn) { return col0 + wnn * NBS * 16 + (b % NBS) * 16 + nn; };
