@@ -119,24 +119,27 @@ __device__ __forceinline__ void route_loaded(TokenLogits<V>& r, int t, int E, in
     uint32_t gsc[kMaxGroups];
 #pragma unroll
     for (int gi = 0; gi < kMaxGroups; ++gi) {
-      if (gi >= o.n_group) break;
-      uint32_t local = 0u;
+      gsc[gi] = 0u;
+      if (gi < o.n_group) {  // uniform: the group's lanes all take it
+        uint32_t local = 0u;
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = gl * V + v;
-        if (e < E && e / gsize == gi) local = max(local, key[v]);
+        for (int v = 0; v < V; ++v) {
+          const int e = gl * V + v;
+          if (e < E && e / gsize == gi) local = max(local, key[v]);
+        }
+        gsc[gi] = group_max_u32<G>(local);
       }
-      gsc[gi] = group_max_u32<G>(local);
     }
     uint32_t keep = 0u;
     for (int rr = 0; rr < o.topk_group; ++rr) {
       int bg = -1;
       uint32_t bs = 0u;
 #pragma unroll
-      for (int gi = 0; gi < kMaxGroups; ++gi) {
-        if (gi >= o.n_group) break;
-        if (!((keep >> gi) & 1u) && (bg < 0 || gsc[gi] > bs)) { bg = gi; bs = gsc[gi]; }
-      }
+      for (int gi = 0; gi < kMaxGroups; ++gi)
+        if (gi < o.n_group && !((keep >> gi) & 1u) && (bg < 0 || gsc[gi] > bs)) {
+          bg = gi;
+          bs = gsc[gi];
+        }
       keep |= 1u << bg;
     }
 #pragma unroll
