@@ -290,6 +290,11 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
  *   cols) gets the power-of-two scale 2^e, e the smallest integer with
  *   max|x| <= 127 * 2^e, and codes q = rint(x / 2^e) (ties to even, |q| <= 127); out holds
  *   q * 2^e, exact in the activation dtype. Needs block_size > 0.
+ *   Ownership: the caller owns both buffers; the call only enqueues one kernel on stream.
+ *   Errors: the parameter block is validated first (its shapes need not match rows and
+ *   cols); block_size 0 -> QMOE_ERR_INVALID; rows < 0 or cols outside [1, 2^31) ->
+ *   QMOE_ERR_SHAPE; rows == 0 -> QMOE_OK with nothing enqueued; NULL in or out ->
+ *   QMOE_ERR_UNBOUND; a launch failure -> QMOE_ERR_DEVICE.
  * qmoe_forward with compute_mode QMOE_COMPUTE_INT8 applies it to x (cols = hidden_size)
  * and to h (cols = inter_size); the GEMM entry points and qmoe_linear_woq take their
  * inputs as given.
