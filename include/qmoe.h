@@ -81,7 +81,8 @@ typedef enum {
 
 typedef struct {
   /* T, H, I, E, k: tokens, hidden_size, inter_size, num_experts, top-k
-     (ClikaRT QMoEWoQ::make counts; graiphic QMoE attribute k). 1 <= k <= E <= 1024. */
+     (ClikaRT QMoEWoQ::make counts; graiphic QMoE attribute k). 1 <= k <= E <= 512,
+     k <= 32 (QMOE_ERR_UNSUPPORTED beyond). */
   int64_t num_tokens, hidden_size, inter_size, num_experts, k;
   /* expert_weight_bits: 4 (two fields per byte, element 2j in the low nibble) or 8. */
   int32_t expert_weight_bits;
@@ -125,7 +126,10 @@ typedef struct {
      QMOE_COMPUTE_INT8 (the int8 block tier of the ClikaRT "QMoEWoQ" page) rounds the
      input of each GEMM to per-block int8 first (qmoe_quantize_act): qmoe_forward does so
      for x and h; the GEMM entry points and qmoe_linear_woq take their inputs as given
-     (their callers apply qmoe_quantize_act first). Needs block_size > 0. */
+     (their callers apply qmoe_quantize_act first). Needs block_size > 0
+     (QMOE_ERR_INVALID) and bf16 activations (QMOE_ERR_UNSUPPORTED with fp32: the codes
+     of h are decided from h, and a last-bit difference in an fp32 h, from summation
+     order, can move one code by a step, which is worth more than the fp32 path's bound). */
   int32_t compute_mode;
 } qmoe_params;
 
@@ -281,6 +285,38 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                          qmoe_stack fc1, qmoe_stack fc2, qmoe_stack fc3,
                          const void* shared_output, void* output, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Where qmoe_forward keeps each intermediate inside its workspace: byte offsets from the
+ * workspace start, in this order, each a multiple of 256. A caller may read the pieces
+ * back after the forward has completed on its stream (to inspect the routing and the
+ * grouping, say); their contents are those of the entry point named beside each.
+ *   topk_ids        int32 [T, k]          qmoe_route (not written when fused_routing is 1)
+ *   topk_w          float [T, k]          qmoe_route
+ *   counts          int32 [E]             qmoe_permute
+ *   padded_offsets  int32 [E + 1]         qmoe_permute
+ *   sorted_assign   int32 [qmoe_max_rows]  qmoe_permute (rows past padded_offsets[E] hold
+ *                                         whatever the workspace held before)
+ *   assign_pos      int32 [T * k]         qmoe_permute
+ *   tile_list       int32 [qmoe_max_tiles, 2], num_tiles int32 [1]: qmoe_permute
+ *   permute_scratch qmoe_permute_scratch_size bytes
+ *   h               act_dtype [qmoe_max_rows, I]   qmoe_grouped_gemm_fc1_swiglu (int8 tier:
+ *                                         after its rounding)
+ *   y               float [qmoe_max_rows, H]       qmoe_grouped_gemm_fc2
+ *   xq              act_dtype [T, H]      the int8 tier's rounded x (0 when compute_mode is
+ *                                         QMOE_COMPUTE_FLOAT: no such piece)
+ *   total           == qmoe_workspace_size(p)
+ *   fused_routing   1 when this batch is routed and grouped by one kernel (small batches:
+ *                   the routed ids stay inside that kernel), else 0.
+ * Errors: invalid parameters as qmoe_validate; out NULL -> QMOE_ERR_UNBOUND.
+ */
+typedef struct {
+  size_t topk_ids, topk_w, counts, padded_offsets, sorted_assign, assign_pos, tile_list,
+      num_tiles, permute_scratch, h, y, xq, total;
+  int32_t fused_routing;
+} qmoe_workspace_layout;
+
+qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);
 
 /*
  * The int8 activation tier's rounding (ClikaRT "QMoEWoQ" page: the activation is rounded

@@ -220,7 +220,8 @@ def test_every_gpu_parity_case_passes_validation(lib):
         cases += [(c, T, 0, "tiles", "variant") for T in c.T_points]
     cases += [(configs.c5_point(b, bs).with_(int8=True), 4096, 0, "rows", "int8 rows")
               for b, bs in ((4, 32), (8, 64))]
-    for E, k, T, _ in t.FUSED_ROUTING_CASES:
+    cases += [(cfg, T, 0, "tiles", "full-size stages " + n) for n, (cfg, T) in t.FULL_STAGE_CASES.items()]
+    for E, k, T, _ in t.FUSED_ROUTING_CASES + t.FUSED_ROUTING_EDGES:
         cases.append((configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64,
                                    bits=4, block_size=32, fusion=1), T, 0, "rows", "fused"))
     bad = []
@@ -277,6 +278,10 @@ def test_int8_tier_params(lib):
     block_size > 0 (no device is touched on these paths)."""
     assert status(good(compute_mode="int8")) == _lib.QMOE_OK
     assert status(good(compute_mode="int8", block_size=0)) == _lib.QMOE_ERR_INVALID
+    # fp32 activations keep the float path (the rounding entry point takes both dtypes)
+    assert status(good(compute_mode="int8", act_dtype="f32")) == _lib.QMOE_ERR_UNSUPPORTED
+    assert lib.qmoe_quantize_act(good(act_dtype="f32"), 1 << 20, 0, 64, 1 << 20,
+                                 None) == _lib.QMOE_OK
     p = good()
     p.compute_mode = 2
     assert status(p) == _lib.QMOE_ERR_INVALID

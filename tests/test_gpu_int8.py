@@ -6,9 +6,10 @@ activation is rounded to per-block int8 before the dot).
 * the forward with compute_mode int8 against the oracle's int8 forward on the decode,
   prefill, many-expert and MX FP4 shapes, at the bf16 tolerance.
 
-fp32 activations are checked through the rounding alone: the codes of h are decided from h,
-and an fp32 h that differs from the oracle's fp64 h in its last bit (summation order) can
-move one code by a step, which is worth more than the fp32 tolerance.
+With fp32 activations the forward refuses the tier (QMOE_ERR_UNSUPPORTED, checked on the
+host): the codes of h are decided from h, and an fp32 h that differs from the oracle's fp64
+h in its last bit (summation order) can move one code by a step, which is worth more than
+the fp32 tolerance. The rounding itself is checked in both dtypes.
 """
 from __future__ import annotations
 

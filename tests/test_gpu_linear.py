@@ -14,7 +14,7 @@ import torch
 import oracle
 import weight_only_quantized_softmax_amd as qm
 from synth import configs, gen
-from tests.gpu_helpers import TOL, dev, host_f64, max_excess_err, max_rel_err
+from tests.gpu_helpers import check_output, dev, host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -59,14 +59,10 @@ def check(cfg, T, layout, sample=None, tile_m=0):
         rng = np.random.default_rng(T + 5)
         rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=sample - 2, replace=False)]))
     ref = oracle.linear(cfg, inp, rows=rows, nthreads=NTHREADS)
-    if cfg.act_dtype == "bf16":
-        ex = max_excess_err(got[rows], ref)
-        print(f"  max err beyond bf16 storage / rms {ex:.3e}", flush=True)
-        assert ex <= TOL["bf16"]
-    else:
-        err = max_rel_err(got[rows], ref)
-        print(f"  max err / rms {err:.3e}", flush=True)
-        assert err <= TOL["f32"]
+    # the layer's output is the result: max |err| against the unrounded fp64 oracle, relative
+    # to its RMS, at the activation dtype's bound (the bf16 rounding floor and the error
+    # beyond it are printed beside it)
+    print("  " + check_output(got[rows], ref, cfg.act_dtype), flush=True)
     return M
 
 

@@ -19,8 +19,8 @@ import oracle
 import weight_only_quantized_softmax_amd as qm
 from synth import configs, gen
 from synth.gen import as_f32, store
-from tests.gpu_helpers import (TOL, DeviceInputs, dev, host, host_f64, max_excess_err,
-                               max_rel_err, params_for, rms)
+from tests.gpu_helpers import (TOL, DeviceInputs, check_output, dev, host, host_f64,
+                               max_excess_err, max_rel_err, params_for, rms)
 
 pytestmark = pytest.mark.gpu
 
@@ -318,6 +318,87 @@ def test_fc2_stage(name, tile_m, layout):
     assert np.all(got[P:] == 7.0)
 
 
+# Full-size grids in the launch configuration the bench times (the library's tile height
+# for the shapes, tiled weights), with the grouping of the workload's own routing: the first
+# and the last valid row of EVERY tile are compared with the oracle, so that every work item
+# of the grid (the XCD-banded order of the 128-row kernels included, with its last partial
+# band) is checked. fc2 takes a synthetic h (never the GPU's fc1 output).
+FULL_STAGE_CASES = {
+    "c3-prefill-T4096": (configs.C3, 4096),
+    "c4-many-expert-T512": (configs.C4, 512),
+    "c5-b4-bs16-T4096": (configs.c5_point(4, 16), 4096),
+    "c5-b4-bs32-T4096": (configs.c5_point(4, 32), 4096),
+    "c5-b8-bs128-T4096": (configs.c5_point(8, 128), 4096),
+    "c5-b4-bs64-T256": (configs.c5_point(4, 64), 256),
+    "c5-mxfp4-T4096": (configs.C5_MX, 4096),
+}
+
+
+def _tile_ends(perm, M):
+    """Padded row indices of the first and last valid row of every tile."""
+    rows = []
+    for i, (_, v) in enumerate(perm["tiles"][:perm["num_tiles"]]):
+        rows += [i * M, i * M + int(v) - 1]
+    return np.unique(np.array(rows, np.int64))
+
+
+@pytest.mark.parametrize("name", sorted(FULL_STAGE_CASES))
+def test_full_size_stages_every_tile(name):
+    cfg, T = FULL_STAGE_CASES[name]
+    inp = gen.make_inputs(cfg, T)
+    p = params_for(cfg, T, layout="tiles")
+    M = qm.qmoe_tile_m(p)
+    ids_o, _ = oracle.route(cfg, inp.logits, inp.ebias)
+    perm = oracle.permute(cfg, ids_o, M)
+    sa = perm["sorted_assign"]
+    erow = np.repeat(np.arange(cfg.E), np.diff(perm["padded_offsets"]))
+    chk = _tile_ends(perm, M)
+    say(f"full-size {name}: T={T} M={M} tiles={perm['num_tiles']} rows checked={chk.size}")
+    d = DeviceInputs(inp).tiled(p)
+    rows = qm.qmoe_max_rows(p)
+    sa_pad = np.full(rows, -1, np.int32)
+    sa_pad[:len(sa)] = sa
+    tl = np.zeros((qm.qmoe_max_tiles(p), 2), np.int32)
+    tl[:perm["num_tiles"]] = perm["tiles"]
+    ntd = dev(np.array([perm["num_tiles"]], np.int32))
+    tld = dev(tl)
+    # fc1 + activation
+    h = torch.full((rows, cfg.I), 7.0, dtype=torch.bfloat16, device="cuda")
+    qm.qmoe_grouped_gemm_fc1_swiglu(p, d.x, dev(sa_pad), tld, ntd, d.fc1, d.fc3, h)
+    torch.cuda.synchronize()
+    got = host_f64(h[torch.from_numpy(chk).cuda()], "bf16")
+    ref = oracle.fc1_rows(cfg, inp, sa[chk] // cfg.k, erow[chk], nthreads=NTHREADS)
+    # h is an intermediate held in bfloat16: rounding it costs up to half a bf16 spacing of
+    # each value by itself (the floor printed, large where SwiGLU's tail is heavy), so the
+    # bound applies to the error beyond that rounding
+    err = max_rel_err(got, ref)
+    floor = max_rel_err(as_f32(oracle.round_bf16(ref), "bf16").astype(np.float64), ref)
+    ex = max_excess_err(got, ref)
+    say(f"  fc1 max|err|/rms {err:.3e} (bf16 rounding floor {floor:.3e}); beyond the rounding "
+        f"{ex:.3e} (tolerance {TOL['bf16']:.0e})")
+    assert ex <= TOL["bf16"]
+    pads = np.where(sa < 0)[0]
+    if pads.size:
+        hp = host_f64(h[torch.from_numpy(pads[:4096].astype(np.int64)).cuda()], "bf16")
+        assert np.all(hp == 0.0)  # padding rows are written as zeros
+    del h
+    # fc2
+    hin = gen.gen_stage_h(cfg, rows, sigma=3.0)
+    hin[sa.size:] = 0
+    hin[:sa.size][sa < 0] = 0
+    y = torch.full((rows, cfg.H), 7.0, dtype=torch.float32, device="cuda")
+    qm.qmoe_grouped_gemm_fc2(p, dev(hin, "bf16"), tld, ntd, d.fc2, y)
+    torch.cuda.synchronize()
+    goty = host(y[torch.from_numpy(chk).cuda()]).astype(np.float64)
+    refy = oracle.fc2_rows(cfg, inp, hin, chk, erow[chk], nthreads=NTHREADS)
+    erry = max_rel_err(goty, refy)
+    say(f"  fc2 max|err|/rms {erry:.3e} (tolerance 1e-3: fp32 y from exact bf16 products)")
+    assert erry <= 1e-3
+    P = int(perm["padded_offsets"][-1])
+    if P < rows:
+        assert np.all(host(y[P:]) == 7.0)  # rows past the padded layout are never written
+
+
 # --------------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("dtype,H,shared", [("bf16", 2880, False), ("bf16", 2048, True),
@@ -359,7 +440,7 @@ def test_combine_rounds_to_nearest_even():
 
 # --------------------------------------------------------------------------- end to end
 
-def forward_gpu(cfg, inp, d=None, reshape3d=False, layout="rows"):
+def forward_gpu(cfg, inp, d=None, reshape3d=False, layout="rows", workspace=None):
     T = inp.x.shape[0]
     base = d if d is not None else DeviceInputs(inp)
     p = params_for(cfg, T, layout=layout, ebias=base.ebias)
@@ -367,24 +448,70 @@ def forward_gpu(cfg, inp, d=None, reshape3d=False, layout="rows"):
         d = base.tiled(p) if p.weight_layout == qm.QMOE_LAYOUT_TILES else base
     x = d.x.view(1, T, cfg.H) if reshape3d else d.x
     sh = d.shared.view(1, T, cfg.H) if (reshape3d and d.shared is not None) else d.shared
-    out = qm.forward(p, x, d.logits, d.fc1, d.fc2, d.fc3, sh)
+    out = qm.forward(p, x, d.logits, d.fc1, d.fc2, d.fc3, sh, workspace=workspace)
     torch.cuda.synchronize()
     return out.reshape(T, cfg.H), d
 
 
-def check_forward(cfg, T, sample=None, shared=False, seed=0, layout="rows"):
+def workspace_routing(p, ws, T, E, k):
+    """The routing and grouping that qmoe_forward left in its workspace (ws: uint8 tensor)."""
+    lay = qm.qmoe_workspace_layout_of(p)
+    wb = host(ws)
+
+    def piece(off, n, dt=np.int32):
+        return wb[off:off + n * np.dtype(dt).itemsize].view(dt).copy()
+
+    A = T * k
+    rows, tiles = qm.qmoe_max_rows(p), qm.qmoe_max_tiles(p)
+    got = dict(fused=int(lay.fused_routing), topk_w=piece(lay.topk_w, A, np.float32).reshape(T, k),
+               counts=piece(lay.counts, E), padded_offsets=piece(lay.padded_offsets, E + 1),
+               sorted_assign=piece(lay.sorted_assign, rows), assign_pos=piece(lay.assign_pos, A),
+               tiles=piece(lay.tile_list, 2 * tiles).reshape(tiles, 2),
+               num_tiles=int(piece(lay.num_tiles, 1)[0]))
+    if not got["fused"]:
+        got["topk_ids"] = piece(lay.topk_ids, A).reshape(T, k)
+    return got
+
+
+def check_grouping(got, ids_o, w_o, perm_o, E):
+    """The forward's own routing and grouping against the oracle's, bit for bit (weights
+    within 2e-6). The expert of each assignment follows from the grouping alone (the rows of
+    expert e hold its assignments), so the fused path's ids are checked through it."""
+    P, nt = perm_o["rows"], perm_o["num_tiles"]
+    assert np.array_equal(got["counts"], perm_o["counts"])
+    assert np.array_equal(got["padded_offsets"], perm_o["padded_offsets"])
+    assert np.array_equal(got["sorted_assign"][:P], perm_o["sorted_assign"])
+    assert np.array_equal(got["assign_pos"], perm_o["assign_pos"])
+    assert got["num_tiles"] == nt
+    assert np.array_equal(got["tiles"][:nt], perm_o["tiles"])
+    ids_from_rows = np.full(ids_o.size, -1, np.int64)
+    offs, cnt = got["padded_offsets"], got["counts"]
+    for e in range(E):
+        ids_from_rows[got["sorted_assign"][offs[e]:offs[e] + cnt[e]]] = e
+    assert np.array_equal(ids_from_rows.reshape(ids_o.shape), ids_o)
+    if "topk_ids" in got:
+        assert np.array_equal(got["topk_ids"], ids_o)
+    assert np.max(np.abs(got["topk_w"] - w_o)) < 2e-6
+
+
+def check_forward(cfg, T, sample=None, shared=False, seed=0, layout="rows", expect_fused=None):
     say("forward", cfg.name, layout, "T", T, "bits", cfg.bits, "bs", cfg.block_size)
     inp = gen.make_inputs(cfg, T, seed=seed, shared=shared)
-    out, d = forward_gpu(cfg, inp, layout=layout)
+    p = params_for(cfg, T, layout=layout)
+    ws = torch.full((max(qm.qmoe_workspace_size(p), 256),), 0xA5, dtype=torch.uint8, device="cuda")
+    out, d = forward_gpu(cfg, inp, layout=layout, workspace=ws)
     got = host_f64(out, cfg.act_dtype)
-    # routing and grouping of every token, bit for bit
-    ids_g, _ = run_route(cfg, inp.logits, T, inp.ebias)
+    # the forward's own routing and grouping of every token (read back from its
+    # workspace), bit for bit
     ids_o, w_o = oracle.route(cfg, inp.logits, inp.ebias)
-    assert np.array_equal(ids_g, ids_o)
-    M, perm_g = run_permute(cfg, ids_o, T)
+    M = qm.qmoe_tile_m(p)
     perm_o = oracle.permute(cfg, ids_o, M)
-    assert np.array_equal(perm_g["sorted_assign"][:perm_o["rows"]], perm_o["sorted_assign"])
-    assert np.array_equal(perm_g["assign_pos"], perm_o["assign_pos"])
+    grp = workspace_routing(p, ws, T, cfg.E, cfg.k)
+    say(f"  grouping bit-exact ({'one-kernel' if grp['fused'] else 'two-kernel'} routing, "
+        f"M={M}, {perm_o['num_tiles']} tiles)")
+    check_grouping(grp, ids_o, w_o, perm_o, cfg.E)
+    if expect_fused is not None:
+        assert bool(grp["fused"]) == expect_fused
     # outputs
     if sample is None or sample >= T:
         sel = np.arange(T)
@@ -392,12 +519,7 @@ def check_forward(cfg, T, sample=None, shared=False, seed=0, layout="rows"):
         rng = np.random.default_rng(seed + 17)
         sel = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=sample - 2, replace=False)]))
     ref64, _ = oracle.forward(cfg, inp, sel=sel, nthreads=NTHREADS)
-    err = max_rel_err(got[sel], ref64)
-    floor = 0.0
-    if cfg.act_dtype == "bf16":
-        floor = max_rel_err(as_f32(oracle.round_bf16(ref64), "bf16").astype(np.float64), ref64)
-    say(f"  max|err|/rms = {err:.3e} (tolerance {TOL[cfg.act_dtype]:.0e}; rounding floor {floor:.3e})")
-    assert err <= TOL[cfg.act_dtype]
+    say("  " + check_output(got[sel], ref64, cfg.act_dtype))
     return out, d, inp
 
 
@@ -411,18 +533,18 @@ def test_forward_c2_decode(T):
 
 
 def test_forward_c3_prefill_sampled():
-    check_forward(configs.C3, 4096, sample=12)
+    check_forward(configs.C3, 4096, sample=48)
 
 
 def test_forward_c4_many_experts_sampled():
-    check_forward(configs.C4, 512, sample=16)
+    check_forward(configs.C4, 512, sample=64)
 
 
 @pytest.mark.parametrize("bits", configs.C5_BITS)
 @pytest.mark.parametrize("bs", configs.C5_BLOCKS)
 @pytest.mark.parametrize("T", configs.C5.T_points)
 def test_forward_c5_sweep(T, bs, bits):
-    check_forward(configs.c5_point(bits, bs), T, sample=6)
+    check_forward(configs.c5_point(bits, bs), T, sample=24)
 
 
 # the tiled weight layout end to end: every workload
@@ -432,18 +554,18 @@ def test_forward_tiled_c2_decode(T):
 
 
 def test_forward_tiled_c3_prefill_sampled():
-    check_forward(configs.C3, 4096, sample=12, layout="tiles")
+    check_forward(configs.C3, 4096, sample=48, layout="tiles")
 
 
 def test_forward_tiled_c4_many_experts_sampled():
-    check_forward(configs.C4, 512, sample=16, layout="tiles")
+    check_forward(configs.C4, 512, sample=64, layout="tiles")
 
 
 @pytest.mark.parametrize("bits", configs.C5_BITS)
 @pytest.mark.parametrize("bs", configs.C5_BLOCKS)
 @pytest.mark.parametrize("T", [256, 4096])
 def test_forward_tiled_c5_sweep(T, bs, bits):
-    check_forward(configs.c5_point(bits, bs), T, sample=6, layout="tiles")
+    check_forward(configs.c5_point(bits, bs), T, sample=24, layout="tiles")
 
 
 @pytest.mark.parametrize("T", [8, 64])
@@ -465,7 +587,7 @@ def test_forward_mxfp4_c2_decode(T):
 
 @pytest.mark.parametrize("T", [1, 256, 4096])
 def test_forward_mxfp4_c5_sampled(T):
-    check_forward(configs.C5_MX, T, sample=6, layout="tiles")
+    check_forward(configs.C5_MX, T, sample=24, layout="tiles")
 
 
 def test_forward_deterministic_and_3d_input():
@@ -502,7 +624,13 @@ FUSED_ROUTING_CASES = [
     (256, 4, 64, "groups"), (512, 4, 16, None), (512, 8, 17, None), (384, 2, 16, "bias")]
 
 
-@pytest.mark.parametrize("E,k,T,variant", FUSED_ROUTING_CASES)
+# both sides of the one-kernel routing's token limits (64 at c2's 32 experts, 16 above 256)
+FUSED_ROUTING_EDGES = [
+    (32, 4, 1, None), (32, 4, 8, None), (32, 4, 16, None), (32, 4, 17, None), (32, 4, 65, None),
+    (257, 4, 16, None), (300, 6, 17, "bias")]
+
+
+@pytest.mark.parametrize("E,k,T,variant", FUSED_ROUTING_CASES + FUSED_ROUTING_EDGES)
 def test_forward_fused_routing_sizes(E, k, T, variant):
     # qmoe_forward routes and groups in one kernel up to 64 tokens (16 above 256 experts,
     # one token a wave): both sides of those edges, routing variants included
@@ -515,4 +643,7 @@ def test_forward_fused_routing_sizes(E, k, T, variant):
         extra = dict(n_group=8, topk_group=3, score_bias=True, routed_scale=2.0)
     cfg = configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64, bits=4,
                        block_size=32, logit_sigma=2.0, fusion=1, **extra)
-    check_forward(cfg, T)
+    # one kernel routes and groups up to 64 tokens (a 16-lane row per token: E <= 256, k <= 16),
+    # or 16 tokens (a wave per token)
+    fused = T <= (64 if (E <= 256 and k <= 16) else 16)
+    check_forward(cfg, T, expect_fused=fused)

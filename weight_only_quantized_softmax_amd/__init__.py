@@ -15,12 +15,13 @@ import torch
 from . import _lib
 from ._lib import (ACT, QMOE_BF16, QMOE_E8M0, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SHAPE,
                    QMOE_ERR_UNBOUND, QMOE_F32, QMOE_FC1, QMOE_FC2, QMOE_FC3, QMOE_LAYOUT_ROWS,
-                   QMOE_LAYOUT_TILES, QmoeError, QmoeParams, QmoeStack, check, load)
+                   QMOE_LAYOUT_TILES, QmoeError, QmoeParams, QmoeStack, QmoeWorkspaceLayout,
+                   check, load)
 
 __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
+           "qmoe_forward", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
            "qmoe_time_next_gemm", "qmoe_linear_woq", "qmoe_quantize_act", "linear_params", "linear_woq", "forward",
            "QmoeError", "QmoeParams"]
 
@@ -119,6 +120,13 @@ def qmoe_workspace_size(p: QmoeParams) -> int:
     if n == 0:
         check(load().qmoe_validate(p))
     return n
+
+
+def qmoe_workspace_layout_of(p: QmoeParams) -> QmoeWorkspaceLayout:
+    """Byte offsets of qmoe_forward's intermediates inside its workspace."""
+    out = QmoeWorkspaceLayout()
+    check(load().qmoe_workspace_layout_of(p, out))
+    return out
 
 
 def qmoe_route(p, router_logits, topk_ids, topk_w, stream=None) -> None:

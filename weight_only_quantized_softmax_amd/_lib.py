@@ -34,6 +34,13 @@ class QmoeParams(ctypes.Structure):
                 ("compute_mode", ctypes.c_int32)]
 
 
+class QmoeWorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "topk_ids", "topk_w", "counts", "padded_offsets", "sorted_assign", "assign_pos",
+        "tile_list", "num_tiles", "permute_scratch", "h", "y", "xq", "total")] + [
+        ("fused_routing", ctypes.c_int32)]
+
+
 class QmoeStack(ctypes.Structure):
     _fields_ = [("weights", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("bias", ctypes.c_void_p)]
@@ -42,7 +49,7 @@ class QmoeStack(ctypes.Structure):
 EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
+           "qmoe_forward", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
            "qmoe_quantize_act", "qmoe_time_next_gemm", "qmoe_last_error")
 
 _lib = None
@@ -76,6 +83,8 @@ def load() -> ctypes.CDLL:
     L.qmoe_combine.argtypes, L.qmoe_combine.restype = [P, vp, vp, vp, vp, vp, vp], st
     L.qmoe_forward.argtypes = [P, vp, vp, QmoeStack, QmoeStack, QmoeStack, vp, vp, vp, sz, vp]
     L.qmoe_forward.restype = st
+    L.qmoe_workspace_layout_of.argtypes = [P, ctypes.POINTER(QmoeWorkspaceLayout)]
+    L.qmoe_workspace_layout_of.restype = st
     L.qmoe_packed_stack_size.argtypes = [P, ctypes.c_int32]
     L.qmoe_packed_stack_size.restype = sz
     L.qmoe_pack_stack.argtypes, L.qmoe_pack_stack.restype = [P, ctypes.c_int32, vp, vp, vp], st

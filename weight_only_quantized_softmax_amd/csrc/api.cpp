@@ -118,6 +118,12 @@ qmoe_status validate(const qmoe_params* p) {
     return fail(QMOE_ERR_INVALID, "compute_mode %d unknown", p->compute_mode);
   if (p->compute_mode == QMOE_COMPUTE_INT8 && p->block_size == 0)
     return fail(QMOE_ERR_INVALID, "the int8 activation tier needs block_size > 0");
+  // The tier decides the codes of h from h itself. An fp32 h that differs from an exact
+  // evaluation in its last bit (summation order) can move a code by one step, and one step
+  // is worth more than the fp32 path's error bound, so fp32 activations keep the float
+  // path; the rounding itself (qmoe_quantize_act) serves both dtypes.
+  if (p->compute_mode == QMOE_COMPUTE_INT8 && p->act_dtype == QMOE_F32)
+    return fail(QMOE_ERR_UNSUPPORTED, "the int8 activation tier runs with bf16 activations");
   if (p->expert_weight_bits != 4 && p->expert_weight_bits != 8)
     return fail(QMOE_ERR_INVALID, "expert_weight_bits %d is not 4 or 8", p->expert_weight_bits);
   if (p->block_size != 0 && (!is_pow2(p->block_size) || p->block_size < 16))
@@ -236,8 +242,9 @@ Workspace carve(const qmoe_params* p, char* base) {
   const size_t act = p->act_dtype == QMOE_BF16 ? 2 : 4;
   Workspace w{};
   size_t off = 0;
+  // with a null base the pieces' addresses are their byte offsets
   auto take = [&](size_t bytes) {
-    char* ptr = base ? base + off : nullptr;
+    char* ptr = reinterpret_cast<char*>(reinterpret_cast<uintptr_t>(base) + off);
     off += align256(bytes);
     return ptr;
   };
@@ -519,6 +526,31 @@ qmoe_status qmoe_combine(const qmoe_params* p, const float* y, const int32_t* as
                            static_cast<int>(p->hidden_size), static_cast<int>(p->k),
                            static_cast<hipStream_t>(stream)),
       "combine launch");
+}
+
+qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out) {
+  QMOE_TRY(validate(p));
+  QMOE_TRY(need(out, "out"));
+  const Workspace w = carve(p, nullptr);
+  // carve() on a null base yields the offsets themselves (base + offset with base = 0)
+  auto off = [](const void* ptr) { return static_cast<size_t>(reinterpret_cast<uintptr_t>(ptr)); };
+  *out = qmoe_workspace_layout{};
+  out->topk_ids = off(w.topk_ids);
+  out->topk_w = off(w.topk_w);
+  out->counts = off(w.counts);
+  out->padded_offsets = off(w.offsets);
+  out->sorted_assign = off(w.sorted_assign);
+  out->assign_pos = off(w.assign_pos);
+  out->tile_list = off(w.tiles);
+  out->num_tiles = off(w.num_tiles);
+  out->permute_scratch = off(w.perm_scratch);
+  out->h = off(w.h);
+  out->y = off(w.y);
+  out->xq = p->compute_mode == QMOE_COMPUTE_INT8 ? off(w.xq) : 0;
+  out->total = w.bytes;
+  out->fused_routing = qmoe::route_permute_fits(p->num_tokens, p->num_tokens * p->k,
+                                                p->num_experts, p->k) ? 1 : 0;
+  return ok();
 }
 
 qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* router_logits,
