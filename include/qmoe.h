@@ -286,6 +286,28 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                          const void* shared_output, void* output, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed device array that qmoe_forward_noalloc keeps its intermediates in
+   (one copy per GPU the library runs on, held until the process ends). */
+#define QMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * qmoe_forward without a workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, results and errors as qmoe_forward, less the workspace; the intermediates go
+ * to a fixed array of QMOE_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, taken on
+ * the first call on that GPU with hipGetSymbolAddress). The call allocates nothing.
+ *   Size limit: parameters whose qmoe_workspace_size exceeds QMOE_NOALLOC_SCRATCH_BYTES are
+ *   refused with QMOE_ERR_UNSUPPORTED before anything is enqueued (decode-sized batches fit:
+ *   64 tokens at H = I = 2880, E = 32 need about 13 MB).
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents; calls that overlap on one GPU (different streams, or threads without ordering)
+ *   race on it. Calls on different GPUs are independent.
+ */
+qmoe_status qmoe_forward_noalloc(const qmoe_params* p, const void* input,
+                                 const void* router_logits, qmoe_stack fc1, qmoe_stack fc2,
+                                 qmoe_stack fc3, const void* shared_output, void* output,
+                                 void* stream);
+
 /*
  * Where qmoe_forward keeps each intermediate inside its workspace: byte offsets from the
  * workspace start, in this order, each a multiple of 256. A caller may read the pieces

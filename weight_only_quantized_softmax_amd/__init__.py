@@ -15,13 +15,14 @@ import torch
 from . import _lib
 from ._lib import (ACT, QMOE_BF16, QMOE_E8M0, QMOE_ERR_DTYPE, QMOE_ERR_INVALID, QMOE_ERR_SHAPE,
                    QMOE_ERR_UNBOUND, QMOE_F32, QMOE_FC1, QMOE_FC2, QMOE_FC3, QMOE_LAYOUT_ROWS,
+                   QMOE_NOALLOC_SCRATCH_BYTES,
                    QMOE_LAYOUT_TILES, QmoeError, QmoeParams, QmoeStack, QmoeWorkspaceLayout,
                    check, load)
 
 __all__ = ["make_params", "qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
+           "qmoe_forward", "qmoe_forward_noalloc", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "pack_stack",
            "qmoe_time_next_gemm", "qmoe_linear_woq", "qmoe_quantize_act", "linear_params", "linear_woq", "forward",
            "QmoeError", "QmoeParams"]
 
@@ -120,6 +121,16 @@ def qmoe_workspace_size(p: QmoeParams) -> int:
     if n == 0:
         check(load().qmoe_validate(p))
     return n
+
+
+def qmoe_forward_noalloc(p, input, router_logits, fc1: Stack, fc2: Stack, fc3: Stack,
+                         shared_output, output, stream=None) -> None:
+    """qmoe_forward with the library's fixed intermediate array instead of a workspace."""
+    check(load().qmoe_forward_noalloc(p, _ptr(input, "input"),
+                                      _ptr(router_logits, "router_logits"), _stack(fc1, "fc1"),
+                                      _stack(fc2, "fc2"), _stack(fc3, "fc3"),
+                                      _ptr(shared_output, "shared_output"),
+                                      _ptr(output, "output"), _stream(stream)))
 
 
 def qmoe_workspace_layout_of(p: QmoeParams) -> QmoeWorkspaceLayout:

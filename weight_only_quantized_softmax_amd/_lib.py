@@ -15,6 +15,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED",
 QMOE_F32, QMOE_BF16, QMOE_E8M0 = 0, 1, 2
 QMOE_LAYOUT_ROWS, QMOE_LAYOUT_TILES = 0, 1
 QMOE_FC1, QMOE_FC2, QMOE_FC3 = 1, 2, 3
+QMOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
 
 
@@ -49,7 +50,7 @@ class QmoeStack(ctypes.Structure):
 EXPORTS = ("qmoe_validate", "qmoe_tile_m", "qmoe_max_rows", "qmoe_max_tiles",
            "qmoe_permute_scratch_size", "qmoe_workspace_size", "qmoe_route", "qmoe_permute",
            "qmoe_grouped_gemm_fc1_swiglu", "qmoe_grouped_gemm_fc2", "qmoe_combine",
-           "qmoe_forward", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
+           "qmoe_forward", "qmoe_forward_noalloc", "qmoe_workspace_layout_of", "qmoe_packed_stack_size", "qmoe_pack_stack", "qmoe_linear_woq",
            "qmoe_quantize_act", "qmoe_time_next_gemm", "qmoe_last_error")
 
 _lib = None
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     L.qmoe_combine.argtypes, L.qmoe_combine.restype = [P, vp, vp, vp, vp, vp, vp], st
     L.qmoe_forward.argtypes = [P, vp, vp, QmoeStack, QmoeStack, QmoeStack, vp, vp, vp, sz, vp]
     L.qmoe_forward.restype = st
+    L.qmoe_forward_noalloc.argtypes = [P, vp, vp, QmoeStack, QmoeStack, QmoeStack, vp, vp, vp]
+    L.qmoe_forward_noalloc.restype = st
     L.qmoe_workspace_layout_of.argtypes = [P, ctypes.POINTER(QmoeWorkspaceLayout)]
     L.qmoe_workspace_layout_of.restype = st
     L.qmoe_packed_stack_size.argtypes = [P, ctypes.c_int32]

@@ -41,6 +41,10 @@ qmoe_status device_status(hipError_t e, const char* what) {
 
 namespace qmoe {
 
+qmoe_status fail_with(qmoe_status st, const char* msg, const char* detail) {
+  return (detail && detail[0]) ? fail(st, "%s: %s", msg, detail) : fail(st, "%s", msg);
+}
+
 void set_gemm_timing(hipEvent_t start, hipEvent_t stop) { g_timing = GemmTiming{start, stop}; }
 
 GemmTiming take_gemm_timing() {

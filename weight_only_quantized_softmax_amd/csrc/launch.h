@@ -5,7 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qmoe.h"
+
 namespace qmoe {
+
+// Records msg (and a detail, if non-empty) as the calling thread's qmoe_last_error and
+// returns st.
+qmoe_status fail_with(qmoe_status st, const char* msg, const char* detail);
 
 // Grouping: one fused block up to this many assignments, otherwise three kernels
 // over chunks of kPermChunk assignments.
