@@ -2,7 +2,11 @@
 
 A step is one whole forward (route, permute, fc1+SwiGLU, fc2, combine) over one batch of
 synthetic tokens: one call of the library's qmoe_forward C entry point, which launches the
-kernels (routing and grouping as one kernel at small batches). The same stages are also
+kernels (routing and grouping as one kernel at small batches), captured once per weight copy
+launched directly on one stream. The same forwards replayed from HIP graphs (one per weight
+copy, captured once) are timed too, as ``hip_graph_ms_per_step`` (``--no-graph`` skips them).
+The default decode run adds a ``prefill`` object: the prefill-shaped layer at T=4096 measured
+the same way in the same run. The same stages are also
 run one C entry point at a time, the two GEMM kernels recording their own start and end
 on HIP events (qmoe_time_next_gemm), for the kernel times and the roofline of the fc1
 kernel (``staged_ms_per_step`` is that loop's step time). Inputs are resident in HBM
@@ -70,6 +74,12 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     ap.add_argument("--tile-m", type=int, default=0,
                     help="rows per expert tile (0 = the library's choice for the shapes)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the second timing of the forward replayed from HIP graphs")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill line (T=4096 on the prefill-shaped layer) that the "
+                         "default decode run adds")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--layout", default="tiles", choices=["tiles", "rows"],
                     help="weight layout handed to the GEMMs: tiled (packed once, before any "
                          "timing) or the pages' rows layout")
@@ -200,32 +210,29 @@ def algorithmic(cfg, T, counts):
                 fc1_flops=2 * A * (cfg.n1 + (cfg.I if cfg.has_fc3 else 0)) * cfg.H)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the forward runs on a single MI355X, and no "
-              "multi-GPU (sharded) run is launched by this script.",
-              file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the cpu_baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
-        return
 
+def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
+    """One MoE workload: the whole forward timed (one qmoe_forward per step, launched
+    directly, and with graph also replayed from HIP graphs), the fc1/fc2 kernels' own
+    durations from a staged pass, the
+    roofline of the fc1 kernel and, with cpu_leg, the oracle on a bounded sample."""
     import torch
 
     import weight_only_quantized_softmax_amd as qm
     from synth import gen
-    from tests.gpu_helpers import DeviceInputs, params_for
+    from synth.device import DeviceInputs, params_for
 
-    cfg, T = workload(args)
-    torch.cuda.set_device(0)
-    if cfg.E == 1 and cfg.k == 1:
-        if args.int8:
-            sys.exit("--int8 applies to the MoE forward")
-        return main_linear(args, cfg, T)
-    if args.int8:
-        cfg = cfg.with_(int8=True, name=f"{cfg.name}-a8")
     print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
     inp = gen.make_inputs(cfg, T)
     d = DeviceInputs(inp)
@@ -287,8 +294,8 @@ def main():
 
     # HIP events that the fc1 and fc2 kernels record their own start and end on
     # (qmoe_time_next_gemm: hipExtLaunchKernel events)
-    tev = TimingEvents(4 * args.steps)
-    evp = [tev.ev[4 * i:4 * i + 4] for i in range(args.steps)]
+    tev = TimingEvents(4 * steps)
+    evp = [tev.ev[4 * i:4 * i + 4] for i in range(steps)]
 
     def step(i, timed):
         s1, s2, s3 = st_args[i % copies]
@@ -310,54 +317,73 @@ def main():
         run(lib.qmoe_combine(*comb))
 
     print(f"[bench] {copies} weight copies of {per_copy / 1e6:.1f} MB "
-          f"({alg['weight_bytes'] / 1e6:.1f} MB touched); warmup {args.warmup}",
+          f"({alg['weight_bytes'] / 1e6:.1f} MB touched); warmup {warmup}",
           file=sys.stderr, flush=True)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    staged_ms = (t1 - t0) * 1e3 / args.steps
-    fc1_ms = float(np.mean([tev.ms(4 * i, 4 * i + 1) for i in range(args.steps)]))
-    fc2_ms = float(np.mean([tev.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
+    staged_ms = (t1 - t0) * 1e3 / steps
+    fc1_ms = float(np.mean([tev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
+    fc2_ms = float(np.mean([tev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)]))
     tev.close()
 
     # the timed step: the whole-forward entry point (one C call per step, the same kernels
-    # with routing and grouping in one launch at small batches)
+    # with routing and grouping in one launch at small batches); with graph, each weight
+    # copy's forward is also captured once into a HIP graph and timed as graph replays
     xp, lp, op = ptr(d.x), ptr(d.logits), ptr(out)
 
-    def fwd(i):
+    def fwd(i, s):
         s1, s2, s3 = st_args[i % copies]
-        run(lib.qmoe_forward(p, xp, lp, s1, s2, s3, None, op, ptr(ws), wsn, sid))
+        run(lib.qmoe_forward(p, xp, lp, s1, s2, s3, None, op, ptr(ws), wsn, s))
 
-    for i in range(args.warmup):
-        fwd(i)
-    torch.cuda.synchronize()
-    f0 = time.perf_counter()
-    for i in range(args.steps):
-        fwd(i)
-    torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - f0) * 1e3 / args.steps
-    ms_per_step = fwd_ms
+    def timed(launch):
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for i in range(steps):
+            launch(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - f0) * 1e3 / steps
+
+    ms_per_step = timed(lambda i: fwd(i, sid))
+    graph_ms = None
+    if graph:
+        cap = torch.cuda.Stream()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fwd(c, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        graph_ms = timed(lambda i: graphs[i % copies].replay())
 
     fc1_gbps = alg["fc1_bytes"] / (fc1_ms * 1e-3) / 1e9
     stream_gbps = alg["weight_bytes"] / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
     kind = "f32" if cfg.act_dtype == "f32" else ("prefill" if qm.qmoe_tile_m(p) == 128 else "decode")
     traffic = committed_traffic(kind, f"{cfg.name}_T{T}")
-    decode = T <= 64
-    if decode or alg["flops"] / alg["weight_bytes"] < 300:
+    if T <= 64 or alg["flops"] / alg["weight_bytes"] < 300:
         roof = dict(bound="hbm", achieved=round(fc1_gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(fc1_gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
     else:
         tf = alg["fc1_flops"] / (fc1_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic)
+    fc2_flops = alg["flops"] - alg["fc1_flops"]
+    kernels = dict(fc1_ms=round(fc1_ms, 5), fc2_ms=round(fc2_ms, 5),
+                   fc1_hbm_frac=round(fc1_gbps / HBM_PEAK_GBPS, 4),
+                   fc2_hbm_frac=round(alg["fc2_bytes"] / (fc2_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   fc1_mfma_frac=round(alg["fc1_flops"] / (fc1_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   fc2_mfma_frac=round(fc2_flops / (fc2_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_leg:
         import oracle
         threads = min(16, os.cpu_count() or 1)
         chunk = min(T, args.cpu_tokens)
@@ -373,28 +399,73 @@ def main():
             start = (start + chunk) % T
         csec = time.perf_counter() - c0
         cpu = dict(value=round(done / csec, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   cpu_model=cpu_model(),
                    sample=f"{calls} fp64 oracle forwards of {chunk} consecutive tokens of the same "
-                          f"T={T} workload (cycling through its tokens), {done} tokens in {csec:.1f} s")
+                          f"T={T} workload (cycling through its tokens), {done} tokens in {csec:.1f} s "
+                          f"on {threads} threads of the host CPU ({cpu_model()})")
+    return dict(cfg=cfg, T=T, p=p, layout=layout, copies=copies, alg=alg, ms_per_step=ms_per_step,
+                staged_ms=staged_ms, fc1_ms=fc1_ms, fc2_ms=fc2_ms, roof=roof, cpu=cpu,
+                stream_gbps=stream_gbps, kernels=kernels, graph_ms=graph_ms)
 
-    value = T / (ms_per_step * 1e-3)
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the forward runs on a single MI355X, and no "
+              "multi-GPU (sharded) run is launched by this script.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return
+
+    import torch
+
+    import weight_only_quantized_softmax_amd as qm
+    from synth import configs
+
+    cfg, T = workload(args)
+    torch.cuda.set_device(0)
+    if cfg.E == 1 and cfg.k == 1:
+        if args.int8:
+            sys.exit("--int8 applies to the MoE forward")
+        return main_linear(args, cfg, T)
+    if args.int8:
+        cfg = cfg.with_(int8=True, name=f"{cfg.name}-a8")
+    graph = not args.no_graph
+    r = measure_moe(args, cfg, T, args.steps, args.warmup, not args.no_cpu_baseline, graph)
+    alg = r["alg"]
+    value = T / (r["ms_per_step"] * 1e-3)
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
-        warmup=args.warmup, ms_per_step=round(ms_per_step, 5), higher_is_better=True,
+        warmup=args.warmup, ms_per_step=round(r["ms_per_step"], 5), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16" if cfg.act_dtype == "bf16" else "f32",
         data="synthetic",
         config=dict(workload=f"{cfg.name} T={T}", T=T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k,
                     bits=cfg.bits, block_size=cfg.block_size, swiglu_fusion=cfg.fusion,
-                    weight_layout=layout, tile_m=qm.qmoe_tile_m(p), weight_copies=copies,
-                    touched_experts=alg["touched"],
+                    weight_layout=r["layout"], tile_m=qm.qmoe_tile_m(r["p"]),
+                    weight_copies=r["copies"], touched_experts=alg["touched"],
                     activations="int8 blocks" if cfg.int8 else cfg.act_dtype),
-        roofline=roof,
-        cpu_baseline=cpu,
-        weight_stream_GBps=round(stream_gbps, 1),
-        kernel_ms=dict(fc1=round(fc1_ms, 5), fc2=round(fc2_ms, 5)),
-        staged_ms_per_step=round(staged_ms, 5),
+        roofline=r["roof"],
+        cpu_baseline=r["cpu"],
+        weight_stream_GBps=round(r["stream_gbps"], 1),
+        kernel_ms=dict(fc1=round(r["fc1_ms"], 5), fc2=round(r["fc2_ms"], 5)),
+        kernels=r["kernels"],
+        staged_ms_per_step=round(r["staged_ms"], 5),
+        hip_graph_ms_per_step=None if r["graph_ms"] is None else round(r["graph_ms"], 5),
         algorithmic=dict(fc1_bytes=alg["fc1_bytes"], fc2_bytes=alg["fc2_bytes"],
                          weight_bytes=alg["weight_bytes"], flops=alg["flops"]),
     )
+    # the prefill half of the metric (T = 4096 on the prefill-shaped layer), in the same run
+    if args.workload == "c2" and not args.no_prefill:
+        q = measure_moe(args, configs.C3, 4096, args.prefill_steps, 3, False, False)
+        line["prefill"] = dict(
+            workload=f"{configs.C3.name} T=4096", tokens_per_s=round(4096 / (q["ms_per_step"] * 1e-3), 1),
+            ms_per_step=round(q["ms_per_step"], 5), steps=args.prefill_steps, warmup=3,
+            kernel_ms=dict(fc1=round(q["fc1_ms"], 5), fc2=round(q["fc2_ms"], 5)),
+            roofline=q["roof"], kernels=q["kernels"],
+            tile_m=qm.qmoe_tile_m(q["p"]), weight_copies=q["copies"])
     print(json.dumps(line), flush=True)
 
 
@@ -404,7 +475,7 @@ def main_linear(args, cfg, T):
 
     import weight_only_quantized_softmax_amd as qm
     from synth import gen
-    from tests.gpu_helpers import dev
+    from synth.device import dev
 
     print(f"[bench] {cfg.name} T={T}: generating inputs", file=sys.stderr, flush=True)
     inp = gen.make_linear_inputs(cfg, T)
