@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16, E8M0 = 0, 1, 2
 _SDT = {"f32": F32, "bf16": BF16, "e8m0": E8M0}
-ACTS = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
+ACTS = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3, "gelu": 4}
 
 
 def build(force: bool = True) -> str:
@@ -42,7 +42,10 @@ class Params(ctypes.Structure):
                 ("beta", ctypes.c_double), ("limit", ctypes.c_double),
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("routed_scale", ctypes.c_double), ("score_bias", ctypes.c_void_p),
-                ("int8_act", ctypes.c_int32), ("pad2_", ctypes.c_int32)]
+                ("int8_act", ctypes.c_int32), ("pad2_", ctypes.c_int32),
+                ("gelu_mode", ctypes.c_int32), ("on_input", ctypes.c_int32),
+                ("out_scale", ctypes.c_double), ("sparse_mixer", ctypes.c_int32),
+                ("pad3_", ctypes.c_int32), ("mixer_eps", ctypes.c_double)]
 
 
 class Stack(ctypes.Structure):
@@ -66,7 +69,7 @@ def lib():
         L.oracle_permute.restype = i64
         L.oracle_weight.argtypes = [P, S, i64, i64, i64, i64, i64]
         L.oracle_weight.restype = ctypes.c_double
-        L.oracle_fc1_rows.argtypes = [P, S, S, vp, i64, vp, vp, vp, i32]
+        L.oracle_fc1_rows.argtypes = [P, S, S, vp, i64, vp, vp, vp, vp, i32]
         L.oracle_fc2_rows.argtypes = [P, S, vp, i64, vp, vp, vp, i32]
         L.oracle_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [P, S, S, S, vp, vp, vp, i64, vp, vp, vp, i32]
@@ -94,7 +97,10 @@ def params(cfg, T: int, score_bias: Optional[np.ndarray] = None) -> Params:
                   scale_dtype=_SDT[cfg.scale_dtype], pad_=0,
                   alpha=cfg.alpha, beta=cfg.beta, limit=lim, n_group=cfg.n_group,
                   topk_group=cfg.topk_group, routed_scale=cfg.routed_scale,
-                  score_bias=_ptr(score_bias), int8_act=int(cfg.int8))
+                  score_bias=_ptr(score_bias), int8_act=int(cfg.int8),
+                  gelu_mode=cfg.gelu_mode, on_input=int(cfg.on_input),
+                  out_scale=cfg.out_scale, sparse_mixer=int(cfg.sparse_mixer),
+                  mixer_eps=cfg.mixer_eps)
 
 
 def _stack(w, s, b) -> Stack:
@@ -146,14 +152,17 @@ def weight(cfg, st: Stack, N: int, K: int, e: int, n: int, kk: int) -> float:
     return lib().oracle_weight(ctypes.byref(p), ctypes.byref(st), N, K, e, n, kk)
 
 
-def fc1_rows(cfg, inp, row_token, row_expert, nthreads: int = 0) -> np.ndarray:
+def fc1_rows(cfg, inp, row_token, row_expert, nthreads: int = 0, row_w=None) -> np.ndarray:
+    """fc1 + activation of the listed rows; row_w (optional): a factor per row on the input
+    (the routing weight, when it goes to the expert's input)."""
     p = params(cfg, inp.x.shape[0])
     fc1, _, fc3 = stacks(inp)
     rt = np.ascontiguousarray(row_token, dtype=np.int32)
     re = np.ascontiguousarray(row_expert, dtype=np.int32)
+    rw = None if row_w is None else np.ascontiguousarray(row_w, dtype=np.float64)
     h = np.zeros((len(rt), cfg.I), np.float64)
     lib().oracle_fc1_rows(ctypes.byref(p), ctypes.byref(fc1), ctypes.byref(fc3), _ptr(inp.x),
-                          len(rt), _ptr(rt), _ptr(re), _ptr(h), nthreads)
+                          len(rt), _ptr(rt), _ptr(re), _ptr(rw), _ptr(h), nthreads)
     return h
 
 

@@ -26,6 +26,21 @@
  *  - SwiGLU: g' = min(g, L), u' = clamp(u, -L, L), h = g' * sigmoid(alpha g') * (u' + beta);
  *  - biases are added before the activation (fc1/fc3) and before the routing
  *    weight (fc2); shared_output is added after the weighted sum;
+ *  - gelu (graiphic "QMoE" page, activation_type gelu; CLIKA "MoE" page, gelu_mode): the
+ *    plain activation x * Phi(x), Phi the standard normal CDF through erf (gelu_mode 0),
+ *    or its tanh approximation 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (mode 1);
+ *  - apply_router_weight_on_input (CLIKA "MoE" page, routing kwargs): the routing weight
+ *    multiplies the row that enters the expert, and the expert outputs are then summed
+ *    with weight 1; expert_output_scale: multiplies each expert's output (fc2 with its
+ *    bias) before the combine (0 means 1);
+ *  - the sparse mixer (graiphic "QMoE" page, use_sparse_mixer; CLIKA "MoE" page,
+ *    sparse_mixer_eps), read from its published definition (the SparseMixer top-2 router
+ *    of the Phi-3.5-MoE model card and GRIN-MoE): k = 2 picks; pick 1 is the largest logit,
+ *    pick 2 the largest of the others (ties to the lower index); each pick's weight is
+ *    the softmax at the picked expert over the experts the pick keeps, where an expert is
+ *    dropped when (m - l) / max(|l|, m) > 2 eps (m the pick's logit, l the expert's; the
+ *    second pick also drops the first); the drop decision is taken in fp32, as the
+ *    kernel takes it; no renormalisation;
  *  - the int8 block tier (ClikaRT "QMoEWoQ" page, class description) rounds each
  *    block_size run of an activation row to int8 codes under one power-of-two scale 2^e,
  *    e the smallest integer with max|x| <= 127 * 2^e, code = x / 2^e rounded to nearest,
@@ -86,6 +101,7 @@ static uint16_t round_to_bf16(double v) {
   return static_cast<uint16_t>(bits >> 16);
 }
 
+/* Pinned against torch's float32 -> bfloat16 conversion and a single rounding from double. */
 void oracle_round_bf16(const double* v, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = round_to_bf16(v[i]);
 }
@@ -132,6 +148,9 @@ static double to_act_dtype(const oracle_params* p, double v) {
   return widen(&h, ORACLE_BF16, 0);
 }
 
+/* Pinned by a search over every power of two (tests/bruteforce.py: int8_round), by its
+   properties (largest code in [64, 127], error at most half a step, idempotence) and by
+   hand-worked blocks including a tie. */
 void oracle_int8_round(const oracle_params* p, const void* in, int64_t rows, int64_t cols,
                        void* out) {
   std::vector<double> v(cols);
@@ -144,11 +163,51 @@ void oracle_int8_round(const oracle_params* p, const void* in, int64_t rows, int
 
 /* ---- routing: softmax over all experts, keep the top k ------------------ */
 
+/* The sparse mixer's drop rule for one expert of one pick: its logit l trails the pick's
+   logit m by more than 2 eps relative to max(|l|, m), evaluated in fp32 (0/0 keeps it). */
+static bool mixer_drops(double m, double l, double eps) {
+  const float mf = static_cast<float>(m), lf = static_cast<float>(l);
+  const float r = (mf - lf) / std::max(std::fabs(lf), mf);
+  return r > 2.0f * static_cast<float>(eps);
+}
+
+/* Sparse mixer routing of one token (k = 2): two picks, each weighted by the softmax at the
+   picked expert over the experts that pick keeps. Pinned by hand-worked cases and limits
+   (eps -> infinity: plain softmaxes; eps = 0 with distinct logits: weights 1). */
+static void route_token_mixer(const oracle_params* p, const std::vector<double>& l, int32_t* ids,
+                              double* w) {
+  const int64_t E = p->E;
+  int64_t e1 = 0;
+  for (int64_t e = 1; e < E; ++e)
+    if (l[e] > l[e1]) e1 = e;
+  double s1 = 0.0;
+  for (int64_t e = 0; e < E; ++e)
+    if (!mixer_drops(l[e1], l[e], p->mixer_eps)) s1 += std::exp(l[e] - l[e1]);
+  int64_t e2 = -1;
+  for (int64_t e = 0; e < E; ++e)
+    if (e != e1 && (e2 < 0 || l[e] > l[e2])) e2 = e;
+  double s2 = 0.0;
+  for (int64_t e = 0; e < E; ++e)
+    if (e != e1 && !mixer_drops(l[e2], l[e], p->mixer_eps)) s2 += std::exp(l[e] - l[e2]);
+  const double scale = p->routed_scale != 0.0 ? p->routed_scale : 1.0;
+  ids[0] = static_cast<int32_t>(e1);
+  ids[1] = static_cast<int32_t>(e2);
+  w[0] = scale / s1;  // exp(l[e1] - l[e1]) / s1
+  w[1] = scale / s2;
+}
+
+/* Softmax-top-k routing of one token, with the selection bias and grouped top-k variants.
+   Pinned by the subset brute force (tests/bruteforce.py: select, gates) with many ties,
+   scipy's softmax, uniform and one-hot logits. */
 static void route_token(const oracle_params* p, const void* logits, int64_t t, int32_t* ids,
                         double* w) {
   const int64_t E = p->E;
   std::vector<double> l(E), key(E);
   for (int64_t e = 0; e < E; ++e) l[e] = widen(logits, p->act_dtype, t * E + e);
+  if (p->sparse_mixer) {
+    route_token_mixer(p, l, ids, w);
+    return;
+  }
   // Selection keys: the logits, or with a selection bias their fp32 sum with it (the sum
   // of two stored values, rounded once to float, as the reading of the bias states).
   for (int64_t e = 0; e < E; ++e) {
@@ -199,12 +258,15 @@ static void route_token(const oracle_params* p, const void* logits, int64_t t, i
   for (int64_t j = 0; j < p->k; ++j) w[j] *= scale;
 }
 
+/* Pinned as route_token and route_token_mixer are. */
 void oracle_route(const oracle_params* p, const void* logits, int32_t* ids, double* w) {
   for (int64_t t = 0; t < p->T; ++t) route_token(p, logits, t, ids + t * p->k, w + t * p->k);
 }
 
 /* ---- grouping by expert -------------------------------------------------- */
 
+/* Pinned against numpy's stable argsort with padding (M = 1, 4, 16, 128) and the
+   permute-then-unpermute identity. */
 int64_t oracle_permute(const oracle_params* p, int32_t M, const int32_t* ids, int32_t* counts,
                        int32_t* padded_offsets, int32_t* sorted_assign, int32_t* assign_pos,
                        int32_t* tiles, int32_t* num_tiles) {
@@ -261,6 +323,9 @@ static double e2m1(int32_t q) {
   return (q & 8) ? -mag[q & 7] : mag[q & 7];
 }
 
+/* Pinned by the dense numpy dequantisation of the brute force, the hand-worked golden cases
+   (nibble order, orientation), E2M1 from its bit fields and the 4-bit/8-bit, per-row/block
+   and ragged-block equivalences. */
 double oracle_weight(const oracle_params* p, const oracle_stack* st, int64_t N, int64_t K,
                      int64_t e, int64_t n, int64_t kk) {
   if (p->scale_dtype == ORACLE_E8M0) {
@@ -299,10 +364,15 @@ static double swiglu(const oracle_params* p, double g, double u) {
   return g * sigmoid(p->alpha * g) * (u + p->beta);
 }
 
+/* The plain activations. gelu is pinned against torch's gelu (both forms) and scipy's
+   normal CDF; relu and silu against torch; identity through the exact integer products. */
 static double plain_act(const oracle_params* p, double z) {
   switch (p->activation) {
     case ORACLE_ACT_RELU: return z > 0.0 ? z : 0.0;
     case ORACLE_ACT_SILU: return z * sigmoid(z);
+    case ORACLE_ACT_GELU:
+      if (p->gelu_mode == 0) return 0.5 * z * (1.0 + std::erf(z / std::sqrt(2.0)));
+      return 0.5 * z * (1.0 + std::tanh(std::sqrt(2.0 / M_PI) * (z + 0.044715 * z * z * z)));
     default: return z;  // identity
   }
 }
@@ -348,18 +418,23 @@ static void set_threads(int nthreads) {
 #endif
 }
 
+/* fc1 and the activation for given rows (the fc1 stage). Pinned through the forward's
+   pins (it is the forward's step) and directly by the layout equivalences. */
 void oracle_fc1_rows(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc3,
                      const void* x, int64_t n_rows, const int32_t* row_token,
-                     const int32_t* row_expert, double* h, int nthreads) {
+                     const int32_t* row_expert, const double* row_w, double* h, int nthreads) {
   set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
     std::vector<double> xr(p->H);
     widen_row(x, p->act_dtype, row_token[r], p->H, xr.data());
+    if (row_w)
+      for (int64_t i = 0; i < p->H; ++i) xr[i] *= row_w[r];
     expert_fc1(p, fc1, fc3, row_expert[r], xr.data(), h + r * p->I);
   }
 }
 
+/* fc2 for given rows (the fc2 stage); pinned like oracle_fc1_rows. */
 void oracle_fc2_rows(const oracle_params* p, const oracle_stack* fc2, const void* h_in,
                      int64_t n_rows, const int32_t* row_index, const int32_t* row_expert,
                      double* y, int nthreads) {
@@ -374,6 +449,15 @@ void oracle_fc2_rows(const oracle_params* p, const oracle_stack* fc2, const void
 
 /* ---- combine -------------------------------------------------------------- */
 
+/* The combine coefficient of one slot: its routing weight, or 1 when the weight went to the
+   expert's input, times the expert output scale. */
+static double combine_coef(const oracle_params* p, double w) {
+  const double s = p->out_scale != 0.0 ? p->out_scale : 1.0;
+  return (p->on_input ? 1.0 : w) * s;
+}
+
+/* The combine (stage). Pinned by the zero-weight closed form out = sum_j w_j b2[e_j] and
+   the composition test (stages compose to the forward). */
 void oracle_combine(const oracle_params* p, const float* y, const int32_t* assign_pos,
                     const float* w, const void* shared, double* out64, void* out_rounded) {
   const int64_t H = p->H, k = p->k;
@@ -381,7 +465,7 @@ void oracle_combine(const oracle_params* p, const float* y, const int32_t* assig
     for (int64_t m = 0; m < H; ++m) {
       double acc = 0.0;
       for (int64_t j = 0; j < k; ++j)
-        acc += static_cast<double>(w[t * k + j]) *
+        acc += combine_coef(p, static_cast<double>(w[t * k + j])) *
                static_cast<double>(y[static_cast<int64_t>(assign_pos[t * k + j]) * H + m]);
       if (shared) acc += widen(shared, p->act_dtype, t * H + m);
       out64[t * H + m] = acc;
@@ -392,6 +476,9 @@ void oracle_combine(const oracle_params* p, const float* y, const int32_t* assig
 
 /* ---- whole forward, token by token ---------------------------------------- */
 
+/* The whole forward, token by token. Pinned by the dense brute force over all expert
+   subsets (tests/bruteforce.py), the closed forms, the linearity and layout equivalences,
+   and the hand-worked examples in tests/golden/. */
 void oracle_forward(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc2,
                     const oracle_stack* fc3, const void* x, const void* logits, const void* shared,
                     int64_t n_sel, const int64_t* sel, double* out64, void* out_rounded,
@@ -407,14 +494,17 @@ void oracle_forward(const oracle_params* p, const oracle_stack* fc1, const oracl
     route_token(p, logits, t, ids.data(), w.data());
     widen_row(x, p->act_dtype, t, H, xr.data());
     if (p->int8_act) int8_round_row(p, xr.data(), H);
+    std::vector<double> xin(H);
     for (int64_t j = 0; j < k; ++j) {
-      expert_fc1(p, fc1, fc3, ids[j], xr.data(), h.data());
+      for (int64_t i = 0; i < H; ++i) xin[i] = p->on_input ? w[j] * xr[i] : xr[i];
+      expert_fc1(p, fc1, fc3, ids[j], xin.data(), h.data());
       if (p->int8_act) {
         for (int64_t i = 0; i < I; ++i) h[i] = to_act_dtype(p, h[i]);
         int8_round_row(p, h.data(), I);
       }
       expert_fc2(p, fc2, ids[j], h.data(), y.data());
-      for (int64_t m = 0; m < H; ++m) acc[m] += w[j] * y[m];
+      const double c = combine_coef(p, w[j]);
+      for (int64_t m = 0; m < H; ++m) acc[m] += c * y[m];
     }
     for (int64_t m = 0; m < H; ++m) {
       double v = acc[m] + (shared ? widen(shared, p->act_dtype, t * H + m) : 0.0);

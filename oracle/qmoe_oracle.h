@@ -23,8 +23,12 @@
  *            the activation dtype (ClikaRT "QMoEWoQ" page, forward)
  *   int8     (optional) x and h rounded to per-block int8 before fc1 and fc2
  *            (ClikaRT "QMoEWoQ" page, class description: the int8 block tier)
+ *   variants (optional) gelu, the routing weight on the input, an expert output scale,
+ *            the sparse mixer routing (CLIKA "MoE" page, routing kwargs; graiphic "QMoE"
+ *            page, activation_type and use_sparse_mixer)
  *
- * Parity status of each function is stated in its comment in qmoe_oracle.cpp.
+ * What pins each function (tests/test_oracle_pins.py) is listed beside it in
+ * qmoe_oracle.cpp.
  */
 #ifndef QMOE_ORACLE_H
 #define QMOE_ORACLE_H
@@ -35,7 +39,8 @@ extern "C" {
 #endif
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E8M0 = 2 /* scales only: 2^(e-127), MX FP4 codes */ };
-enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_IDENTITY = 1, ORACLE_ACT_RELU = 2, ORACLE_ACT_SILU = 3 };
+enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_IDENTITY = 1, ORACLE_ACT_RELU = 2, ORACLE_ACT_SILU = 3,
+       ORACLE_ACT_GELU = 4 };
 
 typedef struct {
   int64_t T, H, I, E, k;
@@ -56,6 +61,16 @@ typedef struct {
   /* 1: the int8 activation tier, x and h rounded to per-block int8 before each GEMM */
   int32_t int8_act;
   int32_t pad2_;
+  /* gelu (ORACLE_ACT_GELU): 0 the exact x * Phi(x), 1 the tanh approximation */
+  int32_t gelu_mode;
+  /* 1: the routing weight multiplies the expert's input row instead of its output */
+  int32_t on_input;
+  /* multiplies every expert's output (fc2 with its bias) before the combine; 0 means 1 */
+  double out_scale;
+  /* 1: the sparse mixer routing (k = 2) with threshold mixer_eps */
+  int32_t sparse_mixer;
+  int32_t pad3_;
+  double mixer_eps;
 } oracle_params;
 
 typedef struct {
@@ -77,17 +92,19 @@ int64_t oracle_permute(const oracle_params* p, int32_t M, const int32_t* ids, in
 double oracle_weight(const oracle_params* p, const oracle_stack* st, int64_t N, int64_t K,
                      int64_t e, int64_t n, int64_t kk);
 
-/* fc1 + activation for rows: h[r,:] = act(fc1(x[row_token[r]])) through expert row_expert[r]. */
+/* fc1 + activation for rows: h[r,:] = act(fc1(x[row_token[r]])) through expert row_expert[r];
+   with row_w (may be NULL) the input row is x[row_token[r]] * row_w[r]. */
 void oracle_fc1_rows(const oracle_params* p, const oracle_stack* fc1, const oracle_stack* fc3,
                      const void* x, int64_t n_rows, const int32_t* row_token,
-                     const int32_t* row_expert, double* h, int nthreads);
+                     const int32_t* row_expert, const double* row_w, double* h, int nthreads);
 
 /* fc2 for rows: y[r,:] = fc2(h_in[row_index[r]]) through expert row_expert[r]; h_in in act dtype. */
 void oracle_fc2_rows(const oracle_params* p, const oracle_stack* fc2, const void* h_in,
                      int64_t n_rows, const int32_t* row_index, const int32_t* row_expert,
                      double* y, int nthreads);
 
-/* Combine: out[t] = sum_j w[t,j] * y[assign_pos[t*k+j]] (+ shared[t]). */
+/* Combine: out[t] = sum_j c[t,j] * y[assign_pos[t*k+j]] (+ shared[t]), c = w (or 1 when the
+   weight went to the input) times the expert output scale. */
 void oracle_combine(const oracle_params* p, const float* y, const int32_t* assign_pos,
                     const float* w, const void* shared, double* out64, void* out_rounded);
 

@@ -57,6 +57,16 @@ class Config:
     ebias_sigma: float = 0.5
     # the int8 activation tier (ClikaRT "QMoEWoQ" page, class description)
     int8: bool = False
+    # the remaining routing kwargs and activations (CLIKA "MoE" page: gelu_mode,
+    # apply_router_weight_on_input, expert_output_scale, sparse_mixer_eps; graiphic "QMoE"
+    # page: activation_type gelu, use_sparse_mixer): gelu_mode 0 the exact gelu, 1 its tanh
+    # approximation; on_input: the routing weight scales the expert's input; out_scale:
+    # multiplies every expert's output; sparse_mixer: the two-pick sparse mixer routing
+    gelu_mode: int = 0
+    on_input: bool = False
+    out_scale: float = 1.0
+    sparse_mixer: bool = False
+    mixer_eps: float = 0.01
 
     def with_(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)

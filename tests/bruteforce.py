@@ -8,7 +8,10 @@ It is built differently from the oracle on purpose:
 * every expert's FFN is evaluated for every token and mixed through a dense
   [T, E] gate matrix; no grouping or permutation is involved;
 * the sigmoid comes from scipy;
-* the int8 activation tier's scale is found by trying every power of two in turn.
+* the int8 activation tier's scale is found by trying every power of two in turn;
+* gelu comes from torch (both of its forms), in float64;
+* with the routing weight on the input, each expert's fc1 output is scaled by the dense
+  gate weight (linearity) and the outputs are mixed through the 0/1 selection matrix.
 
 Sources for what is computed: CLIKA "MoE" page (router picks top-k experts,
 gated FFN, outputs combined under the router weights); CLIKA "QLinearWoQ" page
@@ -20,6 +23,7 @@ from __future__ import annotations
 import itertools
 
 import numpy as np
+import torch
 from scipy.special import expit
 
 from synth.gen import as_f32
@@ -132,7 +136,9 @@ def _act_pair(cfg, g, u):
     return g * expit(cfg.alpha * g) * (u + cfg.beta)
 
 
-def forward(cfg, inp) -> np.ndarray:
+def forward(cfg, inp, mixer_gates=None) -> np.ndarray:
+    """The dense forward. mixer_gates: the [T, E] routing weights to mix with instead of the
+    subset search (the sparse mixer's routing is pinned on its own)."""
     x = as_f32(inp.x, cfg.act_dtype).astype(np.float64)
     lg = as_f32(inp.logits, cfg.act_dtype).astype(np.float64)
     E, H, I = cfg.E, cfg.H, cfg.I
@@ -144,7 +150,11 @@ def forward(cfg, inp) -> np.ndarray:
 
     if cfg.int8:
         x = int8_round(x, cfg.block_size)
-    z1 = np.einsum("th,enh->etn", x, W1) + (0.0 if inp.b1 is None else bias(inp.b1)[:, None, :])
+    eb = None if inp.ebias is None else as_f32(inp.ebias, cfg.act_dtype)
+    G = gates(cfg, lg, eb) if mixer_gates is None else mixer_gates
+    # the routing weight on the input: expert e sees G[t, e] * x_t, and x -> x W^T is linear
+    gin = G.T[:, :, None] if cfg.on_input else 1.0
+    z1 = gin * np.einsum("th,enh->etn", x, W1) + (0.0 if inp.b1 is None else bias(inp.b1)[:, None, :])
     if cfg.activation == "swiglu":
         if cfg.fusion == 1:
             g, u = z1[:, :, 0::2], z1[:, :, 1::2]
@@ -152,7 +162,7 @@ def forward(cfg, inp) -> np.ndarray:
             g, u = z1[:, :, :I], z1[:, :, I:]
         else:
             W3 = dequant_dense(inp.w3, inp.s3, cfg, I, H)
-            z3 = np.einsum("th,enh->etn", x, W3) + (0.0 if inp.b3 is None else bias(inp.b3)[:, None, :])
+            z3 = gin * np.einsum("th,enh->etn", x, W3) + (0.0 if inp.b3 is None else bias(inp.b3)[:, None, :])
             g, u = z1, z3
         h = _act_pair(cfg, g, u)
     elif cfg.activation == "identity":
@@ -161,14 +171,17 @@ def forward(cfg, inp) -> np.ndarray:
         h = np.maximum(z1, 0.0)
     elif cfg.activation == "silu":
         h = z1 * expit(z1)
+    elif cfg.activation == "gelu":
+        h = torch.nn.functional.gelu(torch.from_numpy(z1),
+                                     approximate="tanh" if cfg.gelu_mode else "none").numpy()
     else:
         raise ValueError(cfg.activation)
     if cfg.int8:
         h = int8_round(round_act(h, cfg.act_dtype), cfg.block_size)
     y = np.einsum("eti,ehi->eth", h, W2) + (0.0 if inp.b2 is None else bias(inp.b2)[:, None, :])
-    eb = None if inp.ebias is None else as_f32(inp.ebias, cfg.act_dtype)
-    G = gates(cfg, lg, eb)
-    out = np.einsum("te,eth->th", G, y)
+    y = y * (cfg.out_scale if cfg.out_scale != 0 else 1.0)
+    mix = (G != 0).astype(np.float64) if cfg.on_input else G
+    out = np.einsum("te,eth->th", mix, y)
     if inp.shared is not None:
         out = out + as_f32(inp.shared, cfg.act_dtype).astype(np.float64)
     return out

@@ -12,6 +12,7 @@ Run: python tests/golden/make_hand_examples.py
 import json
 import math
 import os
+import struct
 
 
 def sigmoid(v):
@@ -64,8 +65,62 @@ cases.append(dict(
     expect=[[sigmoid(0.5) * sigmoid(1.0)] * 32],
 ))
 
+# Sparse mixer routing (graiphic "QMoE" page, use_sparse_mixer; CLIKA "MoE" page,
+# sparse_mixer_eps; the SparseMixer top-2 router as published for Phi-3.5-MoE): pick 1 is
+# the largest logit m1, pick 2 the largest of the others m2 (ties: lower index). A pick
+# keeps expert e unless (m - l_e) / max(|l_e|, m) > 2 eps (the second pick never keeps
+# the first); its weight is exp(m - m) / sum over the kept experts of exp(l_e - m).
+# The logits are stored as float32, so each closed form below uses the float32 values
+# (f32() rounds a literal the way the stored logit is rounded).
+
+
+def f32(v):
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+mixer = []
+eps = 0.01
+# A: l = (2, 1.99, 0.5, -1). Pick 1 (expert 0, m = 2): expert 1 trails by 0.01/2 = 0.005
+# <= 0.02 and is kept; 0.5 trails by 1.5/2 and -1 by 3/2: dropped. w1 = 1/(1 + e^(l1-l0)).
+# Pick 2 (expert 1, m = 1.99): 0.5 trails by 1.49/1.99, -1 by 2.99/1.99: dropped; w2 = 1.
+la = [f32(2.0), f32(1.99), f32(0.5), f32(-1.0)]
+mixer.append(dict(name="keeps-a-near-tie", eps=eps, logits=[la],
+                  ids=[[0, 1]], w=[[1.0 / (1.0 + math.exp(la[1] - la[0])), 1.0]]))
+# B: negative logits (-1, -1.01, -1.015, -3). Pick 1 (m = -1, so max(|l|, m) = |l|):
+# 0.01/1.01 and 0.015/1.015 are kept, 2/3 is dropped. w1 = 1/(1 + e^(l1-l0) + e^(l2-l0)).
+# Pick 2 (expert 1, m = -1.01): expert 2 trails by 0.005/1.015 (kept), expert 3 by 1.99/3
+# (dropped). w2 = 1/(1 + e^(l2-l1)).
+lb = [f32(-1.0), f32(-1.01), f32(-1.015), f32(-3.0)]
+mixer.append(dict(name="negative-logits", eps=eps, logits=[lb], ids=[[0, 1]],
+                  w=[[1.0 / (1.0 + math.exp(lb[1] - lb[0]) + math.exp(lb[2] - lb[0])),
+                      1.0 / (1.0 + math.exp(lb[2] - lb[1]))]]))
+# C: ties (1, 1, 0, 1). Pick 1 takes expert 0; the other 1s trail by 0 (kept), the 0 by
+# 1/1 (dropped): w1 = 1/3. Pick 2 takes expert 1 (the lowest of the remaining ties), keeps
+# expert 3: w2 = 1/2.
+mixer.append(dict(name="ties-to-lower-index", eps=eps, logits=[[1.0, 1.0, 0.0, 1.0]],
+                  ids=[[0, 1]], w=[[1.0 / 3.0, 0.5]]))
+# D: zero logits (0, 0, -0.5, 0). Pick 1 (m = 0): the other zeros give 0/0, which is not
+# above the threshold, so they are kept; -0.5 trails by 0.5/0.5 = 1: dropped. w1 = 1/3.
+# Pick 2 (expert 1, m = 0) keeps expert 3 the same way: w2 = 1/2.
+mixer.append(dict(name="zero-over-zero-keeps", eps=eps, logits=[[0.0, 0.0, -0.5, 0.0]],
+                  ids=[[0, 1]], w=[[1.0 / 3.0, 0.5]]))
+# E: eps = 0.3 (threshold 0.6) on (4, 1, 3, 2): pick 1 (m = 4) keeps 3 (1/4) and 2
+# (2/4), drops 1 (3/4): w1 = 1/(1 + e^-1 + e^-2). Pick 2 takes expert 2 (m = 3): expert 3
+# trails by 1/3 (kept), expert 1 by 2/3 (dropped): w2 = 1/(1 + e^-1).
+mixer.append(dict(name="wide-threshold", eps=0.3, logits=[[4.0, 1.0, 3.0, 2.0]],
+                  ids=[[0, 2]],
+                  w=[[1.0 / (1.0 + math.exp(-1.0) + math.exp(-2.0)), 1.0 / (1.0 + math.exp(-1.0))]]))
+
+# F: the denominator is max(|l|, m), not |m|: l = (-1, -1.0204, -5, -6). Pick 1 (m = -1):
+# expert 1 trails by 0.0204 / 1.0204 = 0.019992 <= 0.02 and is kept (0.0204 / |m| would
+# drop it); experts 2 and 3 trail by 4/5 and 5/6: dropped. w1 = 1/(1 + e^(l1-l0)).
+# Pick 2 (expert 1) drops experts 2 and 3 (3.98/5, 4.98/6): w2 = 1.
+lf = [f32(-1.0), f32(-1.0204), f32(-5.0), f32(-6.0)]
+mixer.append(dict(name="denominator-is-max-of-abs-and-pick", eps=eps, logits=[lf],
+                  ids=[[0, 1]], w=[[1.0 / (1.0 + math.exp(lf[1] - lf[0])), 1.0]]))
+
 here = os.path.dirname(os.path.abspath(__file__))
 with open(os.path.join(here, "hand_examples.json"), "w") as f:
     json.dump({"source": "closed forms derived by hand; see make_hand_examples.py",
-               "cases": cases}, f, indent=1)
-print("wrote", len(cases), "cases")
+               "cases": cases, "mixer_cases": mixer}, f, indent=1)
+print("wrote", len(cases), "forward cases and", len(mixer), "sparse mixer cases")

@@ -64,6 +64,18 @@ BRUTE_CASES = {
     "bf16-int8-mxfp4-separate": configs.tiny(act_dtype="bf16", scale_dtype="e8m0", bits=4,
                                              block_size=32, H=96, I=64, fusion=0,
                                              scale_lo=0.01, scale_hi=0.2, int8=True),
+    # gelu (both forms), the routing weight on the input, the expert output scale
+    "f32-gelu-exact-bias": configs.tiny(activation="gelu", fusion=0, gelu_mode=0, fc1_bias=True,
+                                        fc2_bias=True),
+    "bf16-gelu-tanh-b8": configs.tiny(activation="gelu", fusion=0, gelu_mode=1, bits=8,
+                                      act_dtype="bf16", scale_dtype="bf16"),
+    "f32-on-input-interleaved-bias-clamp": configs.tiny(on_input=True, fusion=1, fc1_bias=True,
+                                                        fc2_bias=True, limit=3.0, E=5, k=3),
+    "bf16-on-input-separate-out-scale": configs.tiny(act_dtype="bf16", scale_dtype="bf16",
+                                                     fusion=0, on_input=True, out_scale=0.75,
+                                                     fc2_bias=True, fc1_bias=True),
+    "f32-out-scale-norenorm-gelu": configs.tiny(out_scale=2.0, normalize=False, fc2_bias=True,
+                                                activation="gelu", fusion=0, E=6, k=3),
 }
 
 
@@ -575,3 +587,118 @@ def test_golden_hand_examples():
         inp.s2[...] = case["s2_fill"]
         out64, _ = oracle.forward(cfg, inp)
         assert np.allclose(out64, np.asarray(case["expect"]), rtol=1e-15, atol=1e-15), case["name"]
+
+
+# --------------------------------------------------------------------------- gelu
+
+@pytest.mark.parametrize("mode,approx", [(0, "none"), (1, "tanh")])
+def test_gelu_matches_torch_and_scipy(mode, approx):
+    """The single-expert layer with gelu (E = 1, k = 1: out = fc2(gelu(fc1(x)))) against torch's
+    gelu on the dense dequantised weights; the exact form also against scipy's normal CDF;
+    and the odd identity gelu(z) - gelu(-z) = z that both forms satisfy."""
+    from scipy.special import ndtr
+    cfg = configs.tiny(E=1, k=1, activation="gelu", fusion=0, gelu_mode=mode, fc1_bias=True,
+                       H=64, I=48, scale_lo=0.05, scale_hi=0.2)
+    inp = gen.make_inputs(cfg, 9)
+    x = as_f32(inp.x, "f32").astype(np.float64)
+    W1 = bruteforce.dequant_dense(inp.w1, inp.s1, cfg, cfg.I, cfg.H)[0]
+    z = x @ W1.T + as_f32(inp.b1, "f32").astype(np.float64)[0]
+    h_torch = torch.nn.functional.gelu(torch.from_numpy(z), approximate=approx).numpy()
+    rows = oracle.fc1_rows(cfg, inp, np.arange(9), np.zeros(9, np.int32))
+    assert np.max(np.abs(rows - h_torch)) <= 1e-12 * max(np.max(np.abs(h_torch)), 1.0)
+    assert np.max(np.abs(z)) > 2.0  # the tails are exercised
+    if mode == 0:
+        assert np.max(np.abs(rows - z * ndtr(z))) <= 1e-12 * np.max(np.abs(z))
+    # odd identity: h(z) - h(-z) = z, through the linear layer with x and -x
+    neg = gen.make_inputs(cfg, 9)
+    neg.x[...] = (-as_f32(inp.x, "f32")).astype(np.float32)
+    neg.b1[...] = (-as_f32(inp.b1, "f32")).astype(np.float32)
+    hn = oracle.fc1_rows(cfg, neg, np.arange(9), np.zeros(9, np.int32))
+    assert np.max(np.abs((rows - hn) - z)) <= 1e-12 * np.max(np.abs(z))
+
+
+# --------------------------------------------------------------------------- weights on input
+
+def test_weight_on_input_is_linear_for_identity_experts():
+    """With identity activation and no biases each expert is linear, so the routing weight may
+    go to the input or to the output with the same result (closed form of linearity)."""
+    base = configs.tiny(activation="identity", fusion=0, E=6, k=3, logit_sigma=2.0)
+    inp = gen.make_inputs(base, 11)
+    a, _ = oracle.forward(base, inp)
+    b, _ = oracle.forward(base.with_(on_input=True), inp)
+    assert np.max(np.abs(a - b)) <= 1e-12 * rms(a)
+
+
+def test_weight_on_input_with_k1_renorm_is_the_plain_forward():
+    """k = 1 with renormalisation gives weight 1: on the input or the output, the same."""
+    base = configs.tiny(k=1, fusion=1, fc1_bias=True, fc2_bias=True, limit=2.0)
+    inp = gen.make_inputs(base, 7)
+    a, _ = oracle.forward(base, inp)
+    b, _ = oracle.forward(base.with_(on_input=True), inp)
+    assert np.array_equal(a, b)
+
+
+def test_expert_output_scale_scales_the_routed_part():
+    base = configs.tiny(fusion=2, fc2_bias=True, E=5, k=2)
+    inp = gen.make_inputs(base, 6, shared=True)
+    a, _ = oracle.forward(base, inp)
+    b, _ = oracle.forward(base.with_(out_scale=-0.375), inp)
+    sh = as_f32(inp.shared, "f32").astype(np.float64)
+    assert np.max(np.abs((b - sh) - (-0.375) * (a - sh))) <= 1e-12 * rms(a)
+    c, _ = oracle.forward(base.with_(out_scale=0.0), inp)  # 0 means 1
+    assert np.array_equal(a, c)
+
+
+# --------------------------------------------------------------------------- sparse mixer
+
+def _mixer_cfg(E, eps, **kw):
+    return configs.tiny(E=E, k=2, sparse_mixer=True, mixer_eps=eps, normalize=False, **kw)
+
+
+def test_sparse_mixer_hand_examples():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        cases = json.load(f)["mixer_cases"]
+    assert len(cases) >= 5
+    for case in cases:
+        lg = np.asarray(case["logits"], np.float32)
+        cfg = _mixer_cfg(lg.shape[1], case["eps"])
+        ids, w = oracle.route(cfg, lg)
+        assert ids.tolist() == case["ids"], case["name"]
+        assert np.allclose(w, np.asarray(case["w"]), rtol=1e-14, atol=0), case["name"]
+
+
+def test_sparse_mixer_limits():
+    """eps beyond every ratio keeps every expert: the picks' weights are plain softmaxes
+    (scipy), the second over the experts other than the first; eps = 0 with distinct
+    logits keeps only the pick itself: weights 1. The picks are the two largest logits
+    (numpy's stable argsort)."""
+    rng = np.random.default_rng(11)
+    lg = rng.normal(0, 1.5, (50, 9)).astype(np.float32)
+    l64 = lg.astype(np.float64)
+    order = np.argsort(-l64, axis=1, kind="stable")[:, :2]
+    ids, w = oracle.route(_mixer_cfg(9, 1e30), lg)
+    assert np.array_equal(ids, order)
+    for t in range(lg.shape[0]):
+        e1, e2 = order[t]
+        assert abs(w[t, 0] - softmax(l64[t])[e1]) < 1e-14
+        rest = np.delete(l64[t], e1)
+        assert abs(w[t, 1] - softmax(rest)[e2 - (e2 > e1)]) < 1e-14
+    ids0, w0 = oracle.route(_mixer_cfg(9, 0.0), lg)
+    assert np.array_equal(ids0, order) and np.all(w0 == 1.0)
+    ids2, w2 = oracle.route(_mixer_cfg(9, 0.0, routed_scale=2.5), lg)
+    assert np.all(w2 == 2.5)
+
+
+def test_sparse_mixer_forward_composes_with_its_routing():
+    """The forward with the mixer mixes the dense expert outputs (brute force) under the
+    mixer's routing weights, whose values are pinned above."""
+    cfg = _mixer_cfg(6, 0.05, fusion=1, fc1_bias=True, fc2_bias=True, logit_sigma=0.3)
+    inp = gen.make_inputs(cfg, 9)
+    ids, w = oracle.route(cfg, inp.logits)
+    G = np.zeros((9, cfg.E))
+    for t in range(9):
+        G[t, ids[t]] = w[t]
+    assert np.mean(w[:, 0] < 0.999) > 0.3  # the threshold keeps neighbours for many tokens
+    ref = bruteforce.forward(cfg, inp, mixer_gates=G)
+    out64, _ = oracle.forward(cfg, inp)
+    assert np.max(np.abs(out64 - ref)) <= 1e-11 * rms(ref)
