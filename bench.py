@@ -307,8 +307,8 @@ def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
             x = xq
         if timed:
             run(lib.qmoe_time_next_gemm(evp[i][0], evp[i][1]))
-        run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(x), ptr(sa), ptr(tl), ptr(nt), s1, s3,
-                                             ptr(h), sid))
+        run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(x), ptr(sa), ptr(tl), ptr(nt), ptr(w), s1,
+                                             s3, ptr(h), sid))
         if cfg.int8:
             run(lib.qmoe_quantize_act(p, ptr(h), rows, cfg.I, ptr(h), sid))
         if timed:

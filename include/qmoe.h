@@ -71,12 +71,15 @@ typedef enum { QMOE_LAYOUT_ROWS = 0, QMOE_LAYOUT_TILES = 1 } qmoe_layout;
 /* Which stack of a forward: fc1 (gate, or fused gate/up), fc2 (down), fc3 (separate up). */
 typedef enum { QMOE_FC1 = 1, QMOE_FC2 = 2, QMOE_FC3 = 3 } qmoe_which;
 
-/* activation_type of the graiphic "QMoE" page. gelu is not provided. */
+/* activation_type of the graiphic "QMoE" page (relu, gelu, silu, swiglu, identity). gelu is
+   the plain activation z * Phi(z) (Phi the standard normal CDF) or its tanh approximation,
+   as qmoe_params.gelu_mode selects (CLIKA "MoE" page, routing kwarg gelu_mode). */
 typedef enum {
   QMOE_ACT_SWIGLU = 0,
   QMOE_ACT_IDENTITY = 1,
   QMOE_ACT_RELU = 2,
-  QMOE_ACT_SILU = 3
+  QMOE_ACT_SILU = 3,
+  QMOE_ACT_GELU = 4
 } qmoe_act;
 
 typedef struct {
@@ -131,6 +134,30 @@ typedef struct {
      of h are decided from h, and a last-bit difference in an fp32 h, from summation
      order, can move one code by a step, which is worth more than the fp32 path's bound). */
   int32_t compute_mode;
+  /* The remaining options of the CLIKA "MoE" page's routing kwargs and the graiphic "QMoE"
+     page's attributes:
+     gelu_mode (activation QMOE_ACT_GELU): 0 = z * Phi(z) through erf, 1 = the tanh
+       approximation 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+     expert_output_scale: multiplies every expert's output (fc2 with its bias) before the
+       combine, the shared output excepted; 0 means 1. Applied by qmoe_combine.
+     apply_router_weight_on_input: non-zero: the routing weight multiplies the row that
+       enters the expert (fc1 takes w * x, as its epilogue scales the fp32 sum by w before
+       the bias), and the combine sums the expert outputs with weight 1. Not with the int8
+       tier (QMOE_ERR_UNSUPPORTED: its codes would depend on each slot's weight).
+     use_sparse_mixer: the sparse mixer routing (graiphic use_sparse_mixer; CLIKA
+       sparse_mixer_eps), read from its published definition (the SparseMixer top-2 router
+       of Phi-3.5-MoE): k must be 2, normalize_routing_weights 0, no grouping and no
+       selection bias (QMOE_ERR_INVALID otherwise). Pick 1 is the largest logit m1, pick 2
+       the largest of the others m2 (equal logits: lower index); pick j keeps expert e
+       unless (mj - l_e) / max(|l_e|, mj) > 2 * sparse_mixer_eps (decided in fp32; pick 2
+       never keeps pick 1), and its weight is the softmax at the picked expert over the
+       experts it keeps; routed_scaling_factor still applies. sparse_mixer_eps: finite,
+       >= 0. */
+  int32_t gelu_mode;
+  float expert_output_scale;
+  int32_t apply_router_weight_on_input;
+  int32_t use_sparse_mixer;
+  float sparse_mixer_eps;
 } qmoe_params;
 
 typedef enum { QMOE_COMPUTE_FLOAT = 0, QMOE_COMPUTE_INT8 = 1 } qmoe_compute_mode;
@@ -240,14 +267,17 @@ qmoe_status qmoe_permute(const qmoe_params* p, const int32_t* topk_ids, int32_t*
  *   fc3: separate up stack [E, I, H*bits/8] (only with swiglu and swiglu_fusion 0);
  *   h [max_rows, I] act_dtype (written for every real row of every tile; padding rows
  *   of a tile are written as zeros).
+ *   topk_w [T*k] float32 from qmoe_route: read only with apply_router_weight_on_input
+ *   (required then, QMOE_ERR_UNBOUND if NULL; may be NULL otherwise).
  * Row r of tile i (expert e, r < valid) computes, for a = sorted_assign[i*M + r] and
- * t = a / k: z = x[t] . dequant(W1_e)^T + b1_e, then h = act(z) (SwiGLU on the
- * gate/up pair selected by swiglu_fusion).
+ * t = a / k: z = c * (x[t] . dequant(W1_e)^T) + b1_e, with c = topk_w[a] under
+ * apply_router_weight_on_input and 1 otherwise, then h = act(z) (SwiGLU on the gate/up
+ * pair selected by swiglu_fusion).
  */
 qmoe_status qmoe_grouped_gemm_fc1_swiglu(const qmoe_params* p, const void* x,
                                          const int32_t* sorted_assign, const int32_t* tile_list,
-                                         const int32_t* num_tiles, qmoe_stack fc1, qmoe_stack fc3,
-                                         void* h, void* stream);
+                                         const int32_t* num_tiles, const float* topk_w,
+                                         qmoe_stack fc1, qmoe_stack fc3, void* h, void* stream);
 
 /*
  * fc2 grouped GEMM (graiphic "QMoE" page: fc2_experts_weights [E, H, I*bits/8],
@@ -263,7 +293,8 @@ qmoe_status qmoe_grouped_gemm_fc2(const qmoe_params* p, const void* h, const int
  * Weighted combine (CLIKA "MoE" page: outputs combine under the router weights;
  * ClikaRT "QMoEWoQ" page forward: shared_output folds into the same epilogue and the
  * result takes x's dtype).
- *   out[t, :] = round( sum_{j<k} topk_w[t, j] * y[assign_pos[t*k + j], :] + shared[t, :] )
+ *   out[t, :] = round( sum_{j<k} c[t, j] * y[assign_pos[t*k + j], :] + shared[t, :] )
+ * with c = topk_w[t, j] (1 under apply_router_weight_on_input) times expert_output_scale,
  * summed in float32 in slot order j, rounded once (nearest-even) to act_dtype.
  * shared_output [T, H] act_dtype may be NULL. No atomics: each output is written once.
  */
@@ -366,7 +397,8 @@ qmoe_status qmoe_quantize_act(const qmoe_params* p, const void* in, int64_t rows
  * the grouped GEMM of this library over one expert and no routing.
  *   p: the parameter block read as one layer -- num_experts 1, k 1; num_tokens = rows of
  *      x (T), hidden_size = in_features (K), inter_size = out_features (N); activation
- *      QMOE_ACT_IDENTITY, _RELU or _SILU (swiglu is rejected, QMOE_ERR_INVALID);
+ *      QMOE_ACT_IDENTITY, _RELU, _SILU or _GELU (swiglu is rejected, QMOE_ERR_INVALID;
+ *      so is apply_router_weight_on_input, which has no routing weight here);
  *      expert_weight_bits, block_size, scale_dtype, act_dtype, tile_m and weight_layout
  *      as for the expert stacks.
  *   x [T, K] act_dtype; w.weights uint8 [N, K*bits/8] (QMOE_LAYOUT_ROWS, dequant

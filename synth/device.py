@@ -43,7 +43,11 @@ def params_for(cfg, T: int, tile_m: int = 0, strict: bool = False, layout: str =
                           strict_blocks=strict, weight_layout=layout, n_group=cfg.n_group,
                           topk_group=cfg.topk_group, routed_scaling_factor=cfg.routed_scale,
                           e_score_correction_bias=ebias,
-                          compute_mode="int8" if cfg.int8 else "float")
+                          compute_mode="int8" if cfg.int8 else "float", gelu_mode=cfg.gelu_mode,
+                          expert_output_scale=cfg.out_scale,
+                          apply_router_weight_on_input=cfg.on_input,
+                          use_sparse_mixer=cfg.sparse_mixer,
+                          sparse_mixer_eps=cfg.mixer_eps if cfg.sparse_mixer else 0.0)
 
 
 class DeviceInputs:

@@ -146,7 +146,7 @@ def test_unbound_pointers(lib):
     assert b"fc2.scales" in lib.qmoe_last_error()
     # separate gate/up stacks need fc3
     p0 = good(swiglu_fusion=0)
-    assert lib.qmoe_grouped_gemm_fc1_swiglu(p0, V(16), V(16), V(16), V(16), full,
+    assert lib.qmoe_grouped_gemm_fc1_swiglu(p0, V(16), V(16), V(16), V(16), None, full,
                                             _lib.QmoeStack(), V(16), None) == \
         _lib.QMOE_ERR_UNBOUND
     assert b"fc3" in lib.qmoe_last_error()
@@ -224,6 +224,12 @@ def test_every_gpu_parity_case_passes_validation(lib):
     for E, k, T, _ in t.FUSED_ROUTING_CASES + t.FUSED_ROUTING_EDGES:
         cases.append((configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64,
                                    bits=4, block_size=32, fusion=1), T, 0, "rows", "fused"))
+    from tests import test_gpu_variants as v
+    cases += [(cfg, 300 if m == 128 else 40, m, lay, "variant stage " + n)
+              for n, cfg in v.STAGE_VARIANTS.items() for m in (16, 32, 128)
+              for lay in ("rows", "tiles")]
+    cases += [(v._mixer(E, eps, act), 257, 0, "rows", "mixer")
+              for E, eps, act in ((8, 0.01, "bf16"), (64, 0.2, "f32"), (300, 0.01, "bf16"))]
     bad = []
     for cfg, T, m, lay, what in cases:
         if lib.qmoe_validate(params_for(cfg, T, tile_m=m, layout=lay)) != 0:
@@ -270,6 +276,39 @@ def test_mxfp4_params(lib):
     p = good(**mx)
     p.scale_dtype = 3
     assert status(p) == _lib.QMOE_ERR_DTYPE
+
+
+def test_variant_params(lib):
+    """gelu takes gelu_mode 0 or 1; the sparse mixer picks k = 2 without renormalisation,
+    grouping or selection bias, with a finite eps >= 0; the weight on the input is refused
+    with the int8 tier and in the linear layer; the output scale must be finite (no device
+    is touched on these paths)."""
+    assert status(good(activation="gelu", swiglu_fusion=0)) == _lib.QMOE_OK
+    assert status(good(activation="gelu", swiglu_fusion=0, gelu_mode=2)) == _lib.QMOE_ERR_INVALID
+    assert status(good(activation="gelu", swiglu_fusion=1)) == _lib.QMOE_ERR_INVALID
+    mix = dict(k=2, normalize_routing_weights=False, use_sparse_mixer=True, sparse_mixer_eps=0.01)
+    assert status(good(**mix)) == _lib.QMOE_OK
+    assert status(good(**dict(mix, k=3))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mix, normalize_routing_weights=True))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mix, sparse_mixer_eps=-1.0))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mix, sparse_mixer_eps=math.inf))) == _lib.QMOE_ERR_INVALID
+    assert status(good(**dict(mix, n_group=2, topk_group=1))) == _lib.QMOE_ERR_INVALID
+    assert status(good(apply_router_weight_on_input=True)) == _lib.QMOE_OK
+    assert status(good(apply_router_weight_on_input=True,
+                       compute_mode="int8")) == _lib.QMOE_ERR_UNSUPPORTED
+    assert status(good(expert_output_scale=math.nan)) == _lib.QMOE_ERR_INVALID
+    lp = qm.linear_params(8, 256, 128, block_size=32, activation="gelu")
+    assert status(lp) == _lib.QMOE_OK
+    full = _lib.QmoeStack(weights=1 << 20, scales=1 << 20, bias=None)
+    lp.apply_router_weight_on_input = 1
+    assert lib.qmoe_linear_woq(lp, 1 << 20, full, 1 << 20, None) == _lib.QMOE_ERR_INVALID
+    # the fc1 entry point needs the routing weights when they go to the input
+    V = ctypes.c_void_p
+    p = good(apply_router_weight_on_input=True)
+    assert lib.qmoe_grouped_gemm_fc1_swiglu(p, V(16), V(16), V(16), V(16), None, full,
+                                            _lib.QmoeStack(), V(16), None) == \
+        _lib.QMOE_ERR_UNBOUND
+    assert b"topk_w" in lib.qmoe_last_error()
 
 
 def test_int8_tier_params(lib):

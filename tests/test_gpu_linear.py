@@ -33,7 +33,7 @@ def lin_params(cfg, T, layout="rows", tile_m=0):
     return qm.linear_params(T, cfg.H, cfg.I, expert_weight_bits=cfg.bits,
                             block_size=cfg.block_size, activation=cfg.activation,
                             act_dtype=cfg.act_dtype, scale_dtype=cfg.scale_dtype,
-                            tile_m=tile_m, weight_layout=layout)
+                            tile_m=tile_m, weight_layout=layout, gelu_mode=cfg.gelu_mode)
 
 
 def run_linear(cfg, inp, layout, tile_m=0):

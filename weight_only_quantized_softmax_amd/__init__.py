@@ -44,7 +44,9 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                 strict_blocks: bool = False, weight_layout: str = "rows", n_group: int = 0,
                 topk_group: int = 0, routed_scaling_factor: float = 1.0,
                 e_score_correction_bias: Optional[torch.Tensor] = None,
-                compute_mode: str = "float") -> QmoeParams:
+                compute_mode: str = "float", gelu_mode: int = 0,
+                expert_output_scale: float = 1.0, apply_router_weight_on_input: bool = False,
+                use_sparse_mixer: bool = False, sparse_mixer_eps: float = 0.0) -> QmoeParams:
     """The parameter block. e_score_correction_bias: a device tensor [E] in the activation
     dtype (the block keeps its address, so the tensor must outlive the calls)."""
     bias = None if e_score_correction_bias is None else _ptr(e_score_correction_bias,
@@ -60,7 +62,11 @@ def make_params(num_tokens: int, hidden_size: int, inter_size: int, num_experts:
                       strict_blocks=int(bool(strict_blocks)),
                       weight_layout=_LAYOUT[weight_layout], n_group=n_group,
                       topk_group=topk_group, routed_scaling_factor=routed_scaling_factor,
-                      e_score_correction_bias=bias, compute_mode=_COMPUTE[compute_mode])
+                      e_score_correction_bias=bias, compute_mode=_COMPUTE[compute_mode],
+                      gelu_mode=gelu_mode, expert_output_scale=expert_output_scale,
+                      apply_router_weight_on_input=int(bool(apply_router_weight_on_input)),
+                      use_sparse_mixer=int(bool(use_sparse_mixer)),
+                      sparse_mixer_eps=sparse_mixer_eps)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str):
@@ -156,11 +162,12 @@ def qmoe_permute(p, topk_ids, counts, padded_offsets, sorted_assign, assign_pos,
 
 
 def qmoe_grouped_gemm_fc1_swiglu(p, x, sorted_assign, tile_list, num_tiles, fc1: Stack,
-                                 fc3: Stack, h, stream=None) -> None:
+                                 fc3: Stack, h, stream=None, topk_w=None) -> None:
+    """topk_w: the routing weights [T, k], read with apply_router_weight_on_input only."""
     check(load().qmoe_grouped_gemm_fc1_swiglu(
         p, _ptr(x, "x"), _ptr(sorted_assign, "sorted_assign"), _ptr(tile_list, "tile_list"),
-        _ptr(num_tiles, "num_tiles"), _stack(fc1, "fc1"), _stack(fc3, "fc3"), _ptr(h, "h"),
-        _stream(stream)))
+        _ptr(num_tiles, "num_tiles"), _ptr(topk_w, "topk_w"), _stack(fc1, "fc1"),
+        _stack(fc3, "fc3"), _ptr(h, "h"), _stream(stream)))
 
 
 def qmoe_grouped_gemm_fc2(p, h, tile_list, num_tiles, fc2: Stack, y, stream=None) -> None:
@@ -207,13 +214,15 @@ def pack_stack(p: QmoeParams, which: str, weights: torch.Tensor, stream=None) ->
 def linear_params(num_tokens: int, in_features: int, out_features: int, *,
                   expert_weight_bits: int = 4, block_size: int = 0, activation: str = "identity",
                   act_dtype: str = "bf16", scale_dtype: str = "bf16", tile_m: int = 0,
-                  strict_blocks: bool = False, weight_layout: str = "rows") -> QmoeParams:
+                  strict_blocks: bool = False, weight_layout: str = "rows",
+                  gelu_mode: int = 0) -> QmoeParams:
     """The parameter block of a QLinearWoQ layer: one expert, k = 1."""
     return make_params(num_tokens, in_features, out_features, 1, 1,
                        expert_weight_bits=expert_weight_bits, block_size=block_size,
                        activation=activation, normalize_routing_weights=False,
                        act_dtype=act_dtype, scale_dtype=scale_dtype, tile_m=tile_m,
-                       strict_blocks=strict_blocks, weight_layout=weight_layout)
+                       strict_blocks=strict_blocks, weight_layout=weight_layout,
+                       gelu_mode=gelu_mode)
 
 
 def qmoe_linear_woq(p: QmoeParams, x, w: Stack, y, stream=None) -> None:

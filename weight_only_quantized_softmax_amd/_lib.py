@@ -16,7 +16,7 @@ QMOE_F32, QMOE_BF16, QMOE_E8M0 = 0, 1, 2
 QMOE_LAYOUT_ROWS, QMOE_LAYOUT_TILES = 0, 1
 QMOE_FC1, QMOE_FC2, QMOE_FC3 = 1, 2, 3
 QMOE_NOALLOC_SCRATCH_BYTES = 64 << 20
-ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3}
+ACT = {"swiglu": 0, "identity": 1, "relu": 2, "silu": 3, "gelu": 4}
 
 
 class QmoeParams(ctypes.Structure):
@@ -32,7 +32,10 @@ class QmoeParams(ctypes.Structure):
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float),
                 ("e_score_correction_bias", ctypes.c_void_p),
-                ("compute_mode", ctypes.c_int32)]
+                ("compute_mode", ctypes.c_int32), ("gelu_mode", ctypes.c_int32),
+                ("expert_output_scale", ctypes.c_float),
+                ("apply_router_weight_on_input", ctypes.c_int32),
+                ("use_sparse_mixer", ctypes.c_int32), ("sparse_mixer_eps", ctypes.c_float)]
 
 
 class QmoeWorkspaceLayout(ctypes.Structure):
@@ -77,7 +80,8 @@ def load() -> ctypes.CDLL:
     L.qmoe_route.argtypes, L.qmoe_route.restype = [P, vp, vp, vp, vp], st
     L.qmoe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qmoe_permute.restype = st
-    L.qmoe_grouped_gemm_fc1_swiglu.argtypes = [P, vp, vp, vp, vp, QmoeStack, QmoeStack, vp, vp]
+    L.qmoe_grouped_gemm_fc1_swiglu.argtypes = [P, vp, vp, vp, vp, vp, QmoeStack, QmoeStack, vp,
+                                               vp]
     L.qmoe_grouped_gemm_fc1_swiglu.restype = st
     L.qmoe_grouped_gemm_fc2.argtypes = [P, vp, vp, vp, QmoeStack, vp, vp]
     L.qmoe_grouped_gemm_fc2.restype = st

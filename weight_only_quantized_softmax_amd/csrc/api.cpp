@@ -134,8 +134,27 @@ qmoe_status validate(const qmoe_params* p) {
     return fail(QMOE_ERR_INVALID, "block_size %d must be 0 or a power of two >= 16", p->block_size);
   if (p->block_size > kMaxBlock)
     return fail(QMOE_ERR_UNSUPPORTED, "block_size %d > %d", p->block_size, kMaxBlock);
-  if (p->activation < QMOE_ACT_SWIGLU || p->activation > QMOE_ACT_SILU)
+  if (p->activation < QMOE_ACT_SWIGLU || p->activation > QMOE_ACT_GELU)
     return fail(QMOE_ERR_INVALID, "activation %d unknown", p->activation);
+  if (p->activation == QMOE_ACT_GELU && p->gelu_mode != 0 && p->gelu_mode != 1)
+    return fail(QMOE_ERR_INVALID, "gelu_mode %d is not 0 (erf) or 1 (tanh)", p->gelu_mode);
+  if (!std::isfinite(p->expert_output_scale))
+    return fail(QMOE_ERR_INVALID, "expert_output_scale must be finite");
+  if (p->apply_router_weight_on_input && p->compute_mode == QMOE_COMPUTE_INT8)
+    return fail(QMOE_ERR_UNSUPPORTED,
+                "the int8 tier with the routing weight on the input (the codes would depend "
+                "on each slot's weight)");
+  if (p->use_sparse_mixer) {
+    if (p->k != 2 || p->num_experts < 2)
+      return fail(QMOE_ERR_INVALID, "the sparse mixer picks k = 2 experts (k %lld, E %lld)",
+                  (long long)p->k, (long long)p->num_experts);
+    if (p->normalize_routing_weights)
+      return fail(QMOE_ERR_INVALID, "the sparse mixer's weights are not renormalised");
+    if (p->n_group > 1 || p->e_score_correction_bias)
+      return fail(QMOE_ERR_INVALID, "the sparse mixer takes no grouping and no selection bias");
+    if (!std::isfinite(p->sparse_mixer_eps) || p->sparse_mixer_eps < 0.f)
+      return fail(QMOE_ERR_INVALID, "sparse_mixer_eps must be finite and >= 0");
+  }
   if (p->swiglu_fusion < 0 || p->swiglu_fusion > 2)
     return fail(QMOE_ERR_INVALID, "swiglu_fusion %d outside {0, 1, 2}", p->swiglu_fusion);
   if (!swiglu(p) && p->swiglu_fusion != 0)
@@ -211,7 +230,16 @@ qmoe::RouteOpts route_opts(const qmoe_params* p) {
   o.n_group = p->n_group > 1 ? p->n_group : 1;
   o.topk_group = p->n_group > 1 ? p->topk_group : 1;
   o.scale = p->routed_scaling_factor != 0.f ? p->routed_scaling_factor : 1.f;
+  o.mixer = p->use_sparse_mixer != 0;
+  o.mixer_eps = p->sparse_mixer_eps;
   return o;
+}
+
+qmoe::CombineOpts combine_opts(const qmoe_params* p) {
+  qmoe::CombineOpts c{};
+  c.weights = p->apply_router_weight_on_input ? 0 : 1;
+  c.scale = p->expert_output_scale != 0.f ? p->expert_output_scale : 1.f;
+  return c;
 }
 
 int64_t max_tiles_of(const qmoe_params* p) {
@@ -310,7 +338,8 @@ qmoe::GemmArgs gemm_args(const qmoe_params* p) {
   g.bs_shift = 0;
   while (g.bs > 0 && (1 << g.bs_shift) < g.bs) ++g.bs_shift;
   g.fusion = p->swiglu_fusion;
-  g.act = p->activation;
+  // activation code of the kernels: 1 identity, 2 relu, 3 silu, 4 gelu (erf), 5 gelu (tanh)
+  g.act = p->activation == QMOE_ACT_GELU ? (p->gelu_mode ? 5 : 4) : p->activation;
   g.alpha = p->swiglu_alpha;
   g.beta = p->swiglu_beta;
   g.limit = (p->swiglu_limit > 0.f) ? p->swiglu_limit : INFINITY;
@@ -338,11 +367,12 @@ hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, 
 }
 
 qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
-                    const int32_t* tiles, const int32_t* num_tiles, qmoe_stack fc1,
-                    qmoe_stack fc3, void* h, hipStream_t s) {
+                    const int32_t* tiles, const int32_t* num_tiles, const float* topk_w,
+                    qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = x;
   g.sorted_assign = sorted_assign;
+  g.row_w = p->apply_router_weight_on_input ? topk_w : nullptr;
   g.tile_list = tiles;
   g.num_tiles = num_tiles;
   g.w = static_cast<const uint8_t*>(fc1.weights);
@@ -487,8 +517,8 @@ qmoe_status qmoe_permute(const qmoe_params* p, const int32_t* topk_ids, int32_t*
 
 qmoe_status qmoe_grouped_gemm_fc1_swiglu(const qmoe_params* p, const void* x,
                                          const int32_t* sorted_assign, const int32_t* tile_list,
-                                         const int32_t* num_tiles, qmoe_stack fc1, qmoe_stack fc3,
-                                         void* h, void* stream) {
+                                         const int32_t* num_tiles, const float* topk_w,
+                                         qmoe_stack fc1, qmoe_stack fc3, void* h, void* stream) {
   QMOE_TRY(validate(p));
   if (p->num_tokens == 0) return ok();
   QMOE_TRY(need(x, "x"));
@@ -498,7 +528,8 @@ qmoe_status qmoe_grouped_gemm_fc1_swiglu(const qmoe_params* p, const void* x,
   QMOE_TRY(check_stack(fc1, "fc1"));
   if (has_fc3(p)) QMOE_TRY(check_stack(fc3, "fc3"));
   QMOE_TRY(need(h, "h"));
-  return run_fc1(p, x, sorted_assign, tile_list, num_tiles, fc1, fc3, h,
+  if (p->apply_router_weight_on_input) QMOE_TRY(need(topk_w, "topk_w"));
+  return run_fc1(p, x, sorted_assign, tile_list, num_tiles, topk_w, fc1, fc3, h,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -528,7 +559,7 @@ qmoe_status qmoe_combine(const qmoe_params* p, const float* y, const int32_t* as
       qmoe::launch_combine(y, assign_pos, topk_w, shared_output, output,
                            p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
                            static_cast<int>(p->hidden_size), static_cast<int>(p->k),
-                           static_cast<hipStream_t>(stream)),
+                           combine_opts(p), static_cast<hipStream_t>(stream)),
       "combine launch");
 }
 
@@ -607,7 +638,7 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                            "quantize x launch"));
     x = w.xq;
   }
-  QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, fc1, fc3, w.h, s));
+  QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s));
   if (int8)
     QMOE_TRY(device_status(qmoe::launch_quantize_blocks(w.h, w.h, abf, max_rows_of(p),
                                                         static_cast<int>(p->inter_size),
@@ -618,7 +649,8 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
   QMOE_TRY(device_status(
       qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output,
                            p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
-                           static_cast<int>(p->hidden_size), static_cast<int>(p->k), s),
+                           static_cast<int>(p->hidden_size), static_cast<int>(p->k),
+                           combine_opts(p), s),
       "combine launch"));
   return ok();
 }
@@ -659,7 +691,9 @@ qmoe_status qmoe_linear_woq(const qmoe_params* p, const void* x, qmoe_stack w, v
     return fail(QMOE_ERR_INVALID, "a linear layer has num_experts 1 and k 1 (got %lld, %lld)",
                 (long long)p->num_experts, (long long)p->k);
   if (swiglu(p))
-    return fail(QMOE_ERR_INVALID, "a linear layer's activation is identity, relu or silu");
+    return fail(QMOE_ERR_INVALID, "a linear layer's activation is identity, relu, silu or gelu");
+  if (p->apply_router_weight_on_input)
+    return fail(QMOE_ERR_INVALID, "a linear layer has no routing weight to apply");
   if (p->num_tokens == 0) return ok();
   QMOE_TRY(need(x, "x"));
   QMOE_TRY(check_stack(w, "weight"));

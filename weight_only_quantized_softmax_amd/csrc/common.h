@@ -98,9 +98,17 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
   return g * sig * (u + beta);
 }
 
+// The plain activations by code: 1 identity, 2 relu, 3 silu, 4 gelu z * Phi(z) (Phi the
+// standard normal CDF, through erf), 5 gelu's tanh approximation (graiphic "QMoE" page,
+// activation_type; CLIKA "MoE" page, gelu_mode).
 __device__ __forceinline__ float plain_act(float z, int act) {
   if (act == 2) return z > 0.f ? z : 0.f;                      // relu
   if (act == 3) return z * (1.0f / (1.0f + __expf(-z)));       // silu
+  if (act == 4) return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  if (act == 5) {
+    const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+    return 0.5f * z * (1.0f + tanhf(u));
+  }
   return z;                                                    // identity
 }
 

@@ -103,12 +103,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
   for (int m = 0; m < kF32MaxTile; ++m) {
     if (m >= M) continue;
-    const float za = wave_sum_f32(accA[m]) + biasA;
+    // fc1 with the routing weight on the input: the row's weight scales its sums
+    const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, row0 + m) : 1.f;
+    const float za = wave_sum_f32(accA[m]) * rs + biasA;
     float v;
     if (MODE == kModeFc2) {
       v = za;
     } else if (MODE == kModeSwiglu) {
-      const float zb = wave_sum_f32(accB[m]) + biasB;
+      const float zb = wave_sum_f32(accB[m]) * rs + biasB;
       v = swiglu(za, zb, g.alpha, g.beta, g.limit);
     } else {
       v = plain_act(za, g.act);

@@ -281,11 +281,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * kq + i;
     const int64_t r = row0 + m;
+    // fc1 with the routing weight on the input: the row's weight scales its sums
+    const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
     if (MODE == kModeSwiglu) {
       const int col = col_of(0);
       if (col >= g.ncols) continue;
       float h = 0.f;
-      if (m < valid) h = swiglu(tot[0][i] + bias[0], tot[1][i] + bias[1], g.alpha, g.beta, g.limit);
+      if (m < valid)
+        h = swiglu(tot[0][i] * rs + bias[0], tot[1][i] * rs + bias[1], g.alpha, g.beta, g.limit);
       if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
     } else {
 #pragma unroll
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
         if (MODE == kModeFc2) {
           if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = tot[st][i] + bias[st];
         } else {
-          const float h = m < valid ? plain_act(tot[st][i] + bias[st], g.act) : 0.f;
+          const float h = m < valid ? plain_act(tot[st][i] * rs + bias[st], g.act) : 0.f;
           if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(h);
         }
       }

@@ -332,6 +332,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_kernel(GemmArgs g) {
       const int m = wm * WTM * 16 + mt * 16 + 4 * kq + i;
       const int64_t r = row0 + m;
       const float rc = PERROW ? rowcorr[m] : 0.f;
+      // fc1 with the routing weight on the input: the row's weight scales its sums
+      const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
 #pragma unroll
       for (int cb = 0; cb < NBS; ++cb) {
         const int col = col0 + wn * NBS * 16 + cb * 16 + n;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_kernel(GemmArgs g) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           const int b = st * NBS + cb;
-          z[st] = (PERROW ? svr[b] * (acc[mt][b][0][i] + rc) : tot[mt][b][i]) + bias[b];
+          z[st] = (PERROW ? svr[b] * (acc[mt][b][0][i] + rc) : tot[mt][b][i]) * rs + bias[b];
         }
         if (MODE == kModeFc2) {
           if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];

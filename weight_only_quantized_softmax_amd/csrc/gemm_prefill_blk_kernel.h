@@ -424,6 +424,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 64 + mt * 16 + 4 * kq + i;
       const int64_t r = row0 + m;
+      // fc1 with the routing weight on the input: the row's weight scales its sums
+      const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
 #pragma unroll
       for (int cb = 0; cb < NBS; ++cb) {
         const int col = slice_col(wn, cb, n);
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_blk_kernel(GemmArgs 
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           const int b = st * NBS + cb;
-          z[st] = tot[mt][b][i] + bias[b];
+          z[st] = tot[mt][b][i] * rs + bias[b];
         }
         if (MODE == kModeFc2) {
           if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];

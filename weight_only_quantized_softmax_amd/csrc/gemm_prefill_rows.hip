@@ -353,6 +353,8 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
       const int m = wm * MT * 16 + mt * 16 + 4 * kq + i;
       const int64_t r = row0 + m;
       const float rc = rowsum[m];
+      // fc1 with the routing weight on the input: the row's weight scales its sums
+      const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
 #pragma unroll
       for (int cb = 0; cb < NBS; ++cb) {
         const int col = col0 + wn * NBS * 16 + cb * 16 + n;
@@ -361,7 +363,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           const int b = st * NBS + cb;
-          z[st] = svr[b] * (acc[mt][b][i] + rc) + bias[b];
+          z[st] = svr[b] * (acc[mt][b][i] + rc) * rs + bias[b];
         }
         if (MODE == kModeFc2) {
           if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];

@@ -58,6 +58,10 @@ struct GemmArgs {
   // MX FP4 weights: E2M1 codes with one E8M0 scale byte per 32 k (tiled layout, natural
   // nibble order); the kernels take them with ST = uint8_t
   int mx;
+  // fc1 with the routing weight on the input: the weight of each row's assignment
+  // (topk_w, indexed by sorted_assign) scales the row's fp32 sums before the bias; nullptr
+  // otherwise
+  const float* row_w;
 };
 
 // Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
@@ -71,6 +75,11 @@ __device__ __forceinline__ int2 gemm_tile(const GemmArgs& g, int tile) {
     return make_int2(0, static_cast<int>(left < g.M ? left : g.M));
   }
   return make_int2(g.tile_list[2 * tile], g.tile_list[2 * tile + 1]);
+}
+// The factor on the fp32 sums of padded row `row` of an fc1-side GEMM (a real row): its
+// assignment's routing weight when the weight goes to the expert's input, else 1.
+__device__ __forceinline__ float gemm_row_scale(const GemmArgs& g, int64_t row) {
+  return g.row_w ? g.row_w[g.sorted_assign[row]] : 1.f;
 }
 // Row of a that feeds padded row `row` of an fc1-side GEMM (fc2 reads row itself).
 __device__ __forceinline__ int64_t gemm_src_row(const GemmArgs& g, int64_t row) {
@@ -114,6 +123,8 @@ struct RouteOpts {
   int n_group;          // <= 1: no grouping
   int topk_group;
   float scale;          // multiplies the k weights
+  bool mixer;           // the sparse mixer (k = 2; no bias, no grouping)
+  float mixer_eps;
 };
 
 hipError_t launch_route(const void* logits, bool bf16, int T, int E, int k, int normalize,
@@ -171,8 +182,14 @@ hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf1
 hipError_t launch_quantize_blocks(const void* in, void* out, bool bf16, int64_t rows, int K,
                                   int bs, const int32_t* num_tiles, int tile_m, hipStream_t s);
 
+// Combine coefficients: the routing weight (weights = 1) or 1 (weights = 0: the weight went
+// to the expert's input), times scale (the expert output scale).
+struct CombineOpts {
+  int weights;
+  float scale;
+};
 hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
                           const void* shared, void* out, bool bf16, int T, int H, int k,
-                          hipStream_t s);
+                          const CombineOpts& c, hipStream_t s);
 
 }  // namespace qmoe

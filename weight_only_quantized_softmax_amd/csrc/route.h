@@ -84,6 +84,64 @@ __device__ __forceinline__ void load_token(const TA* logits, int t, int E, const
   }
 }
 
+// The sparse mixer routing of token t (graiphic "QMoE" page, use_sparse_mixer; CLIKA "MoE"
+// page, sparse_mixer_eps), read from its published definition (the SparseMixer top-2
+// router of Phi-3.5-MoE): two picks, the largest logit m1 and then the largest of the
+// others m2 (equal logits: the lower index, as in the top-k). Pick j keeps expert e unless
+// (mj - l_e) / max(|l_e|, mj) > 2 eps, decided in fp32 with a correctly rounded division
+// (0/0 keeps it); pick 2 never keeps pick 1. Pick j's weight is the softmax at the picked
+// expert over the experts it keeps, 1 / sum_kept exp(l_e - mj), times the scaling factor.
+// Lanes 0 and 1 of the group write the two slots.
+template <int G, int V>
+__device__ __forceinline__ void route_mixer(TokenLogits<V>& r, int t, int E, const RouteOpts& o,
+                                            int32_t* topk_ids, float* topk_w) {
+  const int lane = lane_id();
+  const int gl = lane & (G - 1);
+  const int gbase = lane - gl;
+  const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
+  const float thr = 2.0f * o.mixer_eps;
+  float my_w = 0.f;
+  int my_id = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t best = r.key[0];
+    int bslot = 0;
+#pragma unroll
+    for (int v = 1; v < V; ++v)
+      if (r.key[v] > best) { best = r.key[v]; bslot = v; }
+    const uint32_t gmax = group_max_u32<G>(best);
+    const uint64_t holders = (ballot(best == gmax) >> gbase) & gmask;
+    const int src = gbase + __builtin_ctzll(holders);
+    const int idx = static_cast<int>(group_read<G>(static_cast<uint32_t>(gl * V + bslot), src));
+    const float m = key_value(gmax);  // the pick's logit (-0 read as +0: the same decisions)
+    if (lane == src) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v == bslot) r.key[v] = 0u;  // leaves later picks and pick 2's softmax
+    }
+    // the experts this pick keeps: every expert for pick 1; for pick 2 every expert but
+    // pick 1 (whose key is now 0, as are the keys past E)
+    float part = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = gl * V + v;
+      const bool cand = e < E && (j == 0 || r.key[v] != 0u || e == idx);
+      const float l = r.val[v];
+      const bool drop = __fdiv_rn(m - l, fmaxf(fabsf(l), m)) > thr;
+      if (cand && !drop) part += expf(l - m);
+    }
+    const float w = 1.0f / group_sum_f32<G>(part);
+    if (gl == j) {
+      my_w = w;
+      my_id = idx;
+    }
+  }
+  if (gl < 2) {
+    topk_ids[static_cast<int64_t>(t) * 2 + gl] = my_id;
+    topk_w[static_cast<int64_t>(t) * 2 + gl] = o.scale != 1.0f ? my_w * o.scale : my_w;
+  }
+}
+
 // Routes token t from its loaded logits (all G lanes of the group call this with the same
 // t): lanes j < k of the group write its j-th expert id and weight to topk_ids[t*k + j] and
 // topk_w[t*k + j].
@@ -99,6 +157,10 @@ template <int G, int V>
 __device__ __forceinline__ void route_loaded(TokenLogits<V>& r, int t, int E, int k,
                                              int normalize, const RouteOpts& o,
                                              int32_t* topk_ids, float* topk_w) {
+  if (o.mixer) {
+    route_mixer<G, V>(r, t, E, o, topk_ids, topk_w);
+    return;
+  }
   const int lane = lane_id();
   const int gl = lane & (G - 1);
   const int gbase = lane - gl;
