@@ -390,7 +390,11 @@ hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool 
   // loads activations into LDS directly
   if (g.bs == 0 && (g.packed || g.K % (bits == 4 ? 128 : 64) == 0))
     return launch_gemm_bf16_prefill_rows(g, mode, bits, scale_bf16, max_tiles, s);
-  // block scales likewise, except 8-bit rows-layout blocks shorter than a 64-wide K step
+  // block scales of 16 to 128 in the tiled layout: weights scaled as they are decoded
+  if (prefill_sw_supports(g))
+    return launch_gemm_bf16_prefill_sw(g, mode, bits, scale_bf16, max_tiles, s);
+  // other block scales likewise, except 8-bit rows-layout blocks shorter than a 64-wide
+  // K step
   if (prefill_blk_supports(g, bits))
     return launch_gemm_bf16_prefill_blk(g, mode, bits, scale_bf16, max_tiles, s);
   if (bits == 4)

@@ -172,6 +172,14 @@ hipError_t launch_gemm_bf16_prefill_blk(const GemmArgs& g, int mode, int bits, b
 hipError_t launch_gemm_bf16_prefill_blk_tiled(const GemmArgs& g, int mode, int bits,
                                               bool scale_bf16, int64_t max_tiles, hipStream_t s);
 
+// bf16 activations, MFMA 128-row tiles, tiled layout, blocks of 16 to 128 (and MX FP4):
+// weights scaled as they are decoded, once per tile.
+bool prefill_sw_supports(const GemmArgs& g);
+hipError_t launch_gemm_bf16_prefill_sw(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                       int64_t max_tiles, hipStream_t s);
+hipError_t launch_gemm_bf16_prefill_sw8(const GemmArgs& g, int mode, bool scale_bf16,
+                                        int64_t max_tiles, hipStream_t s);
+
 // f32 activations, VALU kernel.
 hipError_t launch_gemm_f32(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                            int64_t max_tiles, hipStream_t s);
