@@ -2,14 +2,13 @@
 
 A step is one whole forward (route, permute, fc1+SwiGLU, fc2, combine) over one batch of
 synthetic tokens: one call of the library's qmoe_forward C entry point, which launches the
-kernels (routing and grouping as one kernel at small batches), captured once per weight copy
-launched directly on one stream. The same forwards replayed from HIP graphs (one per weight
-copy, captured once) are timed too, as ``hip_graph_ms_per_step`` (``--no-graph`` skips them).
-The default decode run adds a ``prefill`` object: the prefill-shaped layer at T=4096 measured
-the same way in the same run. The same stages are also
-run one C entry point at a time, the two GEMM kernels recording their own start and end
-on HIP events (qmoe_time_next_gemm), for the kernel times and the roofline of the fc1
-kernel (``staged_ms_per_step`` is that loop's step time). Inputs are resident in HBM
+kernels (routing and grouping as one kernel at small batches) directly on one stream. The
+same forwards are run again with their fc1 and fc2 kernels recording their own start and
+end on HIP events (qmoe_time_next_gemm), for the kernel times and the roofline of the fc1
+kernel; replayed from HIP graphs (one per weight copy, captured once), timed as
+``hip_graph_ms_per_step`` (``--no-graph`` skips them); and as the stages' separate C entry
+points (``staged_ms_per_step``). The default decode run adds a ``prefill`` object: the
+prefill-shaped layer at T=4096 measured the same way in the same run. Inputs are resident in HBM
 before the timed region. Several device copies of the expert stacks are rotated
 from step to step so that the 256 MB Infinity Cache cannot serve a step's weights from
 the previous step.
@@ -292,12 +291,7 @@ def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
         if status != 0:
             qm.check(status)
 
-    # HIP events that the fc1 and fc2 kernels record their own start and end on
-    # (qmoe_time_next_gemm: hipExtLaunchKernel events)
-    tev = TimingEvents(4 * steps)
-    evp = [tev.ev[4 * i:4 * i + 4] for i in range(steps)]
-
-    def step(i, timed):
+    def step(i):
         s1, s2, s3 = st_args[i % copies]
         run(lib.qmoe_route(*route))
         run(lib.qmoe_permute(*perm))
@@ -305,14 +299,10 @@ def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
         if cfg.int8:
             run(lib.qmoe_quantize_act(p, ptr(d.x), T, cfg.H, ptr(xq), sid))
             x = xq
-        if timed:
-            run(lib.qmoe_time_next_gemm(evp[i][0], evp[i][1]))
         run(lib.qmoe_grouped_gemm_fc1_swiglu(p, ptr(x), ptr(sa), ptr(tl), ptr(nt), ptr(w), s1,
                                              s3, ptr(h), sid))
         if cfg.int8:
             run(lib.qmoe_quantize_act(p, ptr(h), rows, cfg.I, ptr(h), sid))
-        if timed:
-            run(lib.qmoe_time_next_gemm(evp[i][2], evp[i][3]))
         run(lib.qmoe_grouped_gemm_fc2(p, ptr(h), ptr(tl), ptr(nt), s2, ptr(y), sid))
         run(lib.qmoe_combine(*comb))
 
@@ -320,17 +310,14 @@ def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
           f"({alg['weight_bytes'] / 1e6:.1f} MB touched); warmup {warmup}",
           file=sys.stderr, flush=True)
     for i in range(warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     staged_ms = (t1 - t0) * 1e3 / steps
-    fc1_ms = float(np.mean([tev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
-    fc2_ms = float(np.mean([tev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)]))
-    tev.close()
 
     # the timed step: the whole-forward entry point (one C call per step, the same kernels
     # with routing and grouping in one launch at small batches); with graph, each weight
@@ -352,6 +339,19 @@ def measure_moe(args, cfg, T, steps, warmup, cpu_leg, graph):
         return (time.perf_counter() - f0) * 1e3 / steps
 
     ms_per_step = timed(lambda i: fwd(i, sid))
+
+    # the kernels' own durations: the same forwards, the fc1 and fc2 launches each recording
+    # their start and end on HIP events (qmoe_time_next_gemm armed twice per forward:
+    # hipExtLaunchKernel events)
+    tev = TimingEvents(4 * steps)
+    for i in range(steps):
+        run(lib.qmoe_time_next_gemm(tev.ev[4 * i], tev.ev[4 * i + 1]))
+        run(lib.qmoe_time_next_gemm(tev.ev[4 * i + 2], tev.ev[4 * i + 3]))
+        fwd(i, sid)
+    torch.cuda.synchronize()
+    fc1_ms = float(np.mean([tev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
+    fc2_ms = float(np.mean([tev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)]))
+    tev.close()
     graph_ms = None
     if graph:
         cap = torch.cuda.Stream()

@@ -132,7 +132,12 @@ typedef struct {
      (their callers apply qmoe_quantize_act first). Needs block_size > 0
      (QMOE_ERR_INVALID) and bf16 activations (QMOE_ERR_UNSUPPORTED with fp32: the codes
      of h are decided from h, and a last-bit difference in an fp32 h, from summation
-     order, can move one code by a step, which is worth more than the fp32 path's bound). */
+     order, can move one code by a step, which is worth more than the fp32 path's bound).
+     Where the tiles are prefill-sized (128 rows) in the tiled layout with integer codes,
+     blocks of 64 or 128 and H and I multiples of 64, qmoe_forward multiplies the codes on
+     the int8 matrix cores (int32 block sums, each scaled once by 2^e times the weight
+     scale); elsewhere the rounded activations go through the bf16 kernels. Both give the
+     same products exactly; only the fp32 summation order differs. */
   int32_t compute_mode;
   /* The remaining options of the CLIKA "MoE" page's routing kwargs and the graiphic "QMoE"
      page's attributes:
@@ -357,7 +362,13 @@ qmoe_status qmoe_forward_noalloc(const qmoe_params* p, const void* input,
  *                                         after its rounding)
  *   y               float [qmoe_max_rows, H]       qmoe_grouped_gemm_fc2
  *   xq              act_dtype [T, H]      the int8 tier's rounded x (0 when compute_mode is
- *                                         QMOE_COMPUTE_FLOAT: no such piece)
+ *                                         QMOE_COMPUTE_FLOAT or the int8 dot runs: no such
+ *                                         piece)
+ *   xcodes, xfactors, hcodes, hfactors   with the int8 tier on the int8 matrix cores (bf16
+ *                   activations, tiled weights with integer codes, 128-row tiles, blocks of
+ *                   64 or 128, H and I multiples of 64; 0 otherwise): the rounded x and h as
+ *                   int8 codes [rows, K] (within every 64 consecutive k the chunks of 8 in the
+ *                   order 0, 4, 1, 5, 2, 6, 3, 7) and float factors 2^e [rows, ceil(K/bs)]
  *   total           == qmoe_workspace_size(p)
  *   fused_routing   1 when this batch is routed and grouped by one kernel (small batches:
  *                   the routed ids stay inside that kernel), else 0.
@@ -367,6 +378,7 @@ typedef struct {
   size_t topk_ids, topk_w, counts, padded_offsets, sorted_assign, assign_pos, tile_list,
       num_tiles, permute_scratch, h, y, xq, total;
   int32_t fused_routing;
+  size_t xcodes, xfactors, hcodes, hfactors;
 } qmoe_workspace_layout;
 
 qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);
@@ -413,11 +425,13 @@ qmoe_status qmoe_linear_woq(const qmoe_params* p, const void* x, qmoe_stack w, v
 /*
  * Measurement hook, not a step of the method. The next grouped-GEMM kernel that the calling
  * thread launches -- the one launch of qmoe_grouped_gemm_fc1_swiglu or
- * qmoe_grouped_gemm_fc2, or the first of qmoe_forward's two -- records its own start and
+ * qmoe_grouped_gemm_fc2, or qmoe_forward's fc1 and then its fc2 -- records its own start and
  * end on these HIP events (hipEvent_t, created by the caller, timing enabled; either may
  * be NULL), as hipExtLaunchKernel does, so that hipEventElapsedTime(start, stop) is that
  * kernel's duration alone, without the dispatch gap a separately recorded event holds.
- * The hook is then cleared; (NULL, NULL) clears a pending hook. Thread-local; never fails.
+ * Up to four pairs may be armed; each GEMM launch takes the oldest and removes it (arm two
+ * before qmoe_forward to time both of its GEMMs). (NULL, NULL) clears every pending pair.
+ * Thread-local; never fails (pairs beyond four are ignored).
  */
 qmoe_status qmoe_time_next_gemm(void* start_event, void* stop_event);
 

@@ -204,6 +204,7 @@ def test_every_gpu_parity_case_passes_validation(lib):
     from tests import test_gpu_parity as t
     from tests.gpu_helpers import params_for
 
+    bad = []
     cases = [(cfg, T, 0, "rows", "route " + n) for n, (cfg, T) in t.ROUTE_CASES.items()]
     cases += [t.stage_cfg(n, m) + (m, lay, "stage " + n) for n, m, lay in t.STAGE_CASES]
     for c in (configs.C1, configs.C2, configs.C3, configs.C4):
@@ -224,13 +225,18 @@ def test_every_gpu_parity_case_passes_validation(lib):
     for E, k, T, _ in t.FUSED_ROUTING_CASES + t.FUSED_ROUTING_EDGES:
         cases.append((configs.tiny(E=E, k=k, act_dtype="bf16", scale_dtype="bf16", H=64, I=64,
                                    bits=4, block_size=32, fusion=1), T, 0, "rows", "fused"))
+    from tests import test_gpu_int8 as i8
+    for n, (cfg, T) in i8.I8_DOT_CASES.items():
+        cases.append((cfg, T, 0, "tiles", "int8 dot " + n))
+        p8 = params_for(cfg, T, layout="tiles")
+        if lib.qmoe_tile_m(p8) != 128:
+            bad.append(("int8 dot case is not prefill-sized", n))
     from tests import test_gpu_variants as v
     cases += [(cfg, 300 if m == 128 else 40, m, lay, "variant stage " + n)
               for n, cfg in v.STAGE_VARIANTS.items() for m in (16, 32, 128)
               for lay in ("rows", "tiles")]
     cases += [(v._mixer(E, eps, act), 257, 0, "rows", "mixer")
               for E, eps, act in ((8, 0.01, "bf16"), (64, 0.2, "f32"), (300, 0.01, "bf16"))]
-    bad = []
     for cfg, T, m, lay, what in cases:
         if lib.qmoe_validate(params_for(cfg, T, tile_m=m, layout=lay)) != 0:
             bad.append((what, cfg.name, T, m, lay, lib.qmoe_last_error()))

@@ -110,3 +110,29 @@ def test_forward_int8_unfused_gate_up():
                        fusion=0, bits=4, block_size=64, fc1_bias=True, fc2_bias=True,
                        limit=7.0, int8=True)
     check_forward(cfg, 300, layout="tiles")
+
+
+# The int8 dot on the int8 matrix cores (prefill-sized tiles, tiled layout, integer codes,
+# blocks of 64 and 128, H and I multiples of 64): 4- and 8-bit codes, both block lengths, K
+# an odd multiple of 64 for 4-bit codes (the second half of the last 128-k step is past K),
+# a ragged last block of 64 (c4's 2880 with blocks of 128), fused and separate gate/up.
+I8_DOT_CASES = {
+    "c5-b4-bs64-T4096": (configs.c5_point(4, 64).with_(int8=True), 4096),
+    "c5-b4-bs128-T4096": (configs.c5_point(4, 128).with_(int8=True), 4096),
+    "c5-b8-bs64-T4096": (configs.c5_point(8, 64).with_(int8=True), 4096),
+    "c5-b8-bs128-T4096": (configs.c5_point(8, 128).with_(int8=True), 4096),
+    "c2-b4-bs64-K2880-T1024": (configs.C2_INT8.with_(block_size=64), 1024),
+    "c4-b8-bs128-ragged-T2048": (configs.C4_INT8, 2048),
+    "separate-gate-up-b4-bs64": (configs.tiny(E=4, k=2, act_dtype="bf16", scale_dtype="bf16",
+                                              H=2048, I=1536, fusion=0, bits=4, block_size=64,
+                                              fc1_bias=True, fc2_bias=True, int8=True), 4096),
+}
+
+
+@pytest.mark.parametrize("name", sorted(I8_DOT_CASES))
+def test_forward_int8_dot(name):
+    cfg, T = I8_DOT_CASES[name]
+    p = params_for(cfg, T, layout="tiles")
+    assert qm.qmoe_tile_m(p) == 128
+    assert qm.qmoe_workspace_layout_of(p).xcodes != 0  # the int8 matrix-core path is taken
+    check_forward(cfg, T, sample=24, layout="tiles")

@@ -42,7 +42,8 @@ class QmoeWorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_ids", "topk_w", "counts", "padded_offsets", "sorted_assign", "assign_pos",
         "tile_list", "num_tiles", "permute_scratch", "h", "y", "xq", "total")] + [
-        ("fused_routing", ctypes.c_int32)]
+        ("fused_routing", ctypes.c_int32)] + [(n, ctypes.c_size_t) for n in (
+        "xcodes", "xfactors", "hcodes", "hfactors")]
 
 
 class QmoeStack(ctypes.Structure):

@@ -15,7 +15,10 @@
 namespace {
 
 thread_local std::string g_error;
-thread_local qmoe::GemmTiming g_timing;
+// armed timing pairs, oldest first
+constexpr int kTimingSlots = 4;
+thread_local qmoe::GemmTiming g_timing[kTimingSlots];
+thread_local int g_timing_n = 0;
 
 qmoe_status fail(qmoe_status st, const char* fmt, ...) {
   char buf[512];
@@ -45,11 +48,19 @@ qmoe_status fail_with(qmoe_status st, const char* msg, const char* detail) {
   return (detail && detail[0]) ? fail(st, "%s: %s", msg, detail) : fail(st, "%s", msg);
 }
 
-void set_gemm_timing(hipEvent_t start, hipEvent_t stop) { g_timing = GemmTiming{start, stop}; }
+void set_gemm_timing(hipEvent_t start, hipEvent_t stop) {
+  if (start == nullptr && stop == nullptr) {
+    g_timing_n = 0;
+    return;
+  }
+  if (g_timing_n < kTimingSlots) g_timing[g_timing_n++] = GemmTiming{start, stop};
+}
 
 GemmTiming take_gemm_timing() {
-  const GemmTiming t = g_timing;
-  g_timing = GemmTiming{};
+  if (g_timing_n == 0) return GemmTiming{};
+  const GemmTiming t = g_timing[0];
+  for (int i = 1; i < g_timing_n; ++i) g_timing[i - 1] = g_timing[i];
+  --g_timing_n;
   return t;
 }
 
@@ -252,6 +263,17 @@ int64_t max_rows_of(const qmoe_params* p) { return max_tiles_of(p) * tile_m_of(p
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The int8 tier's dot on the int8 matrix cores: prefill-sized tiles of the tiled layout with
+// integer codes, blocks of 64 and 128 (shorter blocks ran faster on the bf16 kernels), and
+// both contraction lengths multiples of 64 (the codes' 64-groups); elsewhere the tier's
+// rounded activations take the bf16 kernels.
+bool use_i8_dot(const qmoe_params* p) {
+  return p->compute_mode == QMOE_COMPUTE_INT8 && p->act_dtype == QMOE_BF16 &&
+         p->weight_layout == QMOE_LAYOUT_TILES && p->scale_dtype != QMOE_E8M0 &&
+         tile_m_of(p) == 128 && (p->block_size == 64 || p->block_size == 128) &&
+         p->hidden_size % 64 == 0 && p->inter_size % 64 == 0;
+}
+
 struct Workspace {
   int32_t* topk_ids;
   float* topk_w;
@@ -265,6 +287,11 @@ struct Workspace {
   void* h;
   float* y;
   void* xq;  // the int8-tier copy of x (compute_mode QMOE_COMPUTE_INT8)
+  // the int8 dot (use_i8_dot): codes and block factors of x and of h
+  int8_t* xc;
+  float* xf;
+  int8_t* hc;
+  float* hf;
   size_t bytes;
 };
 
@@ -291,7 +318,16 @@ Workspace carve(const qmoe_params* p, char* base) {
   w.perm_scratch = take(qmoe::permute_scratch_bytes(A, static_cast<int>(p->num_experts)));
   w.h = take(rows * p->inter_size * act);
   w.y = reinterpret_cast<float*>(take(rows * p->hidden_size * 4));
-  if (p->compute_mode == QMOE_COMPUTE_INT8) w.xq = take(p->num_tokens * p->hidden_size * act);
+  if (use_i8_dot(p)) {
+    const int64_t nbh = (p->hidden_size + p->block_size - 1) / p->block_size;
+    const int64_t nbi = (p->inter_size + p->block_size - 1) / p->block_size;
+    w.xc = reinterpret_cast<int8_t*>(take(p->num_tokens * p->hidden_size));
+    w.xf = reinterpret_cast<float*>(take(p->num_tokens * nbh * 4));
+    w.hc = reinterpret_cast<int8_t*>(take(rows * p->inter_size));
+    w.hf = reinterpret_cast<float*>(take(rows * nbi * 4));
+  } else if (p->compute_mode == QMOE_COMPUTE_INT8) {
+    w.xq = take(p->num_tokens * p->hidden_size * act);
+  }
   w.bytes = off;
   return w;
 }
@@ -361,6 +397,7 @@ void set_tiles(const qmoe_params* p, qmoe::GemmArgs& g, int rows) {
 hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, hipStream_t s) {
   const bool sbf = p->scale_dtype == QMOE_BF16;
   const int bits = p->expert_weight_bits;
+  if (g.afac) return qmoe::launch_gemm_i8_prefill(g, mode, bits, sbf, max_tiles_of(p), s);
   if (p->act_dtype != QMOE_BF16) return qmoe::launch_gemm_f32(g, mode, bits, sbf, max_tiles_of(p), s);
   if (tile_m_of(p) == 128) return qmoe::launch_gemm_bf16_prefill(g, mode, bits, sbf, max_tiles_of(p), s);
   return qmoe::launch_gemm_bf16(g, mode, bits, sbf, max_tiles_of(p), s);
@@ -368,9 +405,11 @@ hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, 
 
 qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
                     const int32_t* tiles, const int32_t* num_tiles, const float* topk_w,
-                    qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s) {
+                    qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s,
+                    const float* xfac = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = x;
+  g.afac = xfac;
   g.sorted_assign = sorted_assign;
   g.row_w = p->apply_router_weight_on_input ? topk_w : nullptr;
   g.tile_list = tiles;
@@ -414,9 +453,11 @@ qmoe_status run_linear(const qmoe_params* p, const void* x, qmoe_stack w, void* 
 }
 
 qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
-                    const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s) {
+                    const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s,
+                    const float* hfac = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = h;
+  g.afac = hfac;
   g.tile_list = tiles;
   g.num_tiles = num_tiles;
   g.w = static_cast<const uint8_t*>(fc2.weights);
@@ -581,7 +622,12 @@ qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout
   out->permute_scratch = off(w.perm_scratch);
   out->h = off(w.h);
   out->y = off(w.y);
-  out->xq = p->compute_mode == QMOE_COMPUTE_INT8 ? off(w.xq) : 0;
+  out->xq = (p->compute_mode == QMOE_COMPUTE_INT8 && !use_i8_dot(p)) ? off(w.xq) : 0;
+  const bool i8 = use_i8_dot(p);
+  out->xcodes = i8 ? off(w.xc) : 0;
+  out->xfactors = i8 ? off(w.xf) : 0;
+  out->hcodes = i8 ? off(w.hc) : 0;
+  out->hfactors = i8 ? off(w.hf) : 0;
   out->total = w.bytes;
   out->fused_routing = qmoe::route_permute_fits(p->num_tokens, p->num_tokens * p->k,
                                                 p->num_experts, p->k) ? 1 : 0;
@@ -631,6 +677,26 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
   const bool int8 = p->compute_mode == QMOE_COMPUTE_INT8;
   const bool abf = p->act_dtype == QMOE_BF16;
   const void* x = input;
+  if (use_i8_dot(p)) {
+    // the int8 dot: x and h as int8 codes with their block factors
+    const int H = static_cast<int>(p->hidden_size), I = static_cast<int>(p->inter_size);
+    QMOE_TRY(device_status(qmoe::launch_quantize_codes(input, w.xc, w.xf, p->num_tokens, H,
+                                                       p->block_size, nullptr, 0, s),
+                           "quantize x launch"));
+    QMOE_TRY(run_fc1(p, w.xc, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s,
+                     w.xf));
+    QMOE_TRY(device_status(qmoe::launch_quantize_codes(w.h, w.hc, w.hf, max_rows_of(p), I,
+                                                       p->block_size, w.num_tiles, 128, s),
+                           "quantize h launch"));
+    QMOE_TRY(run_fc2(p, w.hc, w.tiles, w.num_tiles, fc2, w.y, s, w.hf));
+    QMOE_TRY(device_status(
+        qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output,
+                             p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),
+                             static_cast<int>(p->hidden_size), static_cast<int>(p->k),
+                             combine_opts(p), s),
+        "combine launch"));
+    return ok();
+  }
   if (int8) {
     QMOE_TRY(device_status(qmoe::launch_quantize_blocks(input, w.xq, abf, p->num_tokens,
                                                         static_cast<int>(p->hidden_size),

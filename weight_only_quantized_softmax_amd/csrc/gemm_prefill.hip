@@ -5,9 +5,11 @@
 // block is decoded inside the GEMM dot, never as a dense copy. graiphic "QMoE" page:
 // stack shapes [E, N, K/pack], scales per row or per K-block, activation attributes.
 //
-// Workgroup: one 128-row tile of one expert, four waves. Per-row scales: the waves form a
-// 2 x 2 grid of 64 rows x 96 weight columns each; block scales: 4 x 1 waves of 32 rows x
-// 96 weight columns (the per-block epilogue needs a second accumulator set). K advances one
+// This kernel serves the rows layout where the LDS-direct kernels do not (8-bit blocks
+// shorter than 64, or K not a whole number of K steps). Workgroup: one 128-row tile of one
+// expert, four waves. Per-row scales: a 2 x 2 grid of waves of 64 rows x 4 weight-row
+// slices (64 weight rows) each; block scales: 4 x 1 waves of 32 rows x 2 to 6 slices
+// (prefill_nb: short blocks need more accumulators, so fewer slices). K advances one
 // super-step at a time (128 k for 4-bit, 64 k for 8-bit):
 //   - the tile's activations for the next super-step are loaded into registers while the
 //     current one computes, then written to LDS in the nibble order of the decode, between

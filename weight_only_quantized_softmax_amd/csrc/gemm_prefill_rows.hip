@@ -2,13 +2,15 @@
 // prefill shape whose expert groups fill large tiles and whose cost is the bf16 MFMA rate.
 //
 // ClikaRT "QMoEWoQ" page, class description: the expert weights stay quantized and are
-// decoded inside the GEMM dot. graiphic "QMoE" page: stacks [E, N, K/pack], per-row
-// scales when block_size is 0 ("the whole column shares one scaling factor").
+// decoded inside the GEMM dot. graiphic "QMoE" page: stacks [E, N, K/pack]; without a
+// block_size every output row (a column of the transposed weight) has one scale.
 //
-// Workgroup: one 128-row tile of one expert by 256 weight rows (fused gate/up: 128 gate +
-// 128 up rows = 128 output columns; otherwise 256 output columns); four waves in a 2 x 2
-// grid of 64 rows x 128 weight rows each, 128 fp32 accumulators per lane, one wave per
-// SIMD (the register file holds the accumulators, two weight buffers and two operand sets).
+// Workgroup: one 128-row tile of one expert, four waves, two waves per SIMD (256 registers
+// a wave), the shape set by RowsShape:
+//   - fc1 with SwiGLU: 1 x 4 waves, each 128 rows x 4 weight-row slices of 16 (2 gate + 2
+//     up), so the workgroup covers 256 weight rows = 128 output columns and each decoded
+//     weight feeds 8 MFMAs; this shape spills one 16-byte fragment per K step;
+//   - the other modes: 2 x 2 waves, each 64 rows x 6 slices (192 weight rows a workgroup).
 //   - Activations reach LDS without passing through registers: buffer loads with the LDS
 //     as destination, 16 bytes per lane, 16 lanes per 256-byte row segment, two stages
 //     (this K step and the next). The 16-byte granule q of row r sits at slot

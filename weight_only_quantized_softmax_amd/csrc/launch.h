@@ -62,6 +62,8 @@ struct GemmArgs {
   // (topk_w, indexed by sorted_assign) scales the row's fp32 sums before the bias; nullptr
   // otherwise
   const float* row_w;
+  // the int8 dot: per-block factors 2^e of the rows of a (a then holds int8 codes)
+  const float* afac;
 };
 
 // Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
@@ -86,9 +88,10 @@ __device__ __forceinline__ int64_t gemm_src_row(const GemmArgs& g, int64_t row) 
   return g.linear ? row : g.sorted_assign[row] / g.topk;
 }
 
-// Measurement hook: HIP events that the calling thread's next grouped-GEMM launch records
-// its own start and end on (hipExtLaunchKernel). take_gemm_timing returns them and clears
-// the hook.
+// Measurement hook: HIP events that the calling thread's next grouped-GEMM launches record
+// their own start and end on (hipExtLaunchKernel), one pair per launch in the order the
+// pairs were armed. take_gemm_timing returns the oldest pair and removes it (a pair of
+// nullptrs when none is armed).
 struct GemmTiming {
   hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -196,6 +199,18 @@ struct CombineOpts {
   int weights;
   float scale;
 };
+// The same rounding of bf16 rows as int8 codes [rows, K] (the chunks of 8 of every 64-group
+// in the order 0, 4, 1, 5, 2, 6, 3, 7) and one factor 2^e per block [rows, ceil(K/bs)] (fp32),
+// for the int8 dot. Needs K % 64 == 0, bs in {64, 128}, 16-byte aligned rows.
+hipError_t launch_quantize_codes(const void* in, int8_t* codes, float* fac, int64_t rows, int K,
+                                 int bs, const int32_t* num_tiles, int tile_m, hipStream_t s);
+
+// The int8 dot at 128-row tiles (tiled layout, 4- or 8-bit codes, blocks of 64 and 128):
+// g.a holds the codes of the rows and g.afac their block factors.
+bool prefill_i8_supports(const GemmArgs& g, int bits);
+hipError_t launch_gemm_i8_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
+                                  int64_t max_tiles, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
                           const void* shared, void* out, bool bf16, int T, int H, int k,
                           const CombineOpts& c, hipStream_t s);

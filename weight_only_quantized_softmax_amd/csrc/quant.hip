@@ -105,6 +105,51 @@ __global__ __launch_bounds__(256) void quantize_blocks_vec_kernel(
   *reinterpret_cast<uint4*>(out + r * K + int64_t(c) * V) = res;
 }
 
+// The same rounding for bf16 rows, written as the int8 codes and a per-block factor 2^e
+// for the int8 dot (the prefill kernel on v_mfma_i32_16x16x64_i8). Each lane holds 8
+// consecutive elements (a chunk); the L = bs / 8 lanes of a block are adjacent. Codes go to
+// codes[r][K] with the chunks of every 64 consecutive k stored in the order
+// 0, 4, 1, 5, 2, 6, 3, 7, so that 16-byte granule q of a 64-group holds the k
+// {8q .. 8q+7} and {32+8q .. 32+8q+7}: the k a lane of the matrix instruction takes.
+// fac[r][b] = 2^e of block b. Needs K % 64 == 0 and bs in {64, 128}.
+template <int L>
+__global__ __launch_bounds__(256) void quantize_codes_kernel(
+    const uint16_t* in, int8_t* codes, float* fac, int64_t rows, int K, int C, int Cp, int nb,
+    const int32_t* __restrict__ num_tiles, int tile_m) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t used = num_tiles ? min<int64_t>(rows, int64_t(*num_tiles) * tile_m) : rows;
+  const int64_t r = idx / Cp;
+  const int c = static_cast<int>(idx - r * Cp);
+  const bool live = r < used && c < C;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4*>(in + r * K + int64_t(c) * 8);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if (!live) return;
+  const int e = block_exponent(a);
+  uint32_t q[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int code = static_cast<int>(rintf(ldexpf(v[i], -e)));
+    q[i / 4] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (i % 4));
+  }
+  // chunk c of its 64-group goes to slot 2 * (c % 4) + c / 4
+  const int g = c / 8, cc = c % 8;
+  const int64_t pos = r * K + int64_t(g) * 64 + 16 * (cc % 4) + 8 * (cc / 4);
+  *reinterpret_cast<uint2*>(codes + pos) = make_uint2(q[0], q[1]);
+  if (c % L == 0) fac[r * nb + c / L] = ldexpf(1.0f, e);
+}
+
 template <typename TA>
 hipError_t launch_vec(const TA* in, TA* out, int64_t rows, int K, int bs,
                       const int32_t* num_tiles, int tile_m, hipStream_t s, bool* done) {
@@ -134,6 +179,28 @@ hipError_t launch_vec(const TA* in, TA* out, int64_t rows, int K, int bs,
 }
 
 }  // namespace
+
+hipError_t launch_quantize_codes(const void* in, int8_t* codes, float* fac, int64_t rows, int K,
+                                 int bs, const int32_t* num_tiles, int tile_m, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int L = bs / 8;
+  const int nb = (K + bs - 1) / bs;
+  const int C = K / 8, Cp = nb * L;
+  const int64_t n = rows * Cp;
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  const uint16_t* x = static_cast<const uint16_t*>(in);
+  switch (L) {
+    case 8:
+      quantize_codes_kernel<8><<<blocks, 256, 0, s>>>(x, codes, fac, rows, K, C, Cp, nb, num_tiles, tile_m);
+      break;
+    case 16:
+      quantize_codes_kernel<16><<<blocks, 256, 0, s>>>(x, codes, fac, rows, K, C, Cp, nb, num_tiles, tile_m);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_blocks(const void* in, void* out, bool bf16, int64_t rows, int K,
                                   int bs, const int32_t* num_tiles, int tile_m, hipStream_t s) {
