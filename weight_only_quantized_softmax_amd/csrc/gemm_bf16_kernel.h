@@ -171,7 +171,7 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
         const int ss = ci * SPC + v * SK + ks;  // super-step (tile) index along K
         const uint32_t off = PK ? static_cast<uint32_t>(ss) * 1024u
                                 : static_cast<uint32_t>(ss * SSK) * BITS / 8;
-        w[st][v] = buf_load16(wres[st], woff[st] + off);
+        w[st][v] = buf_load16_stream(wres[st], woff[st] + off);
       }
   };
 

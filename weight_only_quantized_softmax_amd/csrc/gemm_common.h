@@ -22,6 +22,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// A weight stream read once per launch: the nontemporal policy (nt) lets the lines pass
+// through the caches without displacing what is reused (activations, scales). A plain read
+// of a few hundred MB runs about 8% faster on gfx950 with it.
+__device__ __forceinline__ u32x4 buf_load16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 // with a wave-uniform scalar offset added to the lane offset (the range check covers the
 // lane offset)
 __device__ __forceinline__ u32x4 buf_load16s(rsrc_t r, uint32_t off, uint32_t soff) {

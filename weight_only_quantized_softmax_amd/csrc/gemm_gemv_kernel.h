@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_gemv_kernel(GemmArgs g) {
   auto load = [&](int ss, Slot& sl) {
     if (ss < s1) {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) sl.w[st] = buf_load16(wres[st], 16u * lane + ss * 1024u);
+      for (int st = 0; st < NS; ++st) sl.w[st] = buf_load16_stream(wres[st], 16u * lane + ss * 1024u);
 #pragma unroll
       for (int j = 0; j < MPS; ++j)
         sl.x[j] = buf_load16s(xres, xoff, static_cast<uint32_t>(2 * (ss * SSK + 32 * j)));
