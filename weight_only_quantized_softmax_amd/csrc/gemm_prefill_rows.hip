@@ -7,10 +7,11 @@
 //
 // Workgroup: one 128-row tile of one expert, four waves, two waves per SIMD (256 registers
 // a wave), the shape set by RowsShape:
-//   - fc1 with SwiGLU: 1 x 4 waves, each 128 rows x 4 weight-row slices of 16 (2 gate + 2
-//     up), so the workgroup covers 256 weight rows = 128 output columns and each decoded
-//     weight feeds 8 MFMAs; this shape spills one 16-byte fragment per K step;
-//   - the other modes: 2 x 2 waves, each 64 rows x 6 slices (192 weight rows a workgroup).
+//   - fc1: 1 x 4 waves, each 128 rows x 4 weight-row slices of 16 (with SwiGLU 2 gate + 2
+//     up, so the workgroup covers 256 weight rows = 128 output columns), each decoded
+//     weight feeding 8 MFMAs; each activation fragment is read again for the next k-slice
+//     in place, right after its MFMAs, which keeps this shape within its registers;
+//   - fc2: 2 x 2 waves, each 64 rows x 6 slices (192 weight rows a workgroup).
 //   - Activations reach LDS without passing through registers: buffer loads with the LDS
 //     as destination, 16 bytes per lane, 16 lanes per 256-byte row segment, two stages
 //     (this K step and the next). The 16-byte granule q of row r sits at slot
@@ -53,14 +54,15 @@ __device__ __forceinline__ float dot2_sum(uint32_t v, float acc) {
 
 // Wave grid: WM waves along the tile's rows times 4 / WM along its columns; each wave holds
 // NB 16-row weight slices against its 128 / WM rows. More rows per wave share each decoded
-// weight among more MFMAs (the decode is the kernel's main VALU cost): fc1 with SwiGLU
-// takes 1 x 4 waves of 128 rows x 4 slices; the single-stream modes 2 x 2 waves of 64 rows
-// x 6 slices, where the registers also hold the activation load offsets.
+// weight among more MFMAs (the decode is the kernel's main VALU cost): fc1 (SwiGLU or a
+// plain activation) takes 1 x 4 waves of 128 rows x 4 slices; fc2 2 x 2 waves of 64 rows
+// x 6 slices, where the registers also hold the activation load offsets (measured on c3
+// T=4096: fc2 1% faster so, the plain-activation linear layer 6% slower).
 template <int BITS, int MODE>
 struct RowsShape {
   static constexpr bool kTwo = (MODE == kModeSwiglu);
-  static constexpr int WM = kTwo ? 1 : 2;
-  static constexpr int NB = kTwo ? 4 : 6;
+  static constexpr int WM = MODE == kModeFc2 ? 2 : 1;
+  static constexpr int NB = MODE == kModeFc2 ? 6 : 4;
   static constexpr bool XREG = WM == 2;                 // activation offsets in registers
   // explicit instruction order inside a k-slice (each MFMA followed by two VALU
   // instructions, operand reads first): measured neutral to negative, left off
@@ -243,7 +245,43 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
       return decode8(w2);
     }
   };
+  // Eight row tiles a wave (SwiGLU): each activation fragment is read again in place, for
+  // the next k-slice, right after its MFMAs have been issued, and the slice's four weights
+  // are decoded before its MFMAs. The fragments of the next k-slice then need no registers
+  // of their own, which keeps the wave within its 256 registers without spilling.
+  auto compute_inplace = [&](const uint16_t* stage, const u32x4 (&w)[kRNB]) {
+    u32x4 xa[MT];
+    aread(stage, 0, xa);
+#pragma unroll
+    for (int j = 0; j < MPS; ++j) {
+      const uint32_t an = abase ^ static_cast<uint32_t>((PK ? 64 : 16) * (j + 1));
+      bf16x8 bw[kRNB];
+#pragma unroll
+      for (int b = 0; b < kRNB; ++b) bw[b] = decode(w[b], j);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        u32x4 xv = xa[mt];
+        if (BITS == 4 && !PK) xv = order_for_nibbles(xv);
+        if (mt == 2 * wn || mt == 2 * wn + 1) {
+          // row sums of slices 2 wn, 2 wn + 1
+          const int h = mt - 2 * wn;
+          rs[h] = dot2_sum(xv[3], dot2_sum(xv[2], dot2_sum(xv[1], dot2_sum(xv[0], rs[h]))));
+        }
+#pragma unroll
+        for (int b = 0; b < kRNB; ++b)
+          acc[mt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                               bw[b], acc[mt][b], 0, 0, 0);
+        if (j + 1 < MPS)
+          xa[mt] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(stage) + an +
+                                                   mt * 16 * GPR * 16);
+      }
+    }
+  };
   auto compute = [&](const uint16_t* stage, const u32x4 (&w)[kRNB]) {
+    if constexpr (MT == 8) {
+      compute_inplace(stage, w);
+      return;
+    }
     u32x4 xa[MT];
     [[maybe_unused]] u32x4 xn[MT];
     aread(stage, 0, xa);
