@@ -96,7 +96,9 @@ def kernel_sources_sha(files):
 # dominant kernel of each path: the fc1 launch, by the file that holds it
 KERNEL_FILES = {"decode": ("gemm_bf16.hip", "gemm_bf16_tiled.hip", "gemm_bf16_kernel.h", "gemm_gemv_kernel.h",
                            "gemm_common.h", "common.h", "launch.h"),
-                "prefill": ("gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_prefill_blk_tiled.hip", "gemm_prefill_blk_kernel.h", "gemm_common.h", "common.h", "launch.h"),
+                "prefill": ("gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_prefill_blk_tiled.hip",
+                            "gemm_prefill_blk_kernel.h", "gemm_prefill_sw.hip", "gemm_prefill_sw8.hip", "gemm_prefill_sw_kernel.h",
+                            "gemm_prefill_i8.hip", "gemm_prefill_i8_kernel.h", "gemm_common.h", "common.h", "launch.h"),
                 "f32": ("gemm_f32.hip", "common.h", "launch.h")}
 
 
