@@ -372,6 +372,10 @@ qmoe_status qmoe_forward_noalloc(const qmoe_params* p, const void* input,
  *   total           == qmoe_workspace_size(p)
  *   fused_routing   1 when this batch is routed and grouped by one kernel (small batches:
  *                   the routed ids stay inside that kernel), else 0.
+ *   xsum            float [T]: the sum of each row of x, in fp32, with bf16 activations,
+ *                   tiled weights, 128-row tiles, one scale per output row and
+ *                   compute_mode QMOE_COMPUTE_FLOAT (fc1 takes the zero point's correction
+ *                   from it); 0 otherwise.
  * Errors: invalid parameters as qmoe_validate; out NULL -> QMOE_ERR_UNBOUND.
  */
 typedef struct {
@@ -379,6 +383,7 @@ typedef struct {
       num_tiles, permute_scratch, h, y, xq, total;
   int32_t fused_routing;
   size_t xcodes, xfactors, hcodes, hfactors;
+  size_t xsum;
 } qmoe_workspace_layout;
 
 qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);

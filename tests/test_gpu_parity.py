@@ -540,6 +540,30 @@ def test_forward_c4_many_experts_sampled():
     check_forward(configs.C4, 512, sample=64)
 
 
+# The forward forms each token's row sum once for the 128-row per-row-scale fc1 kernel on
+# tiled weights (the zero point's correction). These layers (sized so that the library
+# picks 128-row tiles itself) take that path with each fusion, both bit widths, biases, a
+# plain activation and the weight on the input, with H not a multiple of the K step (a
+# ragged last step).
+ROWSUM_CASES = {
+    "b4-separate": dict(),
+    "b4-interleaved-clamp-bias": dict(fusion=1, alpha=1.702, beta=1.0, limit=7.0, fc1_bias=True),
+    "b8-concatenated": dict(fusion=2, bits=8, scale_lo=0.005 / 16, scale_hi=0.02 / 16),
+    "b4-gelu-tanh": dict(activation="gelu", gelu_mode=1),
+    "b4-weight-on-input-f32scale": dict(on_input=True, scale_dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROWSUM_CASES))
+def test_forward_rowsum_path(name):
+    cfg = configs.C3.with_(name=f"rowsum-{name}", H=1056, I=1024, E=4, k=2, **ROWSUM_CASES[name])
+    T = 4096
+    p = params_for(cfg, T, layout="tiles")
+    assert qm.qmoe_tile_m(p) == 128
+    assert qm.qmoe_workspace_layout_of(p).xsum != 0  # the per-token row sums are formed
+    check_forward(cfg, T, sample=96, layout="tiles")
+
+
 @pytest.mark.parametrize("bits", configs.C5_BITS)
 @pytest.mark.parametrize("bs", configs.C5_BLOCKS)
 @pytest.mark.parametrize("T", configs.C5.T_points)

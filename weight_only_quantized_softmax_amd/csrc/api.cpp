@@ -274,6 +274,14 @@ bool use_i8_dot(const qmoe_params* p) {
          p->hidden_size % 64 == 0 && p->inter_size % 64 == 0;
 }
 
+// The forward forms each token's row sum once for fc1 (launch_rowsum): the 128-row
+// per-row-scale kernel on tiled weights takes its zero-point correction from it.
+bool use_xsum(const qmoe_params* p) {
+  return p->compute_mode == QMOE_COMPUTE_FLOAT && p->act_dtype == QMOE_BF16 &&
+         p->weight_layout == QMOE_LAYOUT_TILES && p->scale_dtype != QMOE_E8M0 &&
+         p->block_size == 0 && tile_m_of(p) == 128;
+}
+
 struct Workspace {
   int32_t* topk_ids;
   float* topk_w;
@@ -292,6 +300,7 @@ struct Workspace {
   float* xf;
   int8_t* hc;
   float* hf;
+  float* xsum;  // use_xsum: the row sums of x
   size_t bytes;
 };
 
@@ -328,6 +337,7 @@ Workspace carve(const qmoe_params* p, char* base) {
   } else if (p->compute_mode == QMOE_COMPUTE_INT8) {
     w.xq = take(p->num_tokens * p->hidden_size * act);
   }
+  if (use_xsum(p)) w.xsum = reinterpret_cast<float*>(take(p->num_tokens * 4));
   w.bytes = off;
   return w;
 }
@@ -406,10 +416,11 @@ hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, 
 qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
                     const int32_t* tiles, const int32_t* num_tiles, const float* topk_w,
                     qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s,
-                    const float* xfac = nullptr) {
+                    const float* xfac = nullptr, const float* xsum = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = x;
   g.afac = xfac;
+  g.xsum = xsum;
   g.sorted_assign = sorted_assign;
   g.row_w = p->apply_router_weight_on_input ? topk_w : nullptr;
   g.tile_list = tiles;
@@ -628,6 +639,7 @@ qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout
   out->xfactors = i8 ? off(w.xf) : 0;
   out->hcodes = i8 ? off(w.hc) : 0;
   out->hfactors = i8 ? off(w.hf) : 0;
+  out->xsum = use_xsum(p) ? off(w.xsum) : 0;
   out->total = w.bytes;
   out->fused_routing = qmoe::route_permute_fits(p->num_tokens, p->num_tokens * p->k,
                                                 p->num_experts, p->k) ? 1 : 0;
@@ -704,7 +716,12 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                            "quantize x launch"));
     x = w.xq;
   }
-  QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s));
+  if (use_xsum(p))
+    QMOE_TRY(device_status(qmoe::launch_rowsum(x, w.xsum, p->num_tokens,
+                                               static_cast<int>(p->hidden_size), s),
+                           "row sum launch"));
+  QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s,
+                   nullptr, w.xsum));
   if (int8)
     QMOE_TRY(device_status(qmoe::launch_quantize_blocks(w.h, w.h, abf, max_rows_of(p),
                                                         static_cast<int>(p->inter_size),

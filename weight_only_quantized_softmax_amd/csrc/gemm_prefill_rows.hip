@@ -24,9 +24,10 @@
 //     a dword in the order [e0 e4 e1 e5 e2 e6 e3 e7]; the activation fragment is permuted
 //     to match after its LDS read.
 //   - The zero point and the +128 offset leave through the row sums of the activations:
-//     acc - (c+z) * rowsum, scaled once per output row in the epilogue. The row sums come
-//     from v_dot2 on the fragments the waves already read (each wave sums half of its
-//     rows; the halves meet in LDS at the end).
+//     acc - (c+z) * rowsum, scaled once per output row in the epilogue. In the forward
+//     (XS) fc1 reads each token's row sum, formed once by launch_rowsum; otherwise the row
+//     sums come from v_dot2 on the fragments the waves already read (each wave sums a
+//     quarter of the rows; the quarters meet in LDS at the end).
 // One barrier per K step: the loads of step s+1 are issued before step s computes; the
 // activation loads are waited for after it, the weight loads where they are first used
 // (loads complete in issue order, so the wait counts past them).
@@ -80,7 +81,7 @@ struct RowsShape {
 
 // One wave's share of a workgroup; WN (the wave's column position) is a template argument
 // so that every choice that depends on it is made at compile time.
-template <int BITS, typename ST, int MODE, int WN, bool PK>
+template <int BITS, typename ST, int MODE, int WN, bool PK, bool XS>
 __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
                                           uint16_t* xs0, uint16_t* xs1, float* rowsum,
                                           uint32_t* xoffs_lds) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
       for (int mt = 0; mt < MT; ++mt) {
         u32x4 xv = xa[mt];
         if (BITS == 4 && !PK) xv = order_for_nibbles(xv);
-        if (mt == 2 * wn || mt == 2 * wn + 1) {
+        if (!XS && (mt == 2 * wn || mt == 2 * wn + 1)) {
           // row sums of slices 2 wn, 2 wn + 1
           const int h = mt - 2 * wn;
           rs[h] = dot2_sum(xv[3], dot2_sum(xv[2], dot2_sum(xv[1], dot2_sum(xv[0], rs[h]))));
@@ -297,10 +298,12 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
         for (int mt = 0; mt < MT; ++mt) xa[mt] = order_for_nibbles(xa[mt]);
       }
       // row sums of slices 2 wn, 2 wn + 1
+      if constexpr (!XS) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 v = xa[2 * wn + h];
-        rs[h] = dot2_sum(v[3], dot2_sum(v[2], dot2_sum(v[1], dot2_sum(v[0], rs[h]))));
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 v = xa[2 * wn + h];
+          rs[h] = dot2_sum(v[3], dot2_sum(v[2], dot2_sum(v[1], dot2_sum(v[0], rs[h]))));
+        }
       }
       bf16x8 bw = decode(w[0], j);
 #pragma unroll
@@ -339,6 +342,12 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   static_assert(kRNB < 64, "vmcnt holds 6 bits");
   constexpr int kWaitX = (kRNB & 15) | ((kRNB >> 4) << 14) | (7 << 4) | (15 << 8);
   u32x4 wa[kRNB], wb[kRNB];
+  if constexpr (XS) {
+    // the tile's row corrections from the tokens' row sums, into LDS before the first
+    // barrier (their loads overlap the first step's); rows past the valid ones keep 0
+    if (tid < kRTM)
+      rowsum[tid] = tid < valid ? -kCorr * g.xsum[gemm_src_row(g, row0 + tid)] : 0.f;
+  }
   xload(0, xs0);
   wload(0, wa);
   __builtin_amdgcn_s_waitcnt(0);
@@ -367,14 +376,16 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   }
 
   // ---- row sums: reduce over the four k lane groups, meet in LDS ----
+  if constexpr (!XS) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float v = rs[h];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (kq == 0) rowsum[wm * MT * 16 + (2 * wn + h) * 16 + n] = -kCorr * v;
+    for (int h = 0; h < 2; ++h) {
+      float v = rs[h];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (kq == 0) rowsum[wm * MT * 16 + (2 * wn + h) * 16 + n] = -kCorr * v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- epilogue: scale per output row, bias, activation ----
   float bias[kRNB], svr[kRNB];
@@ -419,7 +430,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   }
 }
 
-template <int BITS, typename ST, int MODE, bool PK>
+template <int BITS, typename ST, int MODE, bool PK, bool XS>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
   using S = RowsShape<BITS, MODE>;
   // two stages as two arrays, so that the compiler can tell the stage being read from the
@@ -434,10 +445,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   switch (wave / S::WM) {
-    case 0: rows_body<BITS, ST, MODE, 0, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    case 1: rows_body<BITS, ST, MODE, 1, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    case 2: if constexpr (S::WNC > 2) rows_body<BITS, ST, MODE, 2, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    default: if constexpr (S::WNC > 3) rows_body<BITS, ST, MODE, 3, PK>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 0: rows_body<BITS, ST, MODE, 0, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 1: rows_body<BITS, ST, MODE, 1, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 2: if constexpr (S::WNC > 2) rows_body<BITS, ST, MODE, 2, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    default: if constexpr (S::WNC > 3) rows_body<BITS, ST, MODE, 3, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
   }
 }
 
@@ -445,10 +456,17 @@ template <int BITS, typename ST, int MODE>
 static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = RowsShape<BITS, MODE>::BCOLS;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
+  // the forward's per-token row sums: fc1 in the tiled layout
+  if constexpr (MODE != kModeFc2) {
+    if (g.packed && g.xsum) {
+      launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true, true>, grid, block, 0, s, g);
+      return hipGetLastError();
+    }
+  }
   if (g.packed)
-    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true>, grid, block, 0, s, g);
+    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true, false>, grid, block, 0, s, g);
   else
-    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, false>, grid, block, 0, s, g);
+    launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, false, false>, grid, block, 0, s, g);
   return hipGetLastError();
 }
 

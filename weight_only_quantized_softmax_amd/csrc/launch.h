@@ -64,6 +64,10 @@ struct GemmArgs {
   const float* row_w;
   // the int8 dot: per-block factors 2^e of the rows of a (a then holds int8 codes)
   const float* afac;
+  // the 128-row per-row-scale fc1 kernel: the fp32 sum of each row of a (indexed like a's
+  // rows), from which the zero point's correction is taken; nullptr: the kernel sums the
+  // rows itself
+  const float* xsum;
 };
 
 // Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
@@ -202,6 +206,8 @@ struct CombineOpts {
 // The same rounding of bf16 rows as int8 codes [rows, K] (the chunks of 8 of every 64-group
 // in the order 0, 4, 1, 5, 2, 6, 3, 7) and one factor 2^e per block [rows, ceil(K/bs)] (fp32),
 // for the int8 dot. Needs K % 64 == 0, bs in {64, 128}, 16-byte aligned rows.
+// The fp32 sum of each of the rows of a bf16 [rows, K] matrix (one wave per row).
+hipError_t launch_rowsum(const void* x, float* out, int64_t rows, int K, hipStream_t s);
 hipError_t launch_quantize_codes(const void* in, int8_t* codes, float* fac, int64_t rows, int K,
                                  int bs, const int32_t* num_tiles, int tile_m, hipStream_t s);
 
