@@ -171,7 +171,9 @@ __global__ __launch_bounds__(NW_ * 64) void gemm_bf16_tile_kernel(GemmArgs g) {
         const int ss = ci * SPC + v * SK + ks;  // super-step (tile) index along K
         const uint32_t off = PK ? static_cast<uint32_t>(ss) * 1024u
                                 : static_cast<uint32_t>(ss * SSK) * BITS / 8;
-        w[st][v] = buf_load16_stream(wres[st], woff[st] + off);
+        // tiled: whole 1 KB tiles, read once (nontemporal); rows layout: the other half of
+        // each 128-byte line is read a chunk later and must stay cached
+        w[st][v] = PK ? buf_load16_stream(wres[st], woff[st] + off) : buf_load16(wres[st], woff[st] + off);
       }
   };
 

@@ -22,9 +22,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-// A weight stream read once per launch: the nontemporal policy (nt) lets the lines pass
-// through the caches without displacing what is reused (activations, scales). A plain read
-// of a few hundred MB runs about 8% faster on gfx950 with it.
+// A weight stream read once per launch, whole lines at a time (the tiled layout): the
+// nontemporal policy (nt) lets the lines pass through the caches without displacing what
+// is reused (activations, scales). A plain read of a few hundred MB runs about 8% faster
+// on gfx950 with it; a stream that reads half a line now and the other half later must not
+// use it (the line is gone by then).
 __device__ __forceinline__ u32x4 buf_load16_stream(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
