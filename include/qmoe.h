@@ -12,8 +12,8 @@
  * quantized and are decoded block by block inside the GEMM dot; forward:
  * x [T,H] and router_logits [T,E] give [T,H] in x's dtype, optional
  * shared_output folded into the combine); CLIKA "MoE" page (top-k routing,
- * gated FFN, combine under the router weights; routing kwargs); CLIKA
- * "QLinearWoQ" page (y = x @ dequant(W).T + bias); graiphic "QMoE" page (input
+ * gated FFN, routing-weighted sum of the expert outputs; routing kwargs); CLIKA
+ * "QLinearWoQ" page (y = x·dequant(W)ᵀ + b); graiphic "QMoE" page (input
  * tensors and their shapes; attributes activation_alpha/beta, activation_type,
  * block_size, expert_weight_bits, k, normalize_routing_weights, swiglu_fusion,
  * swiglu_limit).
@@ -112,8 +112,8 @@ typedef struct {
      QMOE_LAYOUT_TILES requires act_dtype QMOE_BF16. */
   int32_t weight_layout;
   /* Routing variants (CLIKA "MoE" page: routing kwargs n_group, topk_group,
-     routed_scaling_factor; ClikaRT "QMoEWoQ" page: the aux-free selection bias
-     e_score_correction_bias [E]). All off when zero / NULL.
+     routed_scaling_factor; ClikaRT "QMoEWoQ" page: e_score_correction_bias [E], a
+     per-expert bias used for the choice of experts). All off when zero / NULL.
      n_group > 1: experts form n_group groups of E / n_group consecutive indices (E a
        multiple, n_group <= 16); a group scores the largest selection key of its experts;
        the topk_group best groups are kept (ties to the lower group) and the k experts are
@@ -230,7 +230,7 @@ size_t qmoe_permute_scratch_size(const qmoe_params* p);
 size_t qmoe_workspace_size(const qmoe_params* p);
 
 /*
- * Routing (CLIKA "MoE" page: router picks top-k experts per token; routing_mode
+ * Routing (CLIKA "MoE" page: each token goes to its top-k experts; routing_mode
  * "softmax_topk", renormalize; graiphic "QMoE" page: k, normalize_routing_weights;
  * ClikaRT "QMoEWoQ" page: the caller hands router logits to forward).
  *   router_logits [T, E] act_dtype  ->  topk_ids [T, k] int32, topk_w [T, k] float32.
@@ -295,7 +295,7 @@ qmoe_status qmoe_grouped_gemm_fc2(const qmoe_params* p, const void* h, const int
                                   void* stream);
 
 /*
- * Weighted combine (CLIKA "MoE" page: outputs combine under the router weights;
+ * Weighted combine (CLIKA "MoE" page: routing-weighted sum of the expert outputs;
  * ClikaRT "QMoEWoQ" page forward: shared_output folds into the same epilogue and the
  * result takes x's dtype).
  *   out[t, :] = round( sum_{j<k} c[t, j] * y[assign_pos[t*k + j], :] + shared[t, :] )
@@ -389,8 +389,8 @@ typedef struct {
 qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);
 
 /*
- * The int8 activation tier's rounding (ClikaRT "QMoEWoQ" page: the activation is rounded
- * to per-block int8 before the dot where a block weight runs on the int8 tier).
+ * The int8 activation tier's rounding (ClikaRT "QMoEWoQ" page, class description: on the
+ * int8 block tier the activation is quantised to int8 per block ahead of the dot product).
  *   in, out: [rows, cols] act_dtype, row-major (out may equal in). Each run of
  *   p->block_size elements of a row (a shorter last one when block_size does not divide
  *   cols) gets the power-of-two scale 2^e, e the smallest integer with
@@ -409,8 +409,8 @@ qmoe_status qmoe_quantize_act(const qmoe_params* p, const void* in, int64_t rows
                               void* out, void* stream);
 
 /*
- * Weight-only-quantized linear layer (ClikaRT "QLinearWoQ" page: y = x @ dequant(weight)^T
- * + bias, the weight at rest quantized, an optional activation fused as the epilogue):
+ * Weight-only-quantized linear layer (ClikaRT "QLinearWoQ" page: y = x·dequant(W)ᵀ + b,
+ * the weight kept quantized at rest, an activation optionally fused as the epilogue):
  * the grouped GEMM of this library over one expert and no routing.
  *   p: the parameter block read as one layer -- num_experts 1, k 1; num_tokens = rows of
  *      x (T), hidden_size = in_features (K), inter_size = out_features (N); activation

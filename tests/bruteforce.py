@@ -13,9 +13,9 @@ It is built differently from the oracle on purpose:
 * with the routing weight on the input, each expert's fc1 output is scaled by the dense
   gate weight (linearity) and the outputs are mixed through the 0/1 selection matrix.
 
-Sources for what is computed: CLIKA "MoE" page (router picks top-k experts,
-gated FFN, outputs combined under the router weights); CLIKA "QLinearWoQ" page
-(y = x @ dequant(W).T + bias); graiphic "QMoE" page (tensor shapes,
+Sources for what is computed: CLIKA "MoE" page (top-k routing per token, gated
+FFN, routing-weighted sum of the expert outputs); CLIKA "QLinearWoQ" page
+(y = x·dequant(W)ᵀ + b); graiphic "QMoE" page (tensor shapes,
 swiglu_fusion, block_size, expert_weight_bits, activation parameters).
 """
 from __future__ import annotations

@@ -191,7 +191,7 @@ qmoe_status validate(const qmoe_params* p) {
     return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be multiples of %d", pack);
   if (p->strict_blocks && p->block_size &&
       (p->hidden_size % p->block_size || p->inter_size % p->block_size))
-    return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be divisible by block_size %d",
+    return fail(QMOE_ERR_SHAPE, "hidden_size and inter_size must be multiples of block_size %d",
                 p->block_size);
   if (p->num_tokens * p->k >= (int64_t(1) << 31))
     return fail(QMOE_ERR_UNSUPPORTED, "num_tokens * k must stay below 2^31");

@@ -1,6 +1,7 @@
 // Weighted combine of the per-assignment expert outputs.
 //
-// CLIKA "MoE" page: the selected experts' outputs combine under the router weights.
+// CLIKA "MoE" page: a token's output is the routing-weighted sum of its selected experts'
+// outputs.
 // ClikaRT "QMoEWoQ" page, forward: an optional shared_output folds into the same
 // epilogue and the result takes the dtype of x.
 //

@@ -1,6 +1,6 @@
 // Grouped dequant GEMM for the smallest decode batches: the weight-streaming form of the
-// per-expert FFN GEMMs of the ClikaRT "QMoEWoQ" page (each expert weight decoded one block
-// at a time inside the dot, the quantized stream read at its stored size), for grids too
+// per-expert FFN GEMMs of the ClikaRT "QMoEWoQ" page (the codes are expanded block by block
+// within the dot product, and the weights stream at their quantized size), for grids too
 // small to fill the chip with 16-row tiles of several column groups each.
 //
 // One workgroup = one 16-row tile x one column group (16 SwiGLU outputs from a gate and

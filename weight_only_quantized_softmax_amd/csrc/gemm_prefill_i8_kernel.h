@@ -1,9 +1,9 @@
 // The int8 activation tier's dot product on the int8 matrix cores: 128-row tiles, tiled
 // weight layout, 4- or 8-bit weight codes, block scales of 64 and 128.
 //
-// ClikaRT "QMoEWoQ" page, class description: where a packed block weight runs on the int8
-// block tier, the activation is rounded to per-block int8 before the dot. graiphic "QMoE"
-// page: stacks [E, N, K/pack], scales [E, N, K/block_size].
+// ClikaRT "QMoEWoQ" page, class description: on the int8 block tier the activation is
+// quantised to int8 per block ahead of the dot product. graiphic "QMoE" page: stacks
+// [E, N, K/pack], scales [E, N, K/block_size].
 //
 // The activations arrive as int8 codes with one power-of-two factor 2^e per row and block
 // (launch_quantize_codes). The weights' codes become signed int8 (q - z) in registers: a

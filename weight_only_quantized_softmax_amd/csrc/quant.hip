@@ -1,6 +1,6 @@
 // The int8 activation tier: an activation row is rounded to int8 block by block before the
-// dequant GEMM (ClikaRT "QMoEWoQ" page: where a packed block weight runs on an int8 block
-// tier, the floating-point activation is rounded to per-block int8 before the dot).
+// dequant GEMM (ClikaRT "QMoEWoQ" page, class description: on the int8 block tier the
+// floating-point activation is quantised to int8 per block ahead of the dot product).
 //
 // Each block of block_size consecutive elements of a row gets the power-of-two scale 2^e,
 // e the smallest exponent with max|x| <= 127 * 2^e, and the codes rint(x / 2^e) (ties to

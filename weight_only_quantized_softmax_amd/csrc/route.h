@@ -1,8 +1,8 @@
 // Softmax-top-k routing of one token by one wavefront, shared by the routing kernel and
 // the fused routing-and-grouping kernel.
 //
-// CLIKA "MoE" page: the router picks the top-k experts of each token and the outputs
-// combine under the router weights (routing_mode "softmax_topk", renormalize);
+// CLIKA "MoE" page: each token goes to its top-k experts, whose outputs are summed with the
+// routing weights as coefficients (routing_mode "softmax_topk", renormalize);
 // graiphic "QMoE" page: attributes k and normalize_routing_weights.
 //
 // A token is routed by a group of G lanes: a whole wave (G = 64), or one 16-lane DPP row
@@ -146,8 +146,8 @@ __device__ __forceinline__ void route_mixer(TokenLogits<V>& r, int t, int E, con
 // t): lanes j < k of the group write its j-th expert id and weight to topk_ids[t*k + j] and
 // topk_w[t*k + j].
 // Routing variants (RouteOpts; CLIKA "MoE" page routing kwargs n_group, topk_group,
-// routed_scaling_factor; ClikaRT "QMoEWoQ" page, the aux-free selection bias
-// e_score_correction_bias [E]): the bias is added to the logits in fp32 for the selection
+// routed_scaling_factor; ClikaRT "QMoEWoQ" page, e_score_correction_bias [E], a per-expert
+// bias for the choice of experts): the bias is added to the logits in fp32 for the selection
 // only; with n_group > 1 the experts form n_group groups of E / n_group consecutive
 // indices, a group scores the largest selection key of its experts, the topk_group best
 // groups (ties to the lower group) are kept and the k experts are chosen among theirs;
