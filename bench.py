@@ -86,10 +86,16 @@ def parse():
 
 
 def kernel_sources_sha(files):
+    """Hash of the kernel sources' code: comments and blank space are dropped first, so that
+    an edit of a comment does not retire a counter summary taken on the same code."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
