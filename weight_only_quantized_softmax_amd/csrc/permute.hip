@@ -18,6 +18,7 @@ namespace qmoe {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
+static_assert(kPermWaves <= kWave, "the wave totals are scanned by one wave");
 
 // Exclusive scan of one int per thread over the block; also returns the total.
 __device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */, int* total) {
@@ -30,14 +31,17 @@ __device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */, int* t
   }
   if (lane == kWave - 1) tmp[w] = inc;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kPermWaves; ++i) {
-      int c = tmp[i];
-      tmp[i] = run;
-      run += c;
+  if (w == 0) {
+    // the waves' totals, scanned by the first wave's lanes (kPermWaves <= 64)
+    const int c = lane < kPermWaves ? tmp[lane] : 0;
+    int cin = c;
+#pragma unroll
+    for (int d = 1; d < kPermWaves; d <<= 1) {
+      const int o = __shfl_up(cin, d);
+      if (lane >= d) cin += o;
     }
-    tmp[kPermWaves] = run;
+    if (lane < kPermWaves) tmp[lane] = cin - c;
+    if (lane == kPermWaves - 1) tmp[kPermWaves] = cin;
   }
   __syncthreads();
   const int excl = tmp[w] + inc - v;
@@ -72,18 +76,22 @@ __device__ void block_rank_scatter(const int32_t* __restrict__ ids, int64_t a0, 
     const int rank = __popcll(same & ((1ull << lane) - 1ull));
     if (valid && rank == 0) wc[w * E + e] = __popcll(same);
     __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int w2 = 0; w2 < w; ++w2) pre += wc[w2 * E + e];
-      const int pos = run[e] + pre + rank;
-      sorted_assign[pos] = static_cast<int32_t>(a);
-      assign_pos[a] = pos;
+    // per expert: its first row for each wave (run[e] plus the counts of the waves
+    // before), in place over wc, and run[e] advanced past the chunk
+    for (int ee = tid; ee < E; ee += kPermThreads) {
+      int r = run[ee];
+      for (int w2 = 0; w2 < kPermWaves; ++w2) {
+        const int c = wc[w2 * E + ee];
+        wc[w2 * E + ee] = r;
+        r += c;
+      }
+      run[ee] = r;
     }
     __syncthreads();
-    for (int ee = tid; ee < E; ee += kPermThreads) {
-      int s = 0;
-      for (int w2 = 0; w2 < kPermWaves; ++w2) s += wc[w2 * E + ee];
-      run[ee] += s;
+    if (valid) {
+      const int pos = wc[w * E + e] + rank;
+      sorted_assign[pos] = static_cast<int32_t>(a);
+      assign_pos[a] = pos;
     }
     __syncthreads();
   }
