@@ -376,6 +376,14 @@ qmoe_status qmoe_forward_noalloc(const qmoe_params* p, const void* input,
  *                   tiled weights, 128-row tiles, one scale per output row and
  *                   compute_mode QMOE_COMPUTE_FLOAT (fc1 takes the zero point's correction
  *                   from it); 0 otherwise.
+ *   x16, xlift, h16, hlift   with 4-bit codes and bf16 block scales of 16 to 128, bf16
+ *                   activations, tiled weights, 128-row tiles, compute_mode
+ *                   QMOE_COMPUTE_FLOAT, H and I multiples of 8 (0 otherwise): x [T, H] and
+ *                   h [qmoe_max_rows, I] as fp16 rows, row r multiplied by 2^lift[r]
+ *                   (int32 [T] and [qmoe_max_rows]; the power of two that puts the row's
+ *                   largest magnitude in [2^14, 2^15)), which the GEMMs take on fp16 matrix
+ *                   cores with each weight (q - 8) * scale exact in one fp16 operand; h16
+ *                   holds only the rows of the tiles in use.
  * Errors: invalid parameters as qmoe_validate; out NULL -> QMOE_ERR_UNBOUND.
  */
 typedef struct {
@@ -384,6 +392,7 @@ typedef struct {
   int32_t fused_routing;
   size_t xcodes, xfactors, hcodes, hfactors;
   size_t xsum;
+  size_t x16, xlift, h16, hlift;
 } qmoe_workspace_layout;
 
 qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);

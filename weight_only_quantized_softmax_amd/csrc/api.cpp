@@ -282,6 +282,18 @@ bool use_xsum(const qmoe_params* p) {
          p->block_size == 0 && tile_m_of(p) == 128;
 }
 
+// The fp16 block-scale path: 4-bit codes with bf16 block scales of 16 to 128 at 128-row
+// tiles in the tiled layout, bf16 activations. The forward lifts x and h into fp16 and the
+// weight rows' scales by powers of two (launch_rows_to_f16, launch_scale_lift), and the GEMMs
+// take each weight exactly as one fp16 operand (gemm_prefill_h16_kernel.h). The stage entry
+// points, which have no workspace for the fp16 rows, keep the bf16 kernels.
+bool use_h16(const qmoe_params* p) {
+  return p->compute_mode == QMOE_COMPUTE_FLOAT && p->act_dtype == QMOE_BF16 &&
+         p->weight_layout == QMOE_LAYOUT_TILES && p->scale_dtype == QMOE_BF16 &&
+         p->expert_weight_bits == 4 && p->block_size >= 16 && p->block_size <= 128 &&
+         tile_m_of(p) == 128 && p->hidden_size % 8 == 0 && p->inter_size % 8 == 0;
+}
+
 struct Workspace {
   int32_t* topk_ids;
   float* topk_w;
@@ -301,6 +313,15 @@ struct Workspace {
   int8_t* hc;
   float* hf;
   float* xsum;  // use_xsum: the row sums of x
+  // use_h16: x and h as lifted fp16 rows with their lifts, and the lifts of the weight rows'
+  // scales (fc1, fc3 when separate, fc2)
+  void* x16;
+  int32_t* xlift;
+  void* h16;
+  int32_t* hlift;
+  int32_t* w1lift;
+  int32_t* w3lift;
+  int32_t* w2lift;
   size_t bytes;
 };
 
@@ -338,6 +359,15 @@ Workspace carve(const qmoe_params* p, char* base) {
     w.xq = take(p->num_tokens * p->hidden_size * act);
   }
   if (use_xsum(p)) w.xsum = reinterpret_cast<float*>(take(p->num_tokens * 4));
+  if (use_h16(p)) {
+    w.x16 = take(p->num_tokens * p->hidden_size * 2);
+    w.xlift = reinterpret_cast<int32_t*>(take(p->num_tokens * 4));
+    w.h16 = take(rows * p->inter_size * 2);
+    w.hlift = reinterpret_cast<int32_t*>(take(rows * 4));
+    w.w1lift = reinterpret_cast<int32_t*>(take(p->num_experts * n1_rows(p) * 4));
+    if (has_fc3(p)) w.w3lift = reinterpret_cast<int32_t*>(take(p->num_experts * p->inter_size * 4));
+    w.w2lift = reinterpret_cast<int32_t*>(take(p->num_experts * p->hidden_size * 4));
+  }
   w.bytes = off;
   return w;
 }
@@ -408,6 +438,7 @@ hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, 
   const bool sbf = p->scale_dtype == QMOE_BF16;
   const int bits = p->expert_weight_bits;
   if (g.afac) return qmoe::launch_gemm_i8_prefill(g, mode, bits, sbf, max_tiles_of(p), s);
+  if (g.alift) return qmoe::launch_gemm_h16_prefill(g, mode, max_tiles_of(p), s);
   if (p->act_dtype != QMOE_BF16) return qmoe::launch_gemm_f32(g, mode, bits, sbf, max_tiles_of(p), s);
   if (tile_m_of(p) == 128) return qmoe::launch_gemm_bf16_prefill(g, mode, bits, sbf, max_tiles_of(p), s);
   return qmoe::launch_gemm_bf16(g, mode, bits, sbf, max_tiles_of(p), s);
@@ -416,11 +447,18 @@ hipError_t launch_gemm(const qmoe_params* p, const qmoe::GemmArgs& g, int mode, 
 qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_assign,
                     const int32_t* tiles, const int32_t* num_tiles, const float* topk_w,
                     qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s,
-                    const float* xfac = nullptr, const float* xsum = nullptr) {
+                    const float* xfac = nullptr, const float* xsum = nullptr,
+                    const Workspace* h16 = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = x;
   g.afac = xfac;
   g.xsum = xsum;
+  if (h16) {
+    g.a = h16->x16;
+    g.alift = h16->xlift;
+    g.wlift = h16->w1lift;
+    g.wlift3 = h16->w3lift;
+  }
   g.sorted_assign = sorted_assign;
   g.row_w = p->apply_router_weight_on_input ? topk_w : nullptr;
   g.tile_list = tiles;
@@ -465,10 +503,15 @@ qmoe_status run_linear(const qmoe_params* p, const void* x, qmoe_stack w, void* 
 
 qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
                     const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s,
-                    const float* hfac = nullptr) {
+                    const float* hfac = nullptr, const Workspace* h16 = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = h;
   g.afac = hfac;
+  if (h16) {
+    g.a = h16->h16;
+    g.alift = h16->hlift;
+    g.wlift = h16->w2lift;
+  }
   g.tile_list = tiles;
   g.num_tiles = num_tiles;
   g.w = static_cast<const uint8_t*>(fc2.weights);
@@ -640,6 +683,11 @@ qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout
   out->hcodes = i8 ? off(w.hc) : 0;
   out->hfactors = i8 ? off(w.hf) : 0;
   out->xsum = use_xsum(p) ? off(w.xsum) : 0;
+  const bool h16 = use_h16(p);
+  out->x16 = h16 ? off(w.x16) : 0;
+  out->xlift = h16 ? off(w.xlift) : 0;
+  out->h16 = h16 ? off(w.h16) : 0;
+  out->hlift = h16 ? off(w.hlift) : 0;
   out->total = w.bytes;
   out->fused_routing = qmoe::route_permute_fits(p->num_tokens, p->num_tokens * p->k,
                                                 p->num_experts, p->k) ? 1 : 0;
@@ -715,6 +763,34 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                                                         p->block_size, nullptr, 0, s),
                            "quantize x launch"));
     x = w.xq;
+  }
+  if (use_h16(p)) {
+    // the fp16 block-scale path: lifts of the weight rows' scales, x in fp16, fc1, h in
+    // fp16 (the rows of the tiles in use), fc2
+    const int H = static_cast<int>(p->hidden_size), I = static_cast<int>(p->inter_size);
+    const int nbh = (H + p->block_size - 1) / p->block_size;
+    const int nbi = (I + p->block_size - 1) / p->block_size;
+    QMOE_TRY(device_status(qmoe::launch_scale_lift(fc1.scales, w.w1lift, p->num_experts * n1_rows(p),
+                                                   nbh, s), "fc1 scale lift launch"));
+    if (has_fc3(p))
+      QMOE_TRY(device_status(qmoe::launch_scale_lift(fc3.scales, w.w3lift, p->num_experts * I, nbh, s),
+                             "fc3 scale lift launch"));
+    QMOE_TRY(device_status(qmoe::launch_scale_lift(fc2.scales, w.w2lift, p->num_experts * H, nbi, s),
+                           "fc2 scale lift launch"));
+    QMOE_TRY(device_status(qmoe::launch_rows_to_f16(input, w.x16, w.xlift, p->num_tokens, H, nullptr, 0, s),
+                           "x to fp16 launch"));
+    QMOE_TRY(run_fc1(p, input, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s,
+                     nullptr, nullptr, &w));
+    QMOE_TRY(device_status(qmoe::launch_rows_to_f16(w.h, w.h16, w.hlift, max_rows_of(p), I, w.num_tiles,
+                                                    128, s),
+                           "h to fp16 launch"));
+    QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s, nullptr, &w));
+    QMOE_TRY(device_status(
+        qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output, true,
+                             static_cast<int>(p->num_tokens), H, static_cast<int>(p->k),
+                             combine_opts(p), s),
+        "combine launch"));
+    return ok();
   }
   if (use_xsum(p))
     QMOE_TRY(device_status(qmoe::launch_rowsum(x, w.xsum, p->num_tokens,

@@ -68,6 +68,12 @@ struct GemmArgs {
   // rows), from which the zero point's correction is taken; nullptr: the kernel sums the
   // rows itself
   const float* xsum;
+  // the fp16 block-scale kernel (launch_gemm_h16_prefill): a holds fp16 rows, row i lifted
+  // by 2^alift[i] (indexed like a's rows); the block scales of weight row n of expert e are
+  // lifted by 2^wlift[e * rows + n] (wlift3: the separate up stack); nullptr otherwise
+  const int32_t* alift;
+  const int32_t* wlift;
+  const int32_t* wlift3;
 };
 
 // Tiles of a GEMM launch: the grouping's tile list, or the linear layer's row tiles.
@@ -216,6 +222,20 @@ hipError_t launch_quantize_codes(const void* in, int8_t* codes, float* fac, int6
 bool prefill_i8_supports(const GemmArgs& g, int bits);
 hipError_t launch_gemm_i8_prefill(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                   int64_t max_tiles, hipStream_t s);
+
+// The fp16 block-scale path (f16prep.hip, gemm_prefill_h16.hip): 4-bit codes with bf16
+// block scales of 16 to 128, tiled layout, 128-row tiles, K % 8 == 0.
+// Rows of a bf16 [rows, K] matrix to fp16, each lifted by the power of two 2^lift[r] that
+// puts its largest magnitude in [2^14, 2^15); num_tiles (device, may be null): only the
+// first *num_tiles * tile_m rows.
+hipError_t launch_rows_to_f16(const void* in, void* out, int32_t* lift, int64_t rows, int K,
+                              const int32_t* num_tiles, int tile_m, hipStream_t s);
+// For each of `rows` rows of nb bf16 scales: the power of two 2^lift[r] that puts the row's
+// largest scale in [2^12, 2^13).
+hipError_t launch_scale_lift(const void* scales, int32_t* lift, int64_t rows, int nb,
+                             hipStream_t s);
+// g.a: fp16 rows with g.alift; g.wlift (and g.wlift3) from launch_scale_lift.
+hipError_t launch_gemm_h16_prefill(const GemmArgs& g, int mode, int64_t max_tiles, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
                           const void* shared, void* out, bool bf16, int T, int H, int k,
