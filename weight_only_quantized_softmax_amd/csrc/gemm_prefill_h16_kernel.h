@@ -29,8 +29,11 @@
 //   - Weights: one 16-byte load per slice and K step (one lane's share of a contiguous 1 KB
 //     tile), a whole step ahead, with the default cache policy: the tiles of one expert that
 //     an XCD runs together (xcd_item's bands) read each weight tile through its L2.
-//   - Scales: the 128 rows x the step's blocks, loaded a step ahead into registers, lifted
-//     and widened to an fp16 pair when written to a two-slot LDS ring before the barrier.
+//   - Scales: the 256 weight rows x the step's blocks (one row per thread), loaded a step
+//     ahead into registers, lifted to fp16 when written to a two-slot LDS ring before the
+//     barrier, widened to a pair when read.
+//   - Rows: the tile's source-row offsets, row factors and lifts in an LDS table formed
+//     once (one thread per row); the activation loads read their offsets from it.
 #pragma once
 
 #include "common.h"
@@ -84,7 +87,13 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
 
   __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
-  __shared__ uint32_t sring[2][SROWS * NBLK];  // lifted scales (fp16 pairs), this step and next
+  __shared__ uint16_t sring[2][SROWS * NBLK];  // lifted scales (fp16), this step and next
+  // the tile's rows, formed once by threads 0..127: byte offset of the row of a that feeds
+  // it (kOutOfRange for padding rows), the factor on its sums (the routing weight when it
+  // goes to the expert's input, else 1) and its lift (written after the main loop)
+  __shared__ uint32_t rsrc[kTM];
+  __shared__ float rscale[kTM];
+  __shared__ int rlift[kTM];
 
   int tile, cblk;
   if (!xcd_item(gemm_tile_count(g), (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
@@ -162,8 +171,7 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
 #pragma unroll
     for (int l = 0; l < NBLK; ++l) {
       const _Float16 h = static_cast<_Float16>(ldexpf(bf16_to_f32(sreg[l]), slift));
-      const uint32_t hb = __builtin_bit_cast(uint16_t, h);
-      sring[slot][tid * NBLK + l] = hb | (hb << 16);
+      sring[slot][tid * NBLK + l] = __builtin_bit_cast(uint16_t, h);
     }
   };
 
@@ -175,18 +183,28 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
     return (p % GPR) ^ key(p / GPR);
   };
   const int gq = granule(0);  // the same for every load t (4t * 64 / GPR rows later)
-  uint32_t xoffs[NDMA];
-#pragma unroll
-  for (int t = 0; t < NDMA; ++t) {
-    const int p = (wave + 4 * t) * 64 + lane;
-    const int r = p / GPR, q = granule(t);
+  int my_lift = 0;  // thread t < 128: the lift of row t, stored to rlift after the main loop
+  if (tid < kTM) {
+    const int m = tid;
     uint32_t off = kOutOfRange;  // padding rows land as zeros
-    if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : gemm_src_row(g, row0 + r);
-      off = static_cast<uint32_t>((src * K + 8 * q) * 2);
+    float rs = 1.f;
+    if (m < valid) {
+      const int64_t r = row0 + m;
+      const int64_t src = (MODE == kModeFc2) ? r : gemm_src_row(g, r);
+      off = static_cast<uint32_t>(src * K * 2);
+      if (MODE != kModeFc2) rs = gemm_row_scale(g, r);
+      my_lift = g.alift[src];
     }
-    xoffs[t] = off;
+    rsrc[m] = off;
+    rscale[m] = rs;
   }
+  __syncthreads();
+  // load t of this lane: row (wave + 4t) * 64 / GPR + lane / GPR of the tile, granule gq;
+  // its offset is read from the row table at each load instead of held in registers
+  auto xoff = [&](int t) -> uint32_t {
+    const uint32_t base = rsrc[(wave + 4 * t) * (64 / GPR) + lane / GPR];
+    return base == kOutOfRange ? kOutOfRange : base + static_cast<uint32_t>(16 * gq);
+  };
   auto xload = [&](int s, uint16_t* stage) {
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
     if (k0 + SSK > K) {
@@ -194,11 +212,11 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
       // zeros
 #pragma unroll
       for (int t = 0; t < NDMA; ++t)
-        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, k0 + 8 * gq < K ? xoffs[t] : kOutOfRange,
+        buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, k0 + 8 * gq < K ? xoff(t) : kOutOfRange,
                        2 * k0);
     } else {
 #pragma unroll
-      for (int t = 0; t < NDMA; ++t) buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoffs[t], 2 * k0);
+      for (int t = 0; t < NDMA; ++t) buf_load16_lds(xres, stage + (wave + 4 * t) * 64 * 8, xoff(t), 2 * k0);
     }
     // the step-end wait counts the loads issued after these: none may move above
     __builtin_amdgcn_sched_barrier(0);
@@ -224,17 +242,17 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
 
   // the lifted scale pair of slice b for this lane's 8 weights of k-slice j (one block: a
   // lane's 8 k lie in one block of 16 or longer)
-  auto lane_scale = [&](const uint32_t* sc, int b, int j) -> half2_t {
-    const uint32_t* row = sc + (wn * 16 * kNB + b * 16 + n) * NBLK;
+  auto lane_scale = [&](const uint16_t* sc, int b, int j) -> half2_t {
+    const uint16_t* row = sc + (wn * 16 * kNB + b * 16 + n) * NBLK;
     uint32_t v;
     if constexpr (BS == 16 && NBLK > 1)
       v = row[2 * j + (kq >> 1)];
     else
       v = row[BS < SSK ? (32 * j) / BS : 0];
-    return __builtin_bit_cast(half2_t, v);
+    return __builtin_bit_cast(half2_t, v | (v << 16));
   };
   auto compute = [&](const uint16_t* stage, const u32x4 (&w)[kNB], int slot) {
-    const uint32_t* sc = sring[slot];
+    const uint16_t* sc = sring[slot];
     u32x4 xa[kMT];
     aread(stage, 0, xa);
 #pragma unroll
@@ -295,7 +313,11 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   }
   if (nss & 1) compute(xs0, wa, 0);
 
-  // ---- epilogue: the lifts divided out, bias, activation ----
+  // ---- epilogue: the lifts divided out, bias, activation; the outputs pass through the
+  // (now free) activation stages so that they leave in 16-byte row segments ----
+  if (tid < kTM) rlift[tid] = my_lift;
+  // every wave is past its last read of the stages, and the lifts are in place
+  __syncthreads();
   float bias[kNB];
   int wl[kNB];
 #pragma unroll
@@ -307,35 +329,75 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
     bias[b] = bp ? bf16_to_f32(bp[wrow]) : 0.f;
     wl[b] = stream_lift(st)[wrow];
   }
+  // staging: 128 output columns per stage, rows of 256 bytes (bf16 h) or 512 bytes (fp32 y,
+  // in two passes of 64 rows); the 16-byte chunk c of row r sits at slot c ^ (r mod chunks),
+  // so the 16 lanes of one MFMA row and the four rows a wave writes at once fall in
+  // distinct banks
+  constexpr int kEl = MODE == kModeFc2 ? 4 : 2;        // bytes per output
+  constexpr int kPass = MODE == kModeFc2 ? 2 : 1;
+  constexpr int kRowsPass = kTM / kPass;
+  constexpr int kChunkEl = 16 / kEl;                   // outputs per 16-byte chunk
+  constexpr int kChunks = 128 / kChunkEl;              // chunks per staged row
+  constexpr int kStages = (BCOLS + 127) / 128;
+  constexpr int kRowBytes = 128 * kEl;
+  static_assert(kRowsPass * kRowBytes == STAGE * 2, "a pass fills a stage");
+  auto staged = [&](int rl, int c) -> char* {
+    char* st = reinterpret_cast<char*>(c < 128 ? xs0 : xs1);
+    const int cc = c & 127;
+    return st + rl * kRowBytes + (((cc / kChunkEl) ^ (rl & (kChunks - 1))) * 16) + (cc % kChunkEl) * kEl;
+  };
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
+  for (int pass = 0; pass < kPass; ++pass) {
+    if (pass > 0) __syncthreads();  // the previous pass's copies have read the stages
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * kq + i;
-      const int64_t r = row0 + m;
-      // fc1 with the routing weight on the input: the row's weight scales its sums
-      const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
-      const int al = m < valid ? g.alift[(MODE == kModeFc2) ? r : gemm_src_row(g, r)] : 0;
+    for (int mt = pass * (kMT / kPass); mt < (pass + 1) * (kMT / kPass); ++mt) {
 #pragma unroll
-      for (int cb = 0; cb < NBS; ++cb) {
-        const int col = slice_col(wn, cb, n);
-        if (col >= g.ncols) continue;
-        float z[NS];
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kq + i;
+        const int rl = m - pass * kRowsPass;
+        const float rs = rscale[m];
+        const int al = rlift[m];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          const int b = st * NBS + cb;
-          z[st] = ldexpf(acc[mt][b][i], -(al + wl[b])) * rs + bias[b];
-        }
-        if (MODE == kModeFc2) {
-          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];
-        } else {
-          float hv = 0.f;
-          if (m < valid)
-            hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
-                                       : plain_act(z[0], g.act);
-          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+        for (int cb = 0; cb < NBS; ++cb) {
+          const int cl = wn * NBS * 16 + cb * 16 + n;  // column inside the workgroup
+          float z[NS];
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const int b = st * NBS + cb;
+            z[st] = ldexpf(acc[mt][b][i], -(al + wl[b])) * rs + bias[b];
+          }
+          if (MODE == kModeFc2) {
+            *reinterpret_cast<float*>(staged(rl, cl)) = z[0];
+          } else {
+            float hv = 0.f;
+            if (m < valid)
+              hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
+                                         : plain_act(z[0], g.act);
+            *reinterpret_cast<uint16_t*>(staged(rl, cl)) = f32_to_bf16(hv);
+          }
         }
       }
+    }
+    __syncthreads();
+    // copies out: chunk q of the pass is stage q / (rows * chunks), row (q / chunks) % rows,
+    // chunk q % chunks; real rows only for y, every row of the tile for h (padding rows as
+    // the zeros staged for them), except for the linear layer
+    constexpr int kTot = kRowsPass * kChunks * kStages;
+#pragma unroll
+    for (int u = 0; u < (kTot + 255) / 256; ++u) {
+      const int q = tid + 256 * u;
+      if (q >= kTot) break;
+      const int stg = q / (kRowsPass * kChunks);
+      const int rl = (q / kChunks) % kRowsPass, ch = q % kChunks;
+      const int m = pass * kRowsPass + rl;
+      const int col = col0 + stg * 128 + ch * kChunkEl;
+      if (col >= g.ncols) continue;
+      if (MODE == kModeFc2 ? m >= valid : (m >= valid && g.linear)) continue;
+      const char* src = reinterpret_cast<const char*>(stg == 0 ? xs0 : xs1) + rl * kRowBytes +
+                        ((ch ^ (rl & (kChunks - 1))) * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      char* dst = static_cast<char*>(g.out) + ((row0 + m) * g.ncols + col) * kEl;
+      *reinterpret_cast<u32x4*>(dst) = v;
     }
   }
 }
