@@ -28,6 +28,13 @@
 //     (XS) fc1 reads each token's row sum, formed once by launch_rowsum; otherwise the row
 //     sums come from v_dot2 on the fragments the waves already read (each wave sums a
 //     quarter of the rows; the quarters meet in LDS at the end).
+//   - The tile's rows are formed once, by one thread per row, into an LDS table: the byte
+//     offset of the row of the activations that feeds it (one division by k per row) and,
+//     with the forward's row sums, its correction. The activation loads take their offsets
+//     from it.
+//   - fc1 (4-bit codes): the outputs pass through the freed activation stages (16-byte
+//     chunks XOR-swizzled by row) and leave in 16-byte row segments; fc2's fp32 outputs and
+//     8-bit codes' outputs are stored directly.
 // One barrier per K step: the loads of step s+1 are issued before step s computes; the
 // activation loads are waited for after it, the weight loads where they are first used
 // (loads complete in issue order, so the wait counts past them).
@@ -84,7 +91,7 @@ struct RowsShape {
 template <int BITS, typename ST, int MODE, int WN, bool PK, bool XS>
 __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
                                           uint16_t* xs0, uint16_t* xs1, float* rowsum,
-                                          uint32_t* xoffs_lds) {
+                                          uint32_t* rtab) {
   using S = RowsShape<BITS, MODE>;
   constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
   constexpr bool kTwo = S::kTwo;
@@ -175,30 +182,42 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   // 64 i .. 64 i + 63 ----
   auto key = [](int r) { return GPR == 16 ? (r & 15) : ((r >> 1) & 7); };
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(g.a_rows * K * 2));
-  // this thread's activation load offsets, fixed over K: in registers where they fit,
-  // else in LDS (each thread reads back only what it wrote)
-  uint32_t xoffs_reg[kRXREG ? NDMA : 1];
-  auto xoff = [&](int t) -> uint32_t& {
-    if constexpr (kRXREG) return xoffs_reg[t];
-    else return xoffs_lds[t * 256 + threadIdx.x];
-  };
   auto granule = [&](int t) {  // logical granule of load t of this lane
     const int p = (wave + 4 * t) * 64 + lane;
     return (p % GPR) ^ key(p / GPR);
   };
   // the same for every load t: 4t * 64 / GPR rows later is a multiple of the key's period
   const int gq = granule(0);
-#pragma unroll
-  for (int t = 0; t < NDMA; ++t) {
-    const int p = (wave + 4 * t) * 64 + lane;
-    const int r = p / GPR, q = granule(t);
-    uint32_t off = kOutOfRange;  // padding rows land as zeros
-    if (r < valid) {
-      const int64_t src = (MODE == kModeFc2) ? row0 + r : gemm_src_row(g, row0 + r);
-      off = static_cast<uint32_t>((src * K + 8 * q) * 2);
+  // the tile's rows, formed once by threads 0..127 (one division per row): the byte offset
+  // of the row of a that feeds each (kOutOfRange for padding rows: they land as zeros) and,
+  // with the tokens' row sums, each row's correction (rows past the valid ones keep 0)
+  if (tid < kRTM) {
+    uint32_t off = kOutOfRange;
+    float corr = 0.f;
+    if (tid < valid) {
+      const int64_t src = (MODE == kModeFc2) ? row0 + tid : gemm_src_row(g, row0 + tid);
+      off = static_cast<uint32_t>(src * K * 2);
+      if constexpr (XS) corr = -kCorr * g.xsum[src];
     }
-    xoff(t) = off;
+    rtab[tid] = off;
+    if constexpr (XS) rowsum[tid] = corr;
   }
+  __syncthreads();
+  // load t's offset: row (wave + 4t) * 64 / GPR + lane / GPR of the tile, granule gq; in
+  // registers where they fit, else read from the row table at each load
+  auto row_off = [&](int t) -> uint32_t {
+    const uint32_t base = rtab[((wave + 4 * t) * 64 + lane) / GPR];
+    return base == kOutOfRange ? kOutOfRange : base + 16u * static_cast<uint32_t>(gq);
+  };
+  uint32_t xoffs_reg[kRXREG ? NDMA : 1];
+  if constexpr (kRXREG) {
+#pragma unroll
+    for (int t = 0; t < NDMA; ++t) xoffs_reg[t] = row_off(t);
+  }
+  auto xoff = [&](int t) -> uint32_t {
+    if constexpr (kRXREG) return xoffs_reg[t];
+    else return row_off(t);
+  };
   auto xload = [&](int s, uint16_t* stage) {
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
     if (PK && k0 + SSK > K) {
@@ -342,12 +361,6 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   static_assert(kRNB < 64, "vmcnt holds 6 bits");
   constexpr int kWaitX = (kRNB & 15) | ((kRNB >> 4) << 14) | (7 << 4) | (15 << 8);
   u32x4 wa[kRNB], wb[kRNB];
-  if constexpr (XS) {
-    // the tile's row corrections from the tokens' row sums, into LDS before the first
-    // barrier (their loads overlap the first step's); rows past the valid ones keep 0
-    if (tid < kRTM)
-      rowsum[tid] = tid < valid ? -kCorr * g.xsum[gemm_src_row(g, row0 + tid)] : 0.f;
-  }
   xload(0, xs0);
   wload(0, wa);
   __builtin_amdgcn_s_waitcnt(0);
@@ -387,7 +400,8 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     __syncthreads();
   }
 
-  // ---- epilogue: scale per output row, bias, activation ----
+  // ---- epilogue: scale per output row, bias, activation; the outputs pass through the
+  // (now free) activation stages so that they leave in 16-byte row segments ----
   float bias[kRNB], svr[kRNB];
 #pragma unroll
   for (int b = 0; b < kRNB; ++b) {
@@ -397,33 +411,111 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     bias[b] = bp ? bf16_to_f32(bp[idx]) : 0.f;
     svr[b] = scale_value<ST>(static_cast<const ST*>(stream_s(st))[idx]);
   }
+  if constexpr (BITS != 4 || MODE == kModeFc2) {
+    // direct stores: 8-bit codes take 64-k stages (16 KB), too small to stage the outputs;
+    // fc2's fp32 rows would take two passes, which measured 2% slower on c3 than storing
+    // each 4-byte value
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * MT * 16 + mt * 16 + 4 * kq + i;
-      const int64_t r = row0 + m;
-      const float rc = rowsum[m];
-      // fc1 with the routing weight on the input: the row's weight scales its sums
-      const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * MT * 16 + mt * 16 + 4 * kq + i;
+        const int64_t r = row0 + m;
+        const float rc = rowsum[m];
+        const float rs = (MODE != kModeFc2 && m < valid) ? gemm_row_scale(g, r) : 1.f;
 #pragma unroll
-      for (int cb = 0; cb < NBS; ++cb) {
-        const int col = col0 + wn * NBS * 16 + cb * 16 + n;
-        if (col >= g.ncols) continue;
-        float z[NS];
+        for (int cb = 0; cb < NBS; ++cb) {
+          const int col = col0 + wn * NBS * 16 + cb * 16 + n;
+          if (col >= g.ncols) continue;
+          float z[NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          const int b = st * NBS + cb;
-          z[st] = svr[b] * (acc[mt][b][i] + rc) * rs + bias[b];
+          for (int st = 0; st < NS; ++st) {
+            const int b = st * NBS + cb;
+            z[st] = svr[b] * (acc[mt][b][i] + rc) * rs + bias[b];
+          }
+          if (MODE == kModeFc2) {
+            if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];
+          } else {
+            float hv = 0.f;
+            if (m < valid)
+              hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
+                                         : plain_act(z[0], g.act);
+            if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+          }
         }
-        if (MODE == kModeFc2) {
-          if (m < valid) static_cast<float*>(g.out)[r * g.ncols + col] = z[0];
-        } else {
+      }
+    }
+    return;
+  } else {
+    // staging (fc1 and the linear layer: bf16 h): 128 output columns per stage, 128 rows of
+    // 256 bytes; the 16-byte chunk c of row r sits at slot c ^ (r mod 16), so the 16 lanes of
+    // one MFMA row and the four rows a wave writes at once fall in distinct banks
+    constexpr int kChunks = 16;                          // 16-byte chunks per staged row
+    constexpr int kStages = (BCOLS + 127) / 128;
+    constexpr int kRowBytes = 256;
+    static_assert(kRTM * kRowBytes == S::STAGE * 2, "the tile's rows fill a stage");
+    static_assert(kStages <= 2 && kRWM == 1, "two stages, one wave row");
+    auto staged = [&](int r, int c) -> uint16_t* {
+      char* st = reinterpret_cast<char*>(c < 128 ? xs0 : xs1);
+      const int cc = c & 127;
+      return reinterpret_cast<uint16_t*>(st + r * kRowBytes + (((cc / 8) ^ (r & (kChunks - 1))) * 16) +
+                                         (cc % 8) * 2);
+    };
+    // 16-byte stores need a 16-byte aligned output (rows are: ncols is a multiple of 32)
+    const bool vec_out = (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+    // every wave is past its last read of the stages
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kq + i;
+        const int64_t r = row0 + m;
+        const float rc = rowsum[m];
+        // fc1 with the routing weight on the input: the row's weight scales its sums
+        const float rs = m < valid ? gemm_row_scale(g, r) : 1.f;
+#pragma unroll
+        for (int cb = 0; cb < NBS; ++cb) {
+          const int cl = wn * NBS * 16 + cb * 16 + n;  // column inside the workgroup
+          float z[NS];
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const int b = st * NBS + cb;
+            z[st] = svr[b] * (acc[mt][b][i] + rc) * rs + bias[b];
+          }
           float hv = 0.f;
           if (m < valid)
             hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
                                        : plain_act(z[0], g.act);
-          if (m < valid || !g.linear) static_cast<uint16_t*>(g.out)[r * g.ncols + col] = f32_to_bf16(hv);
+          *staged(m, cl) = f32_to_bf16(hv);
+        }
+      }
+    }
+    __syncthreads();
+    // copies out: chunk q is stage q / (128 * 16), row (q / 16) % 128, chunk q % 16; every
+    // row of the tile (padding rows as the zeros staged for them), real rows only for the
+    // linear layer
+    constexpr int kTot = kRTM * kChunks * kStages;
+#pragma unroll
+    for (int u = 0; u < kTot / 256; ++u) {
+      const int q = tid + 256 * u;
+      const int stg = q / (kRTM * kChunks);
+      const int m = (q / kChunks) % kRTM, ch = q % kChunks;
+      const int cl = stg * 128 + ch * 8;
+      const int col = col0 + cl;
+      if (cl >= BCOLS || col >= g.ncols) continue;
+      if (m >= valid && g.linear) continue;
+      const char* src = reinterpret_cast<const char*>(stg == 0 ? xs0 : xs1) + m * kRowBytes +
+                        ((ch ^ (m & (kChunks - 1))) * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      uint16_t* dst = static_cast<uint16_t*>(g.out) + (row0 + m) * g.ncols + col;
+      if (vec_out) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          dst[2 * w] = static_cast<uint16_t>(v[w]);
+          dst[2 * w + 1] = static_cast<uint16_t>(v[w] >> 16);
         }
       }
     }
@@ -438,17 +530,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs
   __shared__ __attribute__((aligned(16))) uint16_t xs0[S::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[S::STAGE];
   __shared__ float rowsum[kRTM];
-  __shared__ uint32_t xoffs_lds[S::XREG ? 1 : S::NDMA * 256];
+  __shared__ uint32_t rtab[kRTM];
 
   int tile, cblk;
   if (!xcd_item(gemm_tile_count(g), (g.ncols + S::BCOLS - 1) / S::BCOLS, tile, cblk)) return;
   // the wave index is uniform; saying so keeps LDS bases and slice choices in scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   switch (wave / S::WM) {
-    case 0: rows_body<BITS, ST, MODE, 0, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    case 1: rows_body<BITS, ST, MODE, 1, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    case 2: if constexpr (S::WNC > 2) rows_body<BITS, ST, MODE, 2, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
-    default: if constexpr (S::WNC > 3) rows_body<BITS, ST, MODE, 3, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, xoffs_lds); break;
+    case 0: rows_body<BITS, ST, MODE, 0, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, rtab); break;
+    case 1: rows_body<BITS, ST, MODE, 1, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, rtab); break;
+    case 2: if constexpr (S::WNC > 2) rows_body<BITS, ST, MODE, 2, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, rtab); break;
+    default: if constexpr (S::WNC > 3) rows_body<BITS, ST, MODE, 3, PK, XS>(g, tile, cblk, wave, xs0, xs1, rowsum, rtab); break;
   }
 }
 
