@@ -104,7 +104,8 @@ KERNEL_FILES = {"decode": ("gemm_bf16.hip", "gemm_bf16_tiled.hip", "gemm_bf16_ke
                            "gemm_common.h", "common.h", "launch.h"),
                 "prefill": ("gemm_prefill.hip", "gemm_prefill_rows.hip", "gemm_prefill_blk.hip", "gemm_prefill_blk_tiled.hip",
                             "gemm_prefill_blk_kernel.h", "gemm_prefill_sw.hip", "gemm_prefill_sw8.hip", "gemm_prefill_sw_kernel.h",
-                            "gemm_prefill_i8.hip", "gemm_prefill_i8_kernel.h", "gemm_common.h", "common.h", "launch.h"),
+                            "gemm_prefill_i8.hip", "gemm_prefill_i8_kernel.h", "gemm_prefill_h16.hip",
+                            "gemm_prefill_h16_kernel.h", "f16prep.hip", "gemm_common.h", "common.h", "launch.h"),
                 "f32": ("gemm_f32.hip", "common.h", "launch.h")}
 
 
