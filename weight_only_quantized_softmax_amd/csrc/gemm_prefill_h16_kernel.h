@@ -94,6 +94,9 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   __shared__ uint32_t rsrc[kTM];
   __shared__ float rscale[kTM];
   __shared__ int rlift[kTM];
+  // the workgroup's weight rows (one per thread): bias and lift, for the epilogue
+  __shared__ float wbias[SROWS];
+  __shared__ int wlift[SROWS];
 
   int tile, cblk;
   if (!xcd_item(gemm_tile_count(g), (g.ncols + BCOLS - 1) / BCOLS, tile, cblk)) return;
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   static_assert(SROWS == 256, "one weight row per thread");
   uint32_t soff;
   int slift;
+  float my_bias;
   const uint16_t* srow_base;
   {
     const int R = tid;
@@ -157,6 +161,8 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
     const int64_t wrow = static_cast<int64_t>(e) * stream_rows(st) + local_row(st, c);
     soff = static_cast<uint32_t>(wrow * nb);
     slift = stream_lift(st)[wrow];
+    const uint16_t* bp = static_cast<const uint16_t*>(stream_b(st));
+    my_bias = bp ? bf16_to_f32(bp[wrow]) : 0.f;
     srow_base = static_cast<const uint16_t*>((st == 1 && kTwo && g.fusion == 0) ? g.s3 : g.s);
   }
   uint16_t sreg[NBLK];
@@ -183,6 +189,11 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
     return (p % GPR) ^ key(p / GPR);
   };
   const int gq = granule(0);  // the same for every load t (4t * 64 / GPR rows later)
+  // the first step's weights and scales depend on the expert alone: requested before the
+  // row table, whose loads and division they then overlap
+  u32x4 wa[kNB], wb[kNB];
+  wload(0, wa);
+  sload(0);
   int my_lift = 0;  // thread t < 128: the lift of row t, stored to rlift after the main loop
   if (tid < kTM) {
     const int m = tid;
@@ -198,6 +209,8 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
     rsrc[m] = off;
     rscale[m] = rs;
   }
+  wbias[tid] = my_bias;
+  wlift[tid] = slift;
   __syncthreads();
   // load t of this lane: row (wave + 4t) * 64 / GPR + lane / GPR of the tile, granule gq;
   // its offset is read from the row table at each load instead of held in registers
@@ -282,10 +295,7 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   // issue order per step: activations, scales, weights; waiting down to the weight loads
   // leaves the step's activations in LDS and its scales in registers
   constexpr int kWaitX = (kNB & 15) | ((kNB >> 4) << 14) | (7 << 4) | (15 << 8);
-  u32x4 wa[kNB], wb[kNB];
   xload(0, xs0);
-  sload(0);
-  wload(0, wa);
   __builtin_amdgcn_s_waitcnt(0);
   sstore(0);
   __syncthreads();
@@ -322,12 +332,8 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   int wl[kNB];
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
-    const int st = b / NBS;
-    const int c = min(slice_col(wn, b, n), g.ncols - 1);
-    const int64_t wrow = static_cast<int64_t>(e) * stream_rows(st) + local_row(st, c);
-    const uint16_t* bp = static_cast<const uint16_t*>(stream_b(st));
-    bias[b] = bp ? bf16_to_f32(bp[wrow]) : 0.f;
-    wl[b] = stream_lift(st)[wrow];
+    bias[b] = wbias[wn * 16 * kNB + b * 16 + n];
+    wl[b] = wlift[wn * 16 * kNB + b * 16 + n];
   }
   // staging: 128 output columns per stage, rows of 256 bytes (bf16 h) or 512 bytes (fp32 y,
   // in two passes of 64 rows); the 16-byte chunk c of row r sits at slot c ^ (r mod chunks),
