@@ -284,7 +284,7 @@ bool use_xsum(const qmoe_params* p) {
 
 // The fp16 block-scale path: 4-bit codes with bf16 block scales of 16 to 128 at 128-row
 // tiles in the tiled layout, bf16 activations. The forward lifts x and h into fp16 and the
-// weight rows' scales by powers of two (launch_rows_to_f16, launch_scale_lift), and the GEMMs
+// weight rows' scales by powers of two (launch_prep_f16, launch_rows_to_f16), and the GEMMs
 // take each weight exactly as one fp16 operand (gemm_prefill_h16_kernel.h). The stage entry
 // points, which have no workspace for the fp16 rows, keep the bf16 kernels.
 bool use_h16(const qmoe_params* p) {
@@ -765,20 +765,18 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
     x = w.xq;
   }
   if (use_h16(p)) {
-    // the fp16 block-scale path: lifts of the weight rows' scales, x in fp16, fc1, h in
-    // fp16 (the rows of the tiles in use), fc2
+    // the fp16 block-scale path: lifts of the weight rows' scales and x in fp16 (one
+    // launch), fc1, h in fp16 (the rows of the tiles in use), fc2
     const int H = static_cast<int>(p->hidden_size), I = static_cast<int>(p->inter_size);
     const int nbh = (H + p->block_size - 1) / p->block_size;
     const int nbi = (I + p->block_size - 1) / p->block_size;
-    QMOE_TRY(device_status(qmoe::launch_scale_lift(fc1.scales, w.w1lift, p->num_experts * n1_rows(p),
-                                                   nbh, s), "fc1 scale lift launch"));
-    if (has_fc3(p))
-      QMOE_TRY(device_status(qmoe::launch_scale_lift(fc3.scales, w.w3lift, p->num_experts * I, nbh, s),
-                             "fc3 scale lift launch"));
-    QMOE_TRY(device_status(qmoe::launch_scale_lift(fc2.scales, w.w2lift, p->num_experts * H, nbi, s),
-                           "fc2 scale lift launch"));
-    QMOE_TRY(device_status(qmoe::launch_rows_to_f16(input, w.x16, w.xlift, p->num_tokens, H, nullptr, 0, s),
-                           "x to fp16 launch"));
+    const void* sc[3] = {fc1.scales, has_fc3(p) ? fc3.scales : nullptr, fc2.scales};
+    int32_t* const lifts[3] = {w.w1lift, w.w3lift, w.w2lift};
+    const int64_t srows[3] = {p->num_experts * n1_rows(p), p->num_experts * I, p->num_experts * H};
+    const int snb[3] = {nbh, nbh, nbi};
+    QMOE_TRY(device_status(qmoe::launch_prep_f16(sc, lifts, srows, snb, input, w.x16, w.xlift,
+                                                 p->num_tokens, H, s),
+                           "fp16 operands launch"));
     QMOE_TRY(run_fc1(p, input, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s,
                      nullptr, nullptr, &w));
     QMOE_TRY(device_status(qmoe::launch_rows_to_f16(w.h, w.h16, w.hlift, max_rows_of(p), I, w.num_tiles,

@@ -38,17 +38,10 @@ constexpr int kScaleTop = 12;
 // One wave per row, two passes: the largest magnitude (bf16 bits order like magnitudes once
 // the sign is cleared), then every element times 2^e, rounded to nearest fp16 (exact unless
 // it lies more than 2^31 below the row's largest). K % 8 == 0 and 16-byte aligned rows.
-__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ in,
-                                                          uint16_t* __restrict__ out,
-                                                          int32_t* __restrict__ lift,
-                                                          int64_t rows, int K,
-                                                          const int32_t* __restrict__ num_tiles,
-                                                          int tile_m) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  // rows of tiles past the grouped GEMM's tile count hold nothing
-  const int64_t used = num_tiles ? min<int64_t>(rows, int64_t(*num_tiles) * tile_m) : rows;
-  if (r >= used) return;
+__device__ __forceinline__ void row_to_f16(const uint16_t* __restrict__ in,
+                                           uint16_t* __restrict__ out,
+                                           int32_t* __restrict__ lift, int64_t r, int K,
+                                           int lane) {
   const uint4* src = reinterpret_cast<const uint4*>(in + r * K);
   uint4* dst = reinterpret_cast<uint4*>(out + r * K);
   const int C = K / 8;
@@ -76,12 +69,25 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
   if (lane == 0) lift[r] = e;
 }
 
+__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ in,
+                                                          uint16_t* __restrict__ out,
+                                                          int32_t* __restrict__ lift,
+                                                          int64_t rows, int K,
+                                                          const int32_t* __restrict__ num_tiles,
+                                                          int tile_m) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  // rows of tiles past the grouped GEMM's tile count hold nothing
+  const int64_t used = num_tiles ? min<int64_t>(rows, int64_t(*num_tiles) * tile_m) : rows;
+  if (r >= used) return;
+  row_to_f16(in, out, lift, r, K, threadIdx.x % 64);
+}
+
 // Eight lanes per weight row (a wave covers eight rows): lane l of a row reads scales l,
 // l + 8, ... of its nb bf16 scales; the row's largest magnitude meets over the eight lanes.
-__global__ __launch_bounds__(256) void scale_lift_kernel(const uint16_t* __restrict__ s,
-                                                         int32_t* __restrict__ lift,
-                                                         int64_t rows, int nb) {
-  const int64_t r = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / 8;
+__device__ __forceinline__ void scale_lift_rows(const uint16_t* __restrict__ s,
+                                                int32_t* __restrict__ lift, int64_t rows,
+                                                int nb, int64_t block) {
+  const int64_t r = (block * 256 + threadIdx.x) / 8;
   const int l = threadIdx.x % 8;
   uint32_t m = 0;
   if (r < rows) {
@@ -92,6 +98,38 @@ __global__ __launch_bounds__(256) void scale_lift_kernel(const uint16_t* __restr
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
   if (r < rows && l == 0) lift[r] = lift_of(m, kScaleTop);
+}
+
+// Everything the fp16 path needs before fc1, in one launch: the lifts of up to three
+// scale stacks (fc1, fc3, fc2) and x in fp16. Workgroups [0, b0) take stack 0, the next b1
+// stack 1, the next b2 stack 2, the rest four rows of x each.
+struct PrepArgs {
+  const uint16_t* s[3];
+  int32_t* slift[3];
+  int64_t srows[3];
+  int nb[3];
+  const uint16_t* x;
+  uint16_t* x16;
+  int32_t* xlift;
+  int64_t T;
+  int H;
+};
+
+__device__ __forceinline__ int64_t scale_blocks(int64_t rows) { return (rows * 8 + 255) / 256; }
+
+__global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs a) {
+  int64_t b = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int64_t nbk = a.s[i] ? scale_blocks(a.srows[i]) : 0;
+    if (b < nbk) {
+      scale_lift_rows(a.s[i], a.slift[i], a.srows[i], a.nb[i], b);
+      return;
+    }
+    b -= nbk;
+  }
+  const int64_t r = b * 4 + threadIdx.x / 64;
+  if (r < a.T) row_to_f16(a.x, a.x16, a.xlift, r, a.H, threadIdx.x % 64);
 }
 
 }  // namespace
@@ -107,11 +145,26 @@ hipError_t launch_rows_to_f16(const void* in, void* out, int32_t* lift, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_scale_lift(const void* scales, int32_t* lift, int64_t rows, int nb,
-                             hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  const unsigned blocks = static_cast<unsigned>((rows * 8 + 255) / 256);
-  scale_lift_kernel<<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(scales), lift, rows, nb);
+hipError_t launch_prep_f16(const void* const scales[3], int32_t* const lifts[3],
+                           const int64_t rows[3], const int nb[3], const void* x, void* x16,
+                           int32_t* xlift, int64_t T, int H, hipStream_t s) {
+  if (H % 8 != 0) return hipErrorInvalidValue;
+  PrepArgs a{};
+  int64_t blocks = (T + 3) / 4;
+  for (int i = 0; i < 3; ++i) {
+    a.s[i] = static_cast<const uint16_t*>(scales[i]);
+    a.slift[i] = lifts[i];
+    a.srows[i] = rows[i];
+    a.nb[i] = nb[i];
+    if (scales[i]) blocks += (rows[i] * 8 + 255) / 256;
+  }
+  a.x = static_cast<const uint16_t*>(x);
+  a.x16 = static_cast<uint16_t*>(x16);
+  a.xlift = xlift;
+  a.T = T;
+  a.H = H;
+  if (blocks == 0) return hipSuccess;
+  prep_f16_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

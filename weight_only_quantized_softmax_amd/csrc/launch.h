@@ -230,11 +230,13 @@ hipError_t launch_gemm_i8_prefill(const GemmArgs& g, int mode, int bits, bool sc
 // first *num_tiles * tile_m rows.
 hipError_t launch_rows_to_f16(const void* in, void* out, int32_t* lift, int64_t rows, int K,
                               const int32_t* num_tiles, int tile_m, hipStream_t s);
-// For each of `rows` rows of nb bf16 scales: the power of two 2^lift[r] that puts the row's
-// largest scale in [2^12, 2^13).
-hipError_t launch_scale_lift(const void* scales, int32_t* lift, int64_t rows, int nb,
-                             hipStream_t s);
-// g.a: fp16 rows with g.alift; g.wlift (and g.wlift3) from launch_scale_lift.
+// One launch before fc1: for each of up to three scale stacks (scales[i] may be null) of
+// rows[i] rows of nb[i] bf16 scales, the power of two 2^lifts[i][r] that puts each row's
+// largest scale in [2^12, 2^13); and x [T, H] as rows_to_f16 converts it.
+hipError_t launch_prep_f16(const void* const scales[3], int32_t* const lifts[3],
+                           const int64_t rows[3], const int nb[3], const void* x, void* x16,
+                           int32_t* xlift, int64_t T, int H, hipStream_t s);
+// g.a: fp16 rows with g.alift; g.wlift (and g.wlift3) from launch_prep_f16.
 hipError_t launch_gemm_h16_prefill(const GemmArgs& g, int mode, int64_t max_tiles, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* assign_pos, const float* w,
