@@ -106,6 +106,20 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
   return g * sig * (u + beta);
 }
 
+// The same SwiGLU for epilogues that prepare its constants once: na = -alpha * log2(e), so
+// that the logistic takes one multiply and the hardware exp2 (what __expf computes, with
+// alpha folded into its constant), and the clamps compiled in only when there is a limit.
+template <bool CLAMP>
+__device__ __forceinline__ float swiglu_k(float g, float u, float na, float beta, float limit) {
+  if constexpr (CLAMP) {
+    g = fminf(g, limit);
+    u = fmaxf(-limit, fminf(u, limit));
+  }
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * na));
+  return g * sig * (u + beta);
+}
+__device__ __forceinline__ float swiglu_na(float alpha) { return -alpha * 1.4426950408889634f; }
+
 // The plain activations by code: 1 identity, 2 relu, 3 silu, 4 gelu z * Phi(z) (Phi the
 // standard normal CDF, through erf), 5 gelu's tanh approximation (graiphic "QMoE" page,
 // activation_type; CLIKA "MoE" page, gelu_mode).

@@ -206,8 +206,9 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
   // load t's offset: row (wave + 4t) * 64 / GPR + lane / GPR of the tile, granule gq; in
   // registers where they fit, else read from the row table at each load
   auto row_off = [&](int t) -> uint32_t {
-    const uint32_t base = rtab[((wave + 4 * t) * 64 + lane) / GPR];
-    return base == kOutOfRange ? kOutOfRange : base + 16u * static_cast<uint32_t>(gq);
+    // a padding row's kOutOfRange plus the granule (and the step's scalar offset) stays
+    // past every buffer, so it still reads zeros
+    return rtab[((wave + 4 * t) * 64 + lane) / GPR] + 16u * static_cast<uint32_t>(gq);
   };
   uint32_t xoffs_reg[kRXREG ? NDMA : 1];
   if constexpr (kRXREG) {
@@ -465,31 +466,50 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
     const bool vec_out = (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
     // every wave is past its last read of the stages
     __syncthreads();
+    // the outputs into the stages; instantiated for the SwiGLU clamp and the routing weight on
+    // the input, each compiled in only where the launch has it (one uniform branch)
+    const float na = swiglu_na(g.alpha);
+    auto emit = [&](auto clamp_t, auto roww_t) {
+      constexpr bool kClamp = decltype(clamp_t)::value, kRoww = decltype(roww_t)::value;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * kq + i;
-        const int64_t r = row0 + m;
-        const float rc = rowsum[m];
-        // fc1 with the routing weight on the input: the row's weight scales its sums
-        const float rs = m < valid ? gemm_row_scale(g, r) : 1.f;
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + 4 * kq + i;
+          const float rc = rowsum[m];
+          // fc1 with the routing weight on the input: the row's weight scales its sums
+          float rs = 1.f;
+          if constexpr (kRoww) rs = m < valid ? gemm_row_scale(g, row0 + m) : 1.f;
 #pragma unroll
-        for (int cb = 0; cb < NBS; ++cb) {
-          const int cl = wn * NBS * 16 + cb * 16 + n;  // column inside the workgroup
-          float z[NS];
+          for (int cb = 0; cb < NBS; ++cb) {
+            const int cl = wn * NBS * 16 + cb * 16 + n;  // column inside the workgroup
+            float z[NS];
 #pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const int b = st * NBS + cb;
-            z[st] = svr[b] * (acc[mt][b][i] + rc) * rs + bias[b];
+            for (int st = 0; st < NS; ++st) {
+              const int b = st * NBS + cb;
+              z[st] = kRoww ? svr[b] * (acc[mt][b][i] + rc) * rs + bias[b]
+                            : fmaf(svr[b], acc[mt][b][i] + rc, bias[b]);
+            }
+            float hv = 0.f;
+            if (m < valid)
+              hv = (MODE == kModeSwiglu) ? swiglu_k<kClamp>(z[0], z[NS - 1], na, g.beta, g.limit)
+                                         : plain_act(z[0], g.act);
+            *staged(m, cl) = f32_to_bf16(hv);
           }
-          float hv = 0.f;
-          if (m < valid)
-            hv = (MODE == kModeSwiglu) ? swiglu(z[0], z[NS - 1], g.alpha, g.beta, g.limit)
-                                       : plain_act(z[0], g.act);
-          *staged(m, cl) = f32_to_bf16(hv);
         }
       }
+    };
+    if constexpr (MODE == kModeSwiglu) {
+      const bool clamp = g.limit < INFINITY;
+      if (g.row_w) {
+        if (clamp) emit(std::true_type{}, std::true_type{});
+        else emit(std::false_type{}, std::true_type{});
+      } else {
+        if (clamp) emit(std::true_type{}, std::false_type{});
+        else emit(std::false_type{}, std::false_type{});
+      }
+    } else {
+      emit(std::false_type{}, std::true_type{});  // plain activations: one instance
     }
     __syncthreads();
     // copies out: chunk q is stage q / (128 * 16), row (q / 16) % 128, chunk q % 16; every
