@@ -384,6 +384,12 @@ qmoe_status qmoe_forward_noalloc(const qmoe_params* p, const void* input,
  *                   largest magnitude in [2^14, 2^15)), which the GEMMs take on fp16 matrix
  *                   cores with each weight (q - 8) * scale exact in one fp16 operand; h16
  *                   holds only the rows of the tiles in use.
+ *   hpart           where xsum is formed and the codes are 4-bit (0 otherwise): float
+ *                   [qmoe_max_rows, n] with n the column blocks of fc1's 128-row kernel (I / 128
+ *                   rounded up with SwiGLU, I / 256 with a plain activation): the sum of each
+ *                   row of h over each block of columns, written by fc1; followed by float
+ *                   [qmoe_max_rows], their totals per row, from which fc2 takes its zero
+ *                   point's correction (rows of tiles in use only).
  * Errors: invalid parameters as qmoe_validate; out NULL -> QMOE_ERR_UNBOUND.
  */
 typedef struct {
@@ -393,6 +399,7 @@ typedef struct {
   size_t xcodes, xfactors, hcodes, hfactors;
   size_t xsum;
   size_t x16, xlift, h16, hlift;
+  size_t hpart;
 } qmoe_workspace_layout;
 
 qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout* out);

@@ -43,7 +43,7 @@ class QmoeWorkspaceLayout(ctypes.Structure):
         "topk_ids", "topk_w", "counts", "padded_offsets", "sorted_assign", "assign_pos",
         "tile_list", "num_tiles", "permute_scratch", "h", "y", "xq", "total")] + [
         ("fused_routing", ctypes.c_int32)] + [(n, ctypes.c_size_t) for n in (
-        "xcodes", "xfactors", "hcodes", "hfactors", "xsum", "x16", "xlift", "h16", "hlift")]
+        "xcodes", "xfactors", "hcodes", "hfactors", "xsum", "x16", "xlift", "h16", "hlift", "hpart")]
 
 
 class QmoeStack(ctypes.Structure):

@@ -294,6 +294,15 @@ bool use_h16(const qmoe_params* p) {
          tile_m_of(p) == 128 && p->hidden_size % 8 == 0 && p->inter_size % 8 == 0;
 }
 
+// With 4-bit codes on that path fc1 also writes each row's partial sums of h, one per
+// column block; launch_partsum adds them up, and fc2 takes its zero point's correction from
+// those row sums.
+bool use_hpart(const qmoe_params* p) { return use_xsum(p) && p->expert_weight_bits == 4; }
+int hpart_blocks(const qmoe_params* p) {
+  const int cols = qmoe::prefill_rows_fc1_cols(swiglu(p) ? qmoe::kModeSwiglu : qmoe::kModePlainAct);
+  return static_cast<int>((p->inter_size + cols - 1) / cols);
+}
+
 struct Workspace {
   int32_t* topk_ids;
   float* topk_w;
@@ -313,6 +322,8 @@ struct Workspace {
   int8_t* hc;
   float* hf;
   float* xsum;  // use_xsum: the row sums of x
+  float* hpart;  // use_hpart: fc1's partial row sums of h [qmoe_max_rows, hpart_blocks]
+  float* hsum;   // use_hpart: the row sums of h [qmoe_max_rows]
   // use_h16: x and h as lifted fp16 rows with their lifts, and the lifts of the weight rows'
   // scales (fc1, fc3 when separate, fc2)
   void* x16;
@@ -359,6 +370,10 @@ Workspace carve(const qmoe_params* p, char* base) {
     w.xq = take(p->num_tokens * p->hidden_size * act);
   }
   if (use_xsum(p)) w.xsum = reinterpret_cast<float*>(take(p->num_tokens * 4));
+  if (use_hpart(p)) {
+    w.hpart = reinterpret_cast<float*>(take(rows * hpart_blocks(p) * 4));
+    w.hsum = reinterpret_cast<float*>(take(rows * 4));
+  }
   if (use_h16(p)) {
     w.x16 = take(p->num_tokens * p->hidden_size * 2);
     w.xlift = reinterpret_cast<int32_t*>(take(p->num_tokens * 4));
@@ -448,11 +463,15 @@ qmoe_status run_fc1(const qmoe_params* p, const void* x, const int32_t* sorted_a
                     const int32_t* tiles, const int32_t* num_tiles, const float* topk_w,
                     qmoe_stack fc1, qmoe_stack fc3, void* h, hipStream_t s,
                     const float* xfac = nullptr, const float* xsum = nullptr,
-                    const Workspace* h16 = nullptr) {
+                    const Workspace* h16 = nullptr, float* hpart = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = x;
   g.afac = xfac;
   g.xsum = xsum;
+  if (hpart) {
+    g.hpart = hpart;
+    g.hpart_stride = hpart_blocks(p);
+  }
   if (h16) {
     g.a = h16->x16;
     g.alift = h16->xlift;
@@ -503,10 +522,12 @@ qmoe_status run_linear(const qmoe_params* p, const void* x, qmoe_stack w, void* 
 
 qmoe_status run_fc2(const qmoe_params* p, const void* h, const int32_t* tiles,
                     const int32_t* num_tiles, qmoe_stack fc2, float* y, hipStream_t s,
-                    const float* hfac = nullptr, const Workspace* h16 = nullptr) {
+                    const float* hfac = nullptr, const Workspace* h16 = nullptr,
+                    const float* hsum = nullptr) {
   qmoe::GemmArgs g = gemm_args(p);
   g.a = h;
   g.afac = hfac;
+  g.xsum = hsum;
   if (h16) {
     g.a = h16->h16;
     g.alift = h16->hlift;
@@ -683,6 +704,7 @@ qmoe_status qmoe_workspace_layout_of(const qmoe_params* p, qmoe_workspace_layout
   out->hcodes = i8 ? off(w.hc) : 0;
   out->hfactors = i8 ? off(w.hf) : 0;
   out->xsum = use_xsum(p) ? off(w.xsum) : 0;
+  out->hpart = use_hpart(p) ? off(w.hpart) : 0;
   const bool h16 = use_h16(p);
   out->x16 = h16 ? off(w.x16) : 0;
   out->xlift = h16 ? off(w.xlift) : 0;
@@ -795,14 +817,18 @@ qmoe_status qmoe_forward(const qmoe_params* p, const void* input, const void* ro
                                                static_cast<int>(p->hidden_size), s),
                            "row sum launch"));
   QMOE_TRY(run_fc1(p, x, w.sorted_assign, w.tiles, w.num_tiles, w.topk_w, fc1, fc3, w.h, s,
-                   nullptr, w.xsum));
+                   nullptr, w.xsum, nullptr, w.hpart));
   if (int8)
     QMOE_TRY(device_status(qmoe::launch_quantize_blocks(w.h, w.h, abf, max_rows_of(p),
                                                         static_cast<int>(p->inter_size),
                                                         p->block_size, w.num_tiles,
                                                         static_cast<int>(tile_m_of(p)), s),
                            "quantize h launch"));
-  QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s));
+  if (use_hpart(p))
+    QMOE_TRY(device_status(qmoe::launch_partsum(w.hpart, w.hsum, max_rows_of(p), hpart_blocks(p),
+                                                w.num_tiles, 128, s),
+                           "h row sum launch"));
+  QMOE_TRY(run_fc2(p, w.h, w.tiles, w.num_tiles, fc2, w.y, s, nullptr, nullptr, w.hsum));
   QMOE_TRY(device_status(
       qmoe::launch_combine(w.y, w.assign_pos, w.topk_w, shared_output, output,
                            p->act_dtype == QMOE_BF16, static_cast<int>(p->num_tokens),

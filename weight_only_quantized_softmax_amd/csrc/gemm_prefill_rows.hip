@@ -65,12 +65,15 @@ __device__ __forceinline__ float dot2_sum(uint32_t v, float acc) {
 // weight among more MFMAs (the decode is the kernel's main VALU cost): fc1 (SwiGLU or a
 // plain activation) takes 1 x 4 waves of 128 rows x 4 slices; fc2 2 x 2 waves of 64 rows
 // x 6 slices, where the registers also hold the activation load offsets (measured on c3
-// T=4096: fc2 1% faster so, the plain-activation linear layer 6% slower).
-template <int BITS, int MODE>
+// T=4096: fc2 1% faster so, the plain-activation linear layer 6% slower). fc2 given the
+// row sums of h (XS: fc1's partial sums, in the forward) takes the 1 x 4 shape too, which
+// then fits its registers (without the sums it spills inside the K loop): c3 fc2 4% faster.
+template <int BITS, int MODE, bool XS = false>
 struct RowsShape {
   static constexpr bool kTwo = (MODE == kModeSwiglu);
-  static constexpr int WM = MODE == kModeFc2 ? 2 : 1;
-  static constexpr int NB = MODE == kModeFc2 ? 6 : 4;
+  static constexpr bool kFc2Wide = MODE == kModeFc2 && !XS;
+  static constexpr int WM = kFc2Wide ? 2 : 1;
+  static constexpr int NB = kFc2Wide ? 6 : 4;
   static constexpr bool XREG = WM == 2;                 // activation offsets in registers
   // explicit instruction order inside a k-slice (each MFMA followed by two VALU
   // instructions, operand reads first): measured neutral to negative, left off
@@ -92,7 +95,7 @@ template <int BITS, typename ST, int MODE, int WN, bool PK, bool XS>
 __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk, int wave,
                                           uint16_t* xs0, uint16_t* xs1, float* rowsum,
                                           uint32_t* rtab) {
-  using S = RowsShape<BITS, MODE>;
+  using S = RowsShape<BITS, MODE, XS>;
   constexpr float kCorr = BITS == 4 ? 136.0f : 128.0f;  // offset + zero point
   constexpr bool kTwo = S::kTwo;
   constexpr int NS = S::NS;
@@ -512,6 +515,30 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
       emit(std::false_type{}, std::true_type{});  // plain activations: one instance
     }
     __syncthreads();
+    if (g.hpart) {
+      // each row's sum over this workgroup's columns, of the bf16 values just staged (the
+      // row sums fc2 takes its zero point's correction from): two threads a row, one per
+      // half of its chunks, in every stage; padding rows sum their staged zeros
+      const int m = tid / 2, half = tid % 2;
+      float sum = 0.f;
+#pragma unroll
+      for (int stg = 0; stg < kStages; ++stg) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int ch = half * 8 + c;
+          const int cl = stg * 128 + ch * 8;
+          if (cl >= BCOLS || col0 + cl >= g.ncols) continue;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const char*>(stg == 0 ? xs0 : xs1) + m * kRowBytes +
+              ((ch ^ (m & (kChunks - 1))) * 16));
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            sum += __uint_as_float(v[w] << 16) + __uint_as_float(v[w] & 0xFFFF0000u);
+        }
+      }
+      sum += __shfl_xor(sum, 1);
+      if (half == 0) g.hpart[(row0 + m) * g.hpart_stride + cblk] = sum;
+    }
     // copies out: chunk q is stage q / (128 * 16), row (q / 16) % 128, chunk q % 16; every
     // row of the tile (padding rows as the zeros staged for them), real rows only for the
     // linear layer
@@ -544,7 +571,7 @@ __device__ __forceinline__ void rows_body(const GemmArgs& g, int tile, int cblk,
 
 template <int BITS, typename ST, int MODE, bool PK, bool XS>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_prefill_rows_kernel(GemmArgs g) {
-  using S = RowsShape<BITS, MODE>;
+  using S = RowsShape<BITS, MODE, XS>;
   // two stages as two arrays, so that the compiler can tell the stage being read from the
   // stage being filled and does not wait for the fill before reading
   __shared__ __attribute__((aligned(16))) uint16_t xs0[S::STAGE];
@@ -568,10 +595,14 @@ template <int BITS, typename ST, int MODE>
 static hipError_t launch_rows_mode(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   const int bcols = RowsShape<BITS, MODE>::BCOLS;
   dim3 grid(xcd_grid((g.ncols + bcols - 1) / bcols, max_tiles)), block(256);
-  // the forward's per-token row sums: fc1 in the tiled layout
-  if constexpr (MODE != kModeFc2) {
+  // the forward's row sums (tiled layout): fc1 takes the tokens' sums of x, fc2 (4-bit codes)
+  // those of h, formed from fc1's partial sums (only 4-bit fc1 stages its outputs and writes
+  // them)
+  if constexpr (MODE != kModeFc2 || BITS == 4) {
     if (g.packed && g.xsum) {
-      launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true, true>, grid, block, 0, s, g);
+      constexpr int xbcols = RowsShape<BITS, MODE, true>::BCOLS;
+      dim3 xgrid(xcd_grid((g.ncols + xbcols - 1) / xbcols, max_tiles));
+      launch_gemm_kernel(gemm_bf16_prefill_rows_kernel<BITS, ST, MODE, true, true>, xgrid, block, 0, s, g);
       return hipGetLastError();
     }
   }
@@ -587,6 +618,11 @@ static hipError_t launch_rows_t(const GemmArgs& g, int mode, int64_t max_tiles, 
   if (mode == kModeSwiglu) return launch_rows_mode<BITS, ST, kModeSwiglu>(g, max_tiles, s);
   if (mode == kModePlainAct) return launch_rows_mode<BITS, ST, kModePlainAct>(g, max_tiles, s);
   return launch_rows_mode<BITS, ST, kModeFc2>(g, max_tiles, s);
+}
+
+int prefill_rows_fc1_cols(int mode) {
+  return mode == kModeSwiglu ? RowsShape<4, kModeSwiglu, true>::BCOLS
+                             : RowsShape<4, kModePlainAct, true>::BCOLS;
 }
 
 hipError_t launch_gemm_bf16_prefill_rows(const GemmArgs& g, int mode, int bits, bool scale_bf16,

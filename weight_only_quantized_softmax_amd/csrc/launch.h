@@ -68,6 +68,12 @@ struct GemmArgs {
   // rows), from which the zero point's correction is taken; nullptr: the kernel sums the
   // rows itself
   const float* xsum;
+  // the forward with the per-row-scale 128-row kernels (4-bit codes): fc1 also writes, for
+  // each row of its tile, the fp32 sum of the bf16 outputs of its column block to
+  // hpart[row * hpart_stride + column block] (launch_partsum turns them into h's row sums,
+  // which fc2 takes as xsum)
+  float* hpart;
+  int hpart_stride;
   // the fp16 block-scale kernel (launch_gemm_h16_prefill): a holds fp16 rows, row i lifted
   // by 2^alift[i] (indexed like a's rows); the block scales of weight row n of expert e are
   // lifted by 2^wlift[e * rows + n] (wlift3: the separate up stack); nullptr otherwise
@@ -175,6 +181,9 @@ hipError_t launch_gemm_bf16_prefill(const GemmArgs& g, int mode, int bits, bool 
 // straight into LDS.
 hipError_t launch_gemm_bf16_prefill_rows(const GemmArgs& g, int mode, int bits, bool scale_bf16,
                                          int64_t max_tiles, hipStream_t s);
+// Output columns of one workgroup of that kernel's fc1 in mode `mode` (the column blocks
+// behind GemmArgs::hpart).
+int prefill_rows_fc1_cols(int mode);
 
 // bf16 activations, MFMA 128-row tiles, one scale per output row and K-block. Rows layout:
 // K a multiple of 128 (4-bit) or 64 (8-bit), 8-bit blocks of at least 64; tiled layout:
@@ -214,6 +223,10 @@ struct CombineOpts {
 // for the int8 dot. Needs K % 64 == 0, bs in {64, 128}, 16-byte aligned rows.
 // The fp32 sum of each of the rows of a bf16 [rows, K] matrix (one wave per row).
 hipError_t launch_rowsum(const void* x, float* out, int64_t rows, int K, hipStream_t s);
+// The sum of the n fp32 values of each row of parts (row stride n), one wave per row, in a
+// fixed order; num_tiles (device): only the first *num_tiles * tile_m rows.
+hipError_t launch_partsum(const float* parts, float* out, int64_t rows, int n,
+                          const int32_t* num_tiles, int tile_m, hipStream_t s);
 hipError_t launch_quantize_codes(const void* in, int8_t* codes, float* fac, int64_t rows, int K,
                                  int bs, const int32_t* num_tiles, int tile_m, hipStream_t s);
 

@@ -1,5 +1,6 @@
 // The sum of each activation row, once per token, for the zero point's correction of the
-// 128-row per-row-scale fc1 kernel.
+// 128-row per-row-scale fc1 kernel; and the row sums of h for its fc2, from the partial sums
+// fc1 writes per column block.
 //
 // graiphic "QMoE" page: a weight is (q - zero point) * scale per output row; the kernels
 // decode q as 128 + q (an exact bf16) and take the offset and the zero point out of each
@@ -43,7 +44,32 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict_
   if (lane == 0) out[r] = acc;
 }
 
+// One wave per row: lane l adds values l, l + 64, ... of the row in order, then the lanes'
+// sums meet by the fixed DPP tree of wave_sum_f32.
+__global__ __launch_bounds__(256) void partsum_kernel(const float* __restrict__ parts,
+                                                      float* __restrict__ out, int64_t rows, int n,
+                                                      const int32_t* __restrict__ num_tiles,
+                                                      int tile_m) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int64_t used = min<int64_t>(rows, int64_t(*num_tiles) * tile_m);
+  if (r >= used) return;
+  const float* row = parts + r * n;
+  float acc = 0.f;
+  for (int j = lane; j < n; j += 64) acc += row[j];
+  const float sum = wave_sum_f32(acc);
+  if (lane == 0) out[r] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_partsum(const float* parts, float* out, int64_t rows, int n,
+                          const int32_t* num_tiles, int tile_m, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
+  partsum_kernel<<<blocks, 256, 0, s>>>(parts, out, rows, n, num_tiles, tile_m);
+  return hipGetLastError();
+}
 
 hipError_t launch_rowsum(const void* x, float* out, int64_t rows, int K, hipStream_t s) {
   if (rows == 0) return hipSuccess;
