@@ -11,7 +11,9 @@
 //     up, so the workgroup covers 256 weight rows = 128 output columns), each decoded
 //     weight feeding 8 MFMAs; each activation fragment is read again for the next k-slice
 //     in place, right after its MFMAs, which keeps this shape within its registers;
-//   - fc2: 2 x 2 waves, each 64 rows x 6 slices (192 weight rows a workgroup).
+//   - fc2: 2 x 2 waves, each 64 rows x 6 slices (192 weight rows a workgroup); in the
+//     forward with 4-bit codes, where fc1 has written each row's partial sums of h (one per
+//     column block) and partsum_kernel has added them up, 1 x 4 like fc1.
 //   - Activations reach LDS without passing through registers: buffer loads with the LDS
 //     as destination, 16 bytes per lane, 16 lanes per 256-byte row segment, two stages
 //     (this K step and the next). The 16-byte granule q of row r sits at slot
