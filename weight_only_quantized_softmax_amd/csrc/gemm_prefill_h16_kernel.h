@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256, 2) void gemm_h16_prefill_kernel(GemmArgs g) {
   // load t of this lane: row (wave + 4t) * 64 / GPR + lane / GPR of the tile, granule gq;
   // its offset is read from the row table at each load instead of held in registers
   auto xoff = [&](int t) -> uint32_t {
-    const uint32_t base = rsrc[(wave + 4 * t) * (64 / GPR) + lane / GPR];
-    return base == kOutOfRange ? kOutOfRange : base + static_cast<uint32_t>(16 * gq);
+    // a padding row's kOutOfRange plus the granule (and the step's scalar offset) stays
+    // past every buffer, so it still reads zeros
+    return rsrc[(wave + 4 * t) * (64 / GPR) + lane / GPR] + static_cast<uint32_t>(16 * gq);
   };
   auto xload = [&](int s, uint16_t* stage) {
     const int k0 = __builtin_amdgcn_readfirstlane(s * SSK);
