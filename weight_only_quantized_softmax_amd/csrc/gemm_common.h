@@ -159,8 +159,9 @@ __device__ __forceinline__ void transpose_rows4(u32x4& d) {
   d[3] = q23[1];
 }
 
-// Work order of the 128-row kernels. The hardware hands the workgroups of a 1-D grid to
-// the 8 XCDs in turn (workgroup i to XCD i % 8), and each XCD has its own L2. Workgroup i
+// Work order of the 128-row kernels and of the 16/32-row kernel's fc2. The hardware hands
+// the workgroups of a 1-D grid to the 8 XCDs in turn (workgroup i to XCD i % 8), and each
+// XCD has its own L2. Workgroup i
 // takes item (i % 8) * per + i / 8 of the live items (per = ceil(live / 8)), so each XCD
 // works through one contiguous run of items. Items run in bands of kBand consecutive tiles
 // (one expert's tiles are consecutive): inside a band, column block by column block, the
